@@ -1,0 +1,281 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test names the passage of page "stencil-jacobian.vercel.app" it follows
+(section 01 "The problem", 02 "Method", 04/05 "Results").  None re-types the
+oracle's loops: the checks use closed forms, an independent float64 matrix
+formulation (tests/matrix_forms.py), exact symmetries and the page's printed
+numbers (tests/golden/page1_numbers.json).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import workloads
+from tests import matrix_forms as mf
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page1_numbers.json")))
+EPS32 = float(np.finfo(np.float32).eps)
+
+
+def f32(x):
+    return np.float32(x)
+
+
+# ---------------------------------------------------------------- single ops
+
+@pytest.mark.parametrize("r", [0.5, 1.0, 10.0, 100.0])
+def test_sweep_is_jacobi_step_of_matrix(orc, r):
+    """Section 01: one sweep is u' = u + D^-1 (b_A - A u) with D = (1+4r) I.
+
+    Checked in float64 through the assembled operator on a random field; the
+    float32 sweep may differ only by a few roundings of its operands.
+    """
+    N = 37
+    u = workloads.random_field(N, 3)
+    b = workloads.random_field(N, 4) * f32(0.5)
+    got = orc.sweep(u, b, r).astype(np.float64)
+    exact = u + (mf.boundary_rhs(b, r) - mf.apply_A(u, r)) / (1.0 + 4.0 * r)
+    scale = (np.abs(b) + 4.0 * r * 100.0 + r * 100.0) / (1.0 + 4.0 * r)
+    assert np.all(np.abs(got - exact) <= 6 * EPS32 * scale)
+
+
+@pytest.mark.parametrize("r", [1.0, 10.0, 100.0])
+def test_residual_matches_operator(orc, r):
+    """Section 01: R = ||b_A - A u||_inf; the difference form must agree with float64 A u."""
+    N = 41
+    u = workloads.random_field(N, 5)
+    b = workloads.random_field(N, 6)
+    R = float(orc.residual(u, b, r))
+    R64 = mf.true_residual(u, b, r)
+    assert abs(R - R64) <= 1e-5 * R64
+
+
+def test_residual_nan_propagates(orc):
+    """A NaN anywhere makes R NaN, so rho is NaN and no step can claim convergence."""
+    N = 9
+    u = workloads.random_field(N, 1)
+    b = workloads.random_field(N, 2)
+    u[4, 7] = np.nan
+    assert np.isnan(orc.residual(u, b, 1.0))
+    b2 = b.copy()
+    b2[0, 0] = np.nan
+    assert np.isnan(orc.rhs_norm(b2, 1.0))
+
+
+def test_rhs_and_norm(orc):
+    """Section 02: b = u^n + dt*f once per step; ||b_A|| carries r*100 on the top row."""
+    N = 12
+    u = workloads.random_field(N, 7)
+    s = workloads.random_source(N, 10.0, 8)
+    b = orc.rhs(u, s)
+    assert np.array_equal(b, (u.astype(np.float64) + s).astype(np.float32))
+    expected = np.max(np.abs(mf.boundary_rhs(b, 10.0)))
+    assert abs(float(orc.rhs_norm(b, 10.0)) - expected) <= 2 * EPS32 * expected
+
+
+def test_diag_is_one_plus_four_r(orc):
+    for r, d in [(1.0, 5.0), (10.0, 41.0), (100.0, 401.0), (0.0, 1.0)]:
+        assert orc.diag(r) == np.float32(d)
+
+
+# ------------------------------------------------------------ closed forms
+
+@pytest.mark.parametrize("r", [1.0, 10.0, 100.0])
+def test_single_unknown_closed_form(orc, r):
+    """N = 1: A is the scalar 1+4r and b_A = b + 100r, so Jacobi is exact in one sweep."""
+    s = np.full((1, 1), 0.25, np.float32)
+    res = orc.solve(1, r, s, steps=3)
+    assert res.status == orc.OK
+    assert res.sweeps.tolist() == [8, 8, 8]
+    un = 0.0
+    for _ in range(3):
+        un = (un + 0.25 + 100.0 * r) / (1.0 + 4.0 * r)
+    assert abs(float(res.u[0, 0]) - un) <= 4 * EPS32 * abs(un)
+
+
+def test_zero_coupling(orc):
+    """r = 0: A = I, so one sweep gives u = b and every step ends at the first check."""
+    N = 10
+    s = workloads.random_source(N, 1.0, 11) + np.float32(0.5)
+    u0 = workloads.random_field(N, 12)
+    res = orc.solve(N, 0.0, s, u0=u0, steps=4)
+    assert res.status == orc.OK
+    assert res.sweeps.tolist() == [8] * 4
+    assert np.all(res.rho == 0)
+    expect = u0.copy()
+    for _ in range(4):
+        expect = (expect + s).astype(np.float32)
+    assert np.array_equal(res.u, expect)
+
+
+@pytest.mark.parametrize("r", [1.0, 10.0])
+def test_dense_solve_error_bound_n8(orc, r):
+    """Section 01: A is strictly diagonally dominant with ||A^-1||_inf <= 1, so the
+    error of every accepted iterate is bounded by its residual."""
+    N = 8
+    s = workloads.gaussian_source(N, r) + workloads.random_source(N, r, 21)
+    u = np.zeros((N, N), np.float32)
+    A = mf.dense_matrix(N, r)
+    assert np.max(np.sum(np.abs(np.linalg.inv(A)), axis=1)) <= 1.0
+    for _ in range(10):
+        b = orc.rhs(u, s)
+        res = orc.solve(N, r, s, u0=u, steps=1)
+        assert res.status == orc.OK
+        ustar = mf.dense_solve(b, r)
+        R = float(res.rho[0]) * float(orc.rhs_norm(b, r))
+        assert R == pytest.approx(mf.true_residual(res.u, b, r), rel=1e-3, abs=1e-6)
+        assert np.max(np.abs(res.u - ustar)) <= R * (1 + 1e-3) + 1e-6
+        u = res.u
+
+
+def test_sine_transform_solver_agrees_with_dense():
+    """The DST-I exact solver used at larger N equals the dense solve at N = 8."""
+    b = workloads.random_field(8, 31)
+    assert np.max(np.abs(mf.dst_solve(b, 10.0) - mf.dense_solve(b, 10.0))) < 1e-11
+
+
+@pytest.mark.parametrize("N,r", [(64, 10.0), (256, 1.0), (256, 10.0)])
+def test_error_bound_against_exact_solution(orc, N, r):
+    """Section 01: diagonal dominance makes the residual bound the error (DST-I exact solve)."""
+    s = workloads.gaussian_source(N, r)
+    u = np.zeros((N, N), np.float32)
+    for _ in range(3):
+        b = orc.rhs(u, s)
+        res = orc.solve(N, r, s, u0=u, steps=1)
+        assert res.status == orc.OK and res.rho[0] < 1e-5
+        R = float(res.rho[0]) * float(orc.rhs_norm(b, r))
+        err = np.max(np.abs(res.u - mf.dst_solve(b, r)))
+        assert err <= R * (1 + 1e-3) + 64 * EPS32 * 100.0
+        u = res.u
+
+
+@pytest.mark.parametrize("r", [1.0, 10.0, 100.0])
+def test_residual_contraction(orc, r):
+    """Section 01: the residual obeys res_{k+1} = r/(1+4r) * sum of neighbour residuals,
+    so M sweeps shrink max|res| by at least q^M, q = 4r/(1+4r) (the spectral bound)."""
+    N, M = 96, 8
+    q = 4 * r / (1 + 4 * r)
+    res = orc.solve(N, r, workloads.gaussian_source(N, r), steps=2, M=M, log_cap=10000)
+    R = res.R_log.astype(np.float64)
+    n1 = int(res.sweeps[0] // M)
+    floor = 200 * EPS32 * (100.0 * r + 100.0)
+    for seq in (R[:n1], R[n1:]):
+        for a, b in zip(seq[:-1], seq[1:]):
+            assert b <= q**M * a + floor
+    # the bound is nearly tight for large r: the slowest mode has radius close to q
+    if r == 100.0:
+        ratios = R[1:n1] / R[: n1 - 1]
+        assert ratios.max() > 0.9 * q**M
+
+
+# ------------------------------------------------------------- symmetries
+
+@pytest.mark.parametrize("N,kind,r", [(65, "point", 10.0), (127, "point", 1.0),
+                                      (64, "gaussian", 100.0), (70, "gaussian", 10.0)])
+def test_mirror_symmetry_bitwise(orc, N, kind, r):
+    """The problem is symmetric under j -> N-1-j; with E+W summed first the float32
+    iteration is too, bit for bit."""
+    s = workloads.source(kind, N, r)
+    assert np.array_equal(s, s[:, ::-1])
+    res = orc.solve(N, r, s, steps=3)
+    assert res.status == orc.OK
+    assert np.array_equal(res.u, res.u[:, ::-1])
+    assert not np.array_equal(res.u, res.u[::-1, :])
+
+
+def test_thread_count_does_not_change_results(orc):
+    s = workloads.gaussian_source(70, 10.0)
+    orc.set_threads(1)
+    a = orc.solve(70, 10.0, s, steps=2)
+    orc.set_threads(8)
+    b = orc.solve(70, 10.0, s, steps=2)
+    assert np.array_equal(a.u, b.u) and np.array_equal(a.sweeps, b.sweeps)
+
+
+# ----------------------------------------------------------- page numbers
+
+@pytest.mark.parametrize("r,page_mean", list(zip(GOLDEN["mean_sweeps_per_step"]["r"],
+                                                  GOLDEN["mean_sweeps_per_step"]["value"])))
+def test_sweeps_per_step_match_page(orc, r, page_mean):
+    """Section 01: about 35, 226 and 1417 sweeps per step at r = 1, 10, 100."""
+    N = 512
+    res = orc.solve(N, r, workloads.point_source(N, r))
+    assert res.status == orc.OK
+    assert np.all(res.sweeps % 8 == 0)
+    assert np.all(res.rho < 1e-5)
+    assert abs(res.sweeps.mean() - page_mean) <= 1.5
+
+
+@pytest.mark.parametrize("r", [1.0, 10.0])
+def test_sweep_counts_independent_of_N_and_source(orc, r):
+    """Section 01: the count grows with r but not with N."""
+    a = orc.solve(512, r, workloads.point_source(512, r))
+    b = orc.solve(1024, r, workloads.gaussian_source(1024, r))
+    assert a.sweeps.tolist() == b.sweeps.tolist()
+
+
+def test_max_sweeps_reports_noconv(orc):
+    N = 64
+    res = orc.solve(N, 100.0, workloads.point_source(N, 100.0), steps=2, max_sweeps=40)
+    assert res.status == orc.ENOCONV
+    assert res.sweeps.tolist() == [40, 0]
+    assert res.rho[0] >= 1e-5
+
+
+def test_nan_source_reports_enan(orc):
+    s = workloads.point_source(16, 1.0)
+    s[3, 3] = np.nan
+    res = orc.solve(16, 1.0, s, steps=2)
+    assert res.status == orc.ENAN
+    assert res.sweeps.tolist() == [8, 0]
+
+
+# --------------------------------------------------------- block-async model
+
+def test_async_d1_is_sync(orc):
+    """Section 02: with D = 1 the block-async kernel reproduces the synchronous iterates."""
+    N = 70
+    s = workloads.gaussian_source(N, 10.0)
+    a = orc.solve(N, 10.0, s, steps=3)
+    b = orc.solve(N, 10.0, s, steps=3, mode=orc.ASYNC, D=1, tx=32, ty=8)
+    assert np.array_equal(a.u, b.u) and a.sweeps.tolist() == b.sweeps.tolist()
+
+
+def test_async_single_tile_is_sync(orc):
+    """A tile that covers the grid has only the boundary as halo: D in-tile sweeps
+    are D synchronous sweeps exactly."""
+    N = 23
+    u = workloads.random_field(N, 41)
+    b = workloads.random_field(N, 42)
+    want = u
+    for _ in range(5):
+        want = orc.sweep(want, b, 10.0)
+    assert np.array_equal(orc.async_launch(u, b, 10.0, 32, 32, 5), want)
+
+
+@pytest.mark.parametrize("N,tx,ty,D", [(6, 4, 2, 3), (9, 4, 4, 2), (7, 3, 5, 4)])
+def test_async_launch_matches_block_jacobi(orc, N, tx, ty, D):
+    """Per tile, D Jacobi sweeps of the local system with the outside frozen."""
+    u = workloads.random_field(N, 51)
+    b = workloads.random_field(N, 52)
+    got = orc.async_launch(u, b, 10.0, tx, ty, D).astype(np.float64)
+    want = mf.block_async_launch(u, b, 10.0, tx, ty, D)
+    assert np.max(np.abs(got - want)) <= 1e-5 * 100.0
+
+
+def test_async_sweep_ratio_near_page(orc):
+    """Section 05: D8 at 32x16 tiles needs about 1.738x the sync sweeps at r = 10;
+    section 04: D4 needs 1.35-1.59x."""
+    g = GOLDEN["async_sweep_ratio"]
+    N, r = 512, 10.0
+    s = workloads.gaussian_source(N, r)
+    sync = orc.solve(N, r, s).total_sweeps
+    d8 = orc.solve(N, r, s, mode=orc.ASYNC, D=8, tx=32, ty=16)
+    assert d8.status == orc.OK and np.all(d8.rho < 1e-5)
+    ratio8 = d8.total_sweeps / sync
+    assert abs(ratio8 - g["D8_32x16_r10"]) <= 0.03 * g["D8_32x16_r10"]
+    d4 = orc.solve(N, r, s, mode=orc.ASYNC, D=4, tx=32, ty=8)
+    lo, hi = g["D4_range"]
+    assert 0.97 * lo <= d4.total_sweeps / sync <= 1.03 * hi

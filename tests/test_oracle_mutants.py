@@ -1,0 +1,52 @@
+"""Each plausible mistake planted in a copy of the oracle must fail one pin.
+
+The mutants are built from oracle/jacobi_oracle.c by one textual replacement
+each, compiled into a temporary directory, and the pin suite
+(tests/test_oracle.py) is run against them in a subprocess.  This runs on the
+CPU only and never touches the library path.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "jacobi_oracle.c")
+
+MUTANTS = {
+    "sum_order_north_first": ("float S = uE + uW;\n    S = S + uN;", "float S = uN + uE;\n    S = S + uW;"),
+    "wrong_south_index": ("uS = U[c + P];", "uS = U[c + P + 1];"),
+    "transposed_neighbours": ("float uE = U[c + 1], uW = U[c - 1], uN = U[c - P], uS = U[c + P];",
+                              "float uE = U[c + P], uW = U[c - P], uN = U[c - 1], uS = U[c + 1];"),
+    "residual_drops_south": ("    e = e + (U[c + P] - C);\n", ""),
+    "residual_sign": ("return bc + t;", "return bc - t;"),
+    "norm_without_boundary": ("float v = B[at(N, i, j)] + r * g;", "float v = B[at(N, i, j)];"),
+    "diag_three_r": ("float four_r = 4.0f * r;", "float four_r = 3.0f * r;"),
+    "check_on_previous_iterate": ("float R = residual_padded(N, r, cur, B);",
+                                  "float R = residual_padded(N, r, nxt, B);"),
+    "rhs_misses_source": ("= U[at(N, i, j)] + s[(size_t)i * N + j];", "= U[at(N, i, j)];"),
+    "async_gauss_seidel_in_tile": ("nxt[l] = jacobi_point(cur, l, lp, bl[l], r, d);",
+                                   "cur[l] = jacobi_point(cur, l, lp, bl[l], r, d); nxt[l] = cur[l];"),
+    "async_halo_from_rhs": ("cur[(size_t)a * lp + c] = U[g];",
+                            "cur[(size_t)a * lp + c] = (a == 0 || c == 0 || a == h + 1 || c == w + 1) ? B[g] : U[g];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_fails_a_pin(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    msrc = tmp_path / "jacobi_oracle.c"
+    msrc.write_text(src.replace(old, new))
+    (tmp_path / "jacobi_oracle.h").write_text(open(os.path.join(ROOT, "oracle", "jacobi_oracle.h")).read())
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", *oracle.CFLAGS, str(msrc), "-o", str(lib), "-lm"], check=True)
+    env = dict(os.environ, JACOBI_ORACLE_LIB=str(lib))
+    proc = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", "test_oracle.py")],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert proc.returncode == 1, f"mutant {name} passed every pin:\n{proc.stdout[-2000:]}"
