@@ -1,0 +1,174 @@
+"""Benchmark: time-to-solution of ten backward-Euler steps at N = 8192, r = 10.
+
+One bench "step" is one whole solve: reset the field to u^0 = 0, then ten
+time steps, each Jacobi-iterated until rho < 1e-5 (checked every 8 sweeps),
+everything resident in HBM.  The reported value is Gpoint-updates/s =
+N^2 * (sweeps of the exact method) / time-to-solution.
+
+Beside it, on the same JSON line:
+  roofline      the dominant kernel's algorithmic bytes per launch (12 bytes per
+                point per HBM pass: read u_k, read b, write u_{k+D}) divided by its
+                average launch time, measured with HIP events on the library's
+                stream during the timed solves, against MI355X's 8 TB/s;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--kernel sync|tblock|async] [--D D]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BYTES_PER_POINT_PASS = 12.0    # read u_k, read b, write the next iterate
+METRIC = "Gpoint-updates/s + time-to-solution (10 steps), N=8192 r=10; % HBM roofline"
+KERNELS = {"sync": 0, "tblock": 1, "async": 2}
+DOMINANT_CLASS = {"sync": "sync", "tblock": "tblock", "async": "async"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="C3")
+    ap.add_argument("--kernel", default="sync", choices=sorted(KERNELS))
+    ap.add_argument("--D", type=int, default=1)
+    ap.add_argument("--tile-x", type=int, default=32)
+    ap.add_argument("--tile-y", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-steps", type=int, default=2, help="time steps in the CPU sample")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (from rocprofv3 counters), if present")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, nsteps):
+    import oracle
+    import workloads
+
+    N, r = cfg["N"], cfg["r"]
+    s = workloads.source(cfg["source"], N, r)
+    t0 = time.perf_counter()
+    res = oracle.solve(N, r, s, steps=nsteps)
+    dt = time.perf_counter() - t0
+    sw = int(res.sweeps.sum())
+    return {"value": N * N * sw / dt / 1e9, "unit": "Gpoint-updates/s", "cores": oracle.get_threads(),
+            "kind": "oracle",
+            "sample": f"{cfg['name']} time steps 1-{nsteps} of 10 ({sw} sweeps, {dt:.1f} s), "
+                      f"OpenMP over rows, float32"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the solver runs on a single MI355X "
+              "(multi-GPU sharding is not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import jacobi_stencil_amd as jac
+    import workloads
+
+    cfg = dict(workloads.CONFIGS[args.config], name=args.config)
+    N, r = cfg["N"], cfg["r"]
+    if isinstance(r, tuple):
+        r = r[-1]
+        cfg["r"] = r
+    nsteps = cfg["steps"]
+    s = workloads.source(cfg["source"], N, r)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sol = jac.Solver(N, r, s, stream=stream)
+    opts = jac.jac_opts_default(kernel=KERNELS[args.kernel], D=args.D, tile_x=args.tile_x,
+                                tile_y=args.tile_y)
+
+    def one_solve():
+        sol.reset()
+        return sol.solve(nsteps, opts)
+
+    for _ in range(args.warmup):
+        one_solve()
+    torch.cuda.synchronize()
+
+    sol.profile(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    sweeps = None
+    for _ in range(args.steps):
+        _, sweeps, rho = one_solve()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    cls = DOMINANT_CLASS[args.kernel]
+    k_ms, k_n = sol.profile_read(cls)
+    noop_ms, noop_n = sol.profile_read("noop")
+    sol.profile(False)
+
+    ms_per_step = elapsed / args.steps * 1e3
+    total_sweeps = int(sweeps.sum())
+    value = N * N * total_sweeps / (ms_per_step / 1e3) / 1e9
+    D = 1 if args.kernel == "sync" else args.D
+    launch_ms = k_ms / max(k_n, 1)
+    bytes_per_launch = BYTES_PER_POINT_PASS * N * N
+    achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic):
+        t = json.load(open(args.traffic))
+        key = f"{args.config}:{args.kernel}:D{D}"
+        if key in t and t[key].get("source_sha256") == _kernel_source_hash():
+            traffic = t[key]["bytes_per_launch"]
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "Gpoint-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: N={N} r={r:g} {cfg['source']} source, {nsteps} backward-Euler "
+                               f"steps, Jacobi to rho<1e-5 checked every 8 sweeps",
+                   "N": N, "r": r, "source": cfg["source"], "time_steps": nsteps, "kernel": args.kernel,
+                   "D": D, "tile": [args.tile_x, args.tile_y] if args.kernel == "async" else None},
+        "time_to_solution_ms": round(ms_per_step, 3),
+        "sweeps_per_solve": total_sweeps,
+        "sweeps_per_step": sweeps.tolist(),
+        "pct_hbm_roofline_model": round(100.0 * value * BYTES_PER_POINT_PASS / D / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel_class": cls, "launches": k_n, "avg_launch_us": round(launch_ms * 1e3, 3),
+                     "bytes_per_launch": bytes_per_launch, "noop_launches": noop_n},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_steps)
+    sol.close()
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "jacobi_stencil_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * jacobi.h -- C interface of libjacobi: backward-Euler implicit diffusion on
+ * one MI355X (gfx950), solved step by step with point Jacobi.
+ *
+ * The method is the one of page "stencil-jacobian.vercel.app":
+ *   section 01 "The problem": du/dt = alpha*lap(u) + f on an N x N grid of
+ *     unknowns (unit square), ten backward-Euler steps in float32; each step
+ *     solves  (1+4r) u - r (uE+uW+uN+uS) = b,  b = u^n + dt*f with u^n held
+ *     fixed; the top boundary is held at 100 and the other sides at 0; a step
+ *     has converged when rho = ||b_A - A u||_inf / ||b_A||_inf < tol (1e-5),
+ *     tested every M (8) sweeps with the residual in difference form.
+ *   section 02 "Method": the synchronous sweep (one launch per sweep, fused
+ *     right-hand side), the block-asynchronous sweep (tile plus a frozen
+ *     one-cell halo, D in-tile sweeps) and exact temporal blocking (a D-cell
+ *     ghost zone, D sweeps per pass, identical to D synchronous sweeps); all
+ *     arithmetic is round-to-nearest float32 with no fused multiply-add.
+ *
+ * Readings where the page is silent (the same readings as the test oracle):
+ *   - N counts unknowns; u^0 = 0; each step starts from u^n.
+ *   - ||b||_inf in rho is the norm of b_A = b + r*g, g = 100 on the top row of
+ *     unknowns (the boundary data carried to the right-hand side).
+ *   - operation order: S = ((uE+uW)+uN)+uS, u' = (b + r*S)/(1+4r);
+ *     e = (((uE-C)+(uW-C))+(uN-C))+(uS-C), res = (b-C) + r*e;
+ *     rho = fl(max|res| / ||b_A||).  Subnormals are kept.
+ *   - the check after sweeps M, 2M, ... looks at the newest iterate; a step's
+ *     sweep count is therefore a multiple of the check interval.
+ *
+ * Conventions: every array handed across this interface is N x N float32,
+ * row-major, row 0 next to the top (100) boundary.  All device work is
+ * enqueued on the HIP stream given to jac_create; calls on one context are not
+ * thread-safe.  Every function returns a jac_status; the message of the last
+ * failure on the calling thread is jac_last_error().
+ */
+#ifndef LIBJACOBI_H
+#define LIBJACOBI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct jac_ctx* jac_t;
+
+enum jac_status {
+    JAC_OK = 0,
+    JAC_EINVAL = -1,   /* bad argument: N < 1, r < 0 or not finite, opts out of range, ... */
+    JAC_ENOMEM = -2,   /* workspace too small, or host allocation failed */
+    JAC_EDEVICE = -3,  /* a HIP call failed (message names it) */
+    JAC_ENOCONV = -4,  /* max_sweeps reached without rho < tol */
+    JAC_ENAN = -5      /* rho is NaN (a NaN or Inf reached the field) */
+};
+
+/* Sweep kernels. */
+enum jac_kernel {
+    JAC_SYNC = 0,    /* (a) one synchronous sweep per launch */
+    JAC_TBLOCK = 1,  /* (b) exact temporal blocking: D sweeps per launch, bitwise equal to (a) */
+    JAC_ASYNC = 2    /* (c) block-asynchronous: tile_x x tile_y tiles, frozen halo, D sweeps */
+};
+
+/* How the launches of a step are issued. */
+enum jac_driver {
+    JAC_LAUNCH = 0,      /* host enqueues each launch; reads each check back */
+    JAC_GRAPH = 1,       /* one HIP graph per check interval, replayed */
+    JAC_PERSISTENT = 2   /* one cooperative kernel per solve: device-side loop and decision */
+};
+
+typedef struct {
+    int32_t kernel;      /* jac_kernel */
+    int32_t driver;      /* jac_driver */
+    int32_t D;           /* sweeps per launch for TBLOCK / ASYNC (1..32); ignored for SYNC */
+    int32_t tile_x;      /* ASYNC tile width in columns (1..256) */
+    int32_t tile_y;      /* ASYNC tile height in rows (1..256) */
+    int32_t M;           /* check interval in sweeps (>= 1); the interval is max(M, D) */
+    float tol;           /* rho threshold (> 0) */
+    int32_t reserved;    /* must be 0 */
+    int64_t max_sweeps;  /* per step; a failed check at or past it ends with JAC_ENOCONV */
+} jac_opts;
+
+/* SYNC, LAUNCH, D = 1, 32 x 8 tiles, M = 8, tol = 1e-5, max_sweeps = 1e6. */
+void jac_opts_default(jac_opts* opts);
+
+/* Bytes of device workspace a context of size N needs (u twice, b, dt*f,
+ * scratch).  0 if N is out of range. */
+size_t jac_workspace_bytes(int N);
+
+/*
+ * Create a context for an N x N grid with coupling r = alpha*dt/h^2 (>= 0).
+ *   source_host  N*N floats, s = dt*f, copied during the call; NULL means 0.
+ *   workspace    device memory of at least jac_workspace_bytes(N) bytes,
+ *                256-byte aligned, owned by the caller, not freed by the
+ *                library, and used by no one else while the context lives.
+ *   stream       hipStream_t for every launch and copy (NULL: the null stream).
+ * The field starts at u^0 = 0.  On success *out holds the context.
+ */
+int jac_create(int N, float r, const float* source_host, void* workspace, size_t ws_bytes,
+               void* stream, jac_t* out);
+
+/* One backward-Euler step: b = u^n + s, then Jacobi until rho < tol.  On
+ * return the field is u^{n+1} and *sweeps / *rho (either may be NULL) hold the
+ * sweep count and the rho of the accepted iterate.  For SYNC and TBLOCK the
+ * result is bitwise identical to the oracle's for the same M. */
+int jac_step(jac_t ctx, const jac_opts* opts, int64_t* sweeps, float* rho);
+
+/* nsteps steps; sweeps[n] and rho[n] for each (arrays of nsteps, may be NULL).
+ * Stops at the first step that fails (ENOCONV / ENAN): the field is that
+ * step's last checked iterate, later entries are 0 and NaN. */
+int jac_solve(jac_t ctx, int nsteps, const jac_opts* opts, int64_t* sweeps, float* rho);
+
+/* Throughput entry: b = u^n + s, then exactly nsweeps sweeps with no checks;
+ * the field is left at the last iterate.  If rho != NULL it receives the rho
+ * of that iterate (one extra residual pass). */
+int jac_sweep(jac_t ctx, const jac_opts* opts, int64_t nsweeps, float* rho);
+
+/* Copy the current field to / from host memory (N*N floats).  Blocking. */
+int jac_get_field(jac_t ctx, float* host_out);
+int jac_set_field(jac_t ctx, const float* host_in);
+
+/* Set the field back to u^0 = 0 (device-side fill, no host traffic). */
+int jac_reset(jac_t ctx);
+
+/* Release the context (not the workspace).  NULL is accepted. */
+int jac_destroy(jac_t ctx);
+
+/* Message of the last failure on this thread ("" if none). */
+const char* jac_last_error(void);
+
+/*
+ * Launch timing.  While enabled, every kernel launch of the library is
+ * bracketed by HIP events on the context's stream; jac_profile_read returns
+ * the summed device time and the launch count of one kernel class since the
+ * last enable.  Classes: 0 right-hand side, 1 sync sweep, 2 sync sweep with
+ * check, 3 temporal-blocking launch, 4 block-async launch, 5 residual only,
+ * 6 persistent solve, 7 launches issued ahead of a check that stopped the
+ * step (they return at once and do no sweep).
+ */
+int jac_profile(jac_t ctx, int enable);
+int jac_profile_read(jac_t ctx, int kclass, double* ms_total, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBJACOBI_H */

@@ -1,0 +1,169 @@
+// jacobi_internal.h -- geometry, scratch layout and device helpers shared by
+// the HIP sources of libjacobi.  Not part of the public interface
+// (include/jacobi.h is).
+//
+// The method (page "stencil-jacobian.vercel.app", sections 01 and 02): each
+// backward-Euler step solves (1+4r) u - r (uE+uW+uN+uS) = b with b = u^n + dt*f,
+// the top boundary at 100 and the other sides at 0, by point Jacobi until
+// rho = ||b_A - A u||_inf / ||b_A||_inf < tol, checked every M sweeps.  Every
+// kernel performs the same float32 operations in the same order, each rounded
+// to nearest, none fused (the library is compiled with -ffp-contract=off):
+//   sweep     S = ((uE + uW) + uN) + uS;  u' = (b + r*S) / d,  d = 1 + 4r
+//   residual  e = (((uE-C) + (uW-C)) + (uN-C)) + (uS-C);  res = (b - C) + r*e
+//   norm      bA = max |b + r*g|, g = 100 on the top row of unknowns, else 0
+//   decision  rho = R / bA, R = max |res|; a step stops when !(rho >= tol)
+//             (converged when rho < tol, failed when rho is NaN).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jac {
+
+// ---------------------------------------------------------------- layout
+//
+// Every grid (u0, u1, b, s) is one "plane" of (N + 2*kPad) rows of pitch P
+// floats.  Unknown (i, j) -- i the row from the top, j the column -- lives at
+// origin + i*P + j with origin = kPad*P + kPad.  Row -1, row N, column -1 and
+// column N are the ghost ring (top row 100 in u0/u1, everything else 0); the
+// remaining padding is 0 and is never written after set-up.  kPad = 64 floats
+// keeps column 0 of every row on a 256-byte boundary (P is a multiple of 64)
+// and leaves room for halo loads of up to 63 cells beyond the ghost ring.
+constexpr int kPad = 64;
+constexpr float kTop = 100.0f;
+
+struct Geom {
+    int N;          // unknowns per side
+    int P;          // row pitch in floats
+    int64_t plane;  // floats per plane (multiple of 64)
+    int64_t origin; // offset of unknown (0, 0)
+};
+
+inline Geom make_geom(int N) {
+    Geom g;
+    g.N = N;
+    g.P = ((N + 2 * kPad) + 63) / 64 * 64;
+    g.plane = (int64_t)g.P * (int64_t)(N + 2 * kPad);
+    g.origin = (int64_t)kPad * g.P + kPad;
+    return g;
+}
+
+// Device scratch words (inside the caller's workspace, after the planes).
+// The accumulators reset themselves: the last block of the kernel that fills
+// one reads it out and writes 0 back, so no clearing pass is ever needed.
+struct Scratch {
+    uint32_t acc_R;    // bit pattern of max |res| of the running check (0 between checks)
+    uint32_t cnt_R;    // blocks of the running check that have finished
+    uint32_t acc_bA;   // bit pattern of the running max |b_A|
+    uint32_t cnt_bA;
+    uint32_t bA_bits;  // ||b_A||_inf of the current step
+    uint32_t stop;     // 1 once a check of the current step has decided to stop
+    uint32_t pad[58];
+};
+static_assert(sizeof(Scratch) == 256, "scratch block is 256 bytes");
+
+// Host-visible results, in pinned host memory the device writes directly.
+constexpr int kRing = 64;   // check results kept in flight
+constexpr uint32_t kEmpty = 0xFFFFFFFFu;  // never a |res| bit pattern (sign bit set)
+struct Mailbox {
+    uint32_t bA_bits;
+    uint32_t pad[15];
+    uint32_t R[kRing];
+};
+
+// Arguments every sweep-like kernel takes.
+struct StepArgs {
+    Geom g;
+    float r, d, tol;
+    Scratch* sc;
+    Mailbox* mail;
+    int slot;       // mailbox slot for this kernel's check (if it makes one)
+};
+
+// ---------------------------------------------------------------- device
+
+__device__ __forceinline__ float jacobi_update(float uE, float uW, float uN, float uS,
+                                               float b, float r, float d) {
+    float S = uE + uW;
+    S = S + uN;
+    S = S + uS;
+    float t = r * S;
+    float n = b + t;
+    return n / d;
+}
+
+__device__ __forceinline__ uint32_t residual_bits(float C, float uE, float uW, float uN, float uS,
+                                                  float b, float r) {
+    float e = (uE - C) + (uW - C);
+    e = e + (uN - C);
+    e = e + (uS - C);
+    float bc = b - C;
+    float t = r * e;
+    return __float_as_uint(fabsf(bc + t));  // NaN (any payload) sorts above +Inf
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        uint32_t w = (uint32_t)__shfl_xor((int)v, o, 64);
+        v = v > w ? v : w;
+    }
+    return v;
+}
+
+// Blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous
+// range of logical tiles so that vertically adjacent tiles (which share halo
+// rows) sit behind the same L2.  nblocks must be a multiple of 8; logical ids
+// beyond the tile count are idle blocks.
+__device__ __forceinline__ int xcd_logical_block(int b, int nblocks) {
+    int per = nblocks >> 3;
+    return (b & 7) * per + (b >> 3);
+}
+
+__device__ __forceinline__ bool stop_set(const Scratch* sc) {
+    return __atomic_load_n(&sc->stop, __ATOMIC_RELAXED) != 0;
+}
+
+// Block-wide max of `m`, then one atomic per block; the last block to finish
+// turns the maximum into R, publishes it and the stop decision, and resets the
+// accumulator.  Every block of the grid must call this exactly once.
+template <int WAVES>
+__device__ __forceinline__ void finish_check(uint32_t m, const StepArgs& a) {
+    __shared__ uint32_t part[WAVES];
+    m = wave_max_u32(m);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) part[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t bm = part[0];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) bm = bm > part[w] ? bm : part[w];
+        Scratch* sc = a.sc;
+        atomicMax(&sc->acc_R, bm);
+        __threadfence();
+        uint32_t done = atomicAdd(&sc->cnt_R, 1u);
+        if (done == gridDim.x - 1) {
+            __threadfence();
+            uint32_t Rb = atomicMax(&sc->acc_R, 0u);
+            float bA = __uint_as_float(__atomic_load_n(&sc->bA_bits, __ATOMIC_RELAXED));
+            float rho = __uint_as_float(Rb) / bA;
+            uint32_t stop = (rho >= a.tol) ? 0u : 1u;
+            atomicExch(&sc->acc_R, 0u);
+            atomicExch(&sc->cnt_R, 0u);
+            atomicExch(&sc->stop, stop);
+            __atomic_store_n(&a.mail->R[a.slot], Rb, __ATOMIC_RELAXED);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+// Launchers (kernels_*.hip).  All return hipSuccess or the launch error.
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
+hipError_t launch_ghosts(float* u, const Geom& g, hipStream_t s);
+hipError_t launch_rhs(const float* u, const float* src, float* b, const StepArgs& a, hipStream_t s);
+hipError_t launch_sync(const float* uin, const float* b, float* uout, bool check, const StepArgs& a,
+                       hipStream_t s);
+hipError_t launch_residual(const float* u, const float* b, const StepArgs& a, hipStream_t s);
+
+}  // namespace jac

@@ -1,0 +1,254 @@
+// kernels_sync.hip -- set-up kernels, the right-hand side, the synchronous
+// sweep (kernel a) with the residual check fused into it, and the standalone
+// residual.
+//
+// Synchronous sweep (page "stencil-jacobian.vercel.app", section 02, the
+// synchronous strategy: every point of sweep k+1 reads only sweep k, two
+// ping-pong buffers, one launch per sweep; fused right-hand side so a sweep
+// moves 12 bytes per point: read u_k, read b, write u_{k+1}).
+//
+// MI355X mapping: a wavefront owns 256 consecutive columns (4 per lane, one
+// 16-byte load per row) and walks down H rows keeping the rows above and below
+// in registers, so each row of u is read from memory about once; the west and
+// east neighbours of a lane's 4 columns are single-float loads that hit the
+// cache lines its neighbours just fetched.  Four wavefronts of a block take four
+// consecutive row bands of the same 256 columns.
+#include "jacobi_internal.h"
+
+namespace jac {
+
+// ------------------------------------------------------------ set-up
+
+__global__ void k_fill(float* __restrict__ p, int64_t n, float v) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (; i < n; i += stride) p[i] = v;
+}
+
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(k_fill, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+// Top ghost row (row -1, columns 0..N-1) = 100; the rest of the ring is the
+// zero padding already written by k_fill.
+__global__ void k_ghost_top(float* __restrict__ u, Geom g) {
+    int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < g.N) u[g.origin - g.P + j] = kTop;
+}
+
+hipError_t launch_ghosts(float* u, const Geom& g, hipStream_t s) {
+    hipLaunchKernelGGL(k_ghost_top, dim3((g.N + 255) / 256), dim3(256), 0, s, u, g);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ right-hand side
+
+// b = u^n + s for every unknown; ||b_A||_inf = max |b + r*g| with g = 100 on
+// row 0.  Also opens the step: clears the stop flag.  One thread per 4 columns
+// of one row; the grid is (column groups) x (rows).
+__global__ __launch_bounds__(256) void k_rhs(const float* __restrict__ u, const float* __restrict__ src,
+                                             float* __restrict__ b, StepArgs a) {
+    const Geom g = a.g;
+    const int col0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+    uint32_t m = 0;
+    for (int i = blockIdx.y; i < g.N; i += gridDim.y) {
+        if (col0 >= g.N) break;
+        const int64_t o = g.origin + (int64_t)i * g.P + col0;
+        float4 uu = *reinterpret_cast<const float4*>(u + o);
+        float4 ss = *reinterpret_cast<const float4*>(src + o);
+        float4 bb;
+        bb.x = uu.x + ss.x;
+        bb.y = uu.y + ss.y;
+        bb.z = uu.z + ss.z;
+        bb.w = uu.w + ss.w;
+        const float rg = a.r * (i == 0 ? kTop : 0.0f);
+        const float vb[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (col0 + c < g.N) {
+                uint32_t v = __float_as_uint(fabsf(vb[c] + rg));
+                m = m > v ? m : v;
+            }
+        }
+        if (col0 + 4 <= g.N) {
+            *reinterpret_cast<float4*>(b + o) = bb;
+        } else {
+            for (int c = 0; c < 4; ++c)
+                if (col0 + c < g.N) b[o + c] = vb[c];
+        }
+    }
+    // block max, one atomic per block, the last block publishes ||b_A||
+    __shared__ uint32_t part[4];
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t bm = part[0];
+        for (int w = 1; w < 4; ++w) bm = bm > part[w] ? bm : part[w];
+        Scratch* sc = a.sc;
+        atomicMax(&sc->acc_bA, bm);
+        __threadfence();
+        uint32_t nblk = gridDim.x * gridDim.y;
+        uint32_t done = atomicAdd(&sc->cnt_bA, 1u);
+        if (done == nblk - 1) {
+            __threadfence();
+            uint32_t v = atomicMax(&sc->acc_bA, 0u);
+            atomicExch(&sc->bA_bits, v);
+            atomicExch(&sc->acc_bA, 0u);
+            atomicExch(&sc->cnt_bA, 0u);
+            atomicExch(&sc->acc_R, 0u);
+            atomicExch(&sc->cnt_R, 0u);
+            atomicExch(&sc->stop, 0u);
+            __atomic_store_n(&a.mail->bA_bits, v, __ATOMIC_RELAXED);
+        }
+    }
+}
+
+hipError_t launch_rhs(const float* u, const float* src, float* b, const StepArgs& a, hipStream_t s) {
+    const int gx = (a.g.N + 1023) / 1024;
+    int gy = a.g.N < 1024 ? a.g.N : 1024;
+    hipLaunchKernelGGL(k_rhs, dim3(gx, gy), dim3(256), 0, s, u, src, b, a);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ sync sweep
+
+constexpr int kSyncWaves = 4;
+constexpr int kSyncRows = 16;  // rows per wavefront
+
+struct SyncTiles {
+    int tiles_x, tiles_y, blocks;
+};
+
+static inline SyncTiles sync_tiles(int N) {
+    SyncTiles t;
+    t.tiles_x = (N + 255) / 256;
+    t.tiles_y = (N + kSyncWaves * kSyncRows - 1) / (kSyncWaves * kSyncRows);
+    t.blocks = (t.tiles_x * t.tiles_y + 7) / 8 * 8;
+    return t;
+}
+
+// One row of 4 columns: the sweep and/or the residual of the middle row.
+template <bool DO_SWEEP, bool DO_CHECK>
+__device__ __forceinline__ void sync_row(const float4& up, const float4& mid, const float4& dn, const float4& bb,
+                                         float wl, float er, float r, float d, float4& o4, uint32_t& m,
+                                         int valid /* columns of the 4 that are unknowns */) {
+    if (DO_CHECK) {
+        uint32_t v0 = residual_bits(mid.x, mid.y, wl, up.x, dn.x, bb.x, r);
+        uint32_t v1 = residual_bits(mid.y, mid.z, mid.x, up.y, dn.y, bb.y, r);
+        uint32_t v2 = residual_bits(mid.z, mid.w, mid.y, up.z, dn.z, bb.z, r);
+        uint32_t v3 = residual_bits(mid.w, er, mid.z, up.w, dn.w, bb.w, r);
+        if (valid < 4) {
+            if (valid < 2) v1 = 0;
+            if (valid < 3) v2 = 0;
+            v3 = 0;
+        }
+        uint32_t v01 = v0 > v1 ? v0 : v1, v23 = v2 > v3 ? v2 : v3;
+        uint32_t v = v01 > v23 ? v01 : v23;
+        m = m > v ? m : v;
+    }
+    if (DO_SWEEP) {
+        o4.x = jacobi_update(mid.y, wl, up.x, dn.x, bb.x, r, d);
+        o4.y = jacobi_update(mid.z, mid.x, up.y, dn.y, bb.y, r, d);
+        o4.z = jacobi_update(mid.w, mid.y, up.z, dn.z, bb.z, r, d);
+        o4.w = jacobi_update(er, mid.z, up.w, dn.w, bb.w, r, d);
+    }
+}
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// One sweep u_{k+1} = J(u_k).  With CHECK the same pass also measures the
+// residual of u_k (the iterate it reads), which costs no extra memory traffic;
+// RESID_ONLY measures the residual and writes nothing.
+template <bool CHECK, bool RESID_ONLY>
+__global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, const float* __restrict__ bin,
+                                              float* __restrict__ uout, StepArgs a) {
+    constexpr bool SWEEP = !RESID_ONLY;
+    constexpr bool CHK = CHECK || RESID_ONLY;
+    constexpr int H = kSyncRows;
+    if (a.sc->stop) return;  // a previous check already stopped the step
+    const Geom g = a.g;
+    const int N = g.N, P = g.P;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tiles_x = (N + 255) / 256;
+    const int tiles_y = (N + kSyncWaves * H - 1) / (kSyncWaves * H);
+    const int t = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int wcol = (t % tiles_x) * 256;
+    const int col0 = wcol + lane * 4;
+    const int row0 = (t / tiles_x) * (kSyncWaves * H) + wave * H;
+    const float r = a.r, d = a.d;
+    uint32_t m = 0;
+    if (t < tiles_x * tiles_y && row0 < N) {
+        const int64_t o = g.origin + (int64_t)row0 * P + col0;
+        const float* pu = uin + o;
+        const float* pb = bin + o;
+        float* po = uout + o;
+        if (wcol + 256 <= N && row0 + H <= N) {
+            // interior wavefront: 256 full columns, H full rows
+            float4 up = ld4(pu - P);
+            float4 mid = ld4(pu);
+#pragma unroll
+            for (int i = 0; i < H; ++i) {
+                const float4 dn = ld4(pu + (int64_t)(i + 1) * P);
+                const float4 bb = ld4(pb + (int64_t)i * P);
+                const float wl = pu[(int64_t)i * P - 1];
+                const float er = pu[(int64_t)i * P + 4];
+                float4 o4;
+                sync_row<SWEEP, CHK>(up, mid, dn, bb, wl, er, r, d, o4, m, 4);
+                if (SWEEP) *reinterpret_cast<float4*>(po + (int64_t)i * P) = o4;
+                up = mid;
+                mid = dn;
+            }
+        } else if (col0 < N) {
+            // edge wavefront: ragged rows and/or columns
+            const int rows = (N - row0) < H ? (N - row0) : H;
+            const int valid = (N - col0) < 4 ? (N - col0) : 4;
+            float4 up = ld4(pu - P);
+            float4 mid = ld4(pu);
+            for (int i = 0; i < rows; ++i) {
+                const float4 dn = ld4(pu + (int64_t)(i + 1) * P);
+                const float4 bb = ld4(pb + (int64_t)i * P);
+                const float wl = pu[(int64_t)i * P - 1];
+                const float er = pu[(int64_t)i * P + 4];
+                float4 o4;
+                sync_row<SWEEP, CHK>(up, mid, dn, bb, wl, er, r, d, o4, m, valid);
+                if (SWEEP) {
+                    float* q = po + (int64_t)i * P;
+                    if (valid == 4) {
+                        *reinterpret_cast<float4*>(q) = o4;
+                    } else {
+                        q[0] = o4.x;
+                        if (valid > 1) q[1] = o4.y;
+                        if (valid > 2) q[2] = o4.z;
+                    }
+                }
+                up = mid;
+                mid = dn;
+            }
+        }
+    }
+    if (CHK) finish_check<kSyncWaves>(m, a);
+}
+
+hipError_t launch_sync(const float* uin, const float* b, float* uout, bool check, const StepArgs& a,
+                       hipStream_t s) {
+    SyncTiles t = sync_tiles(a.g.N);
+    if (check)
+        hipLaunchKernelGGL((k_sync<true, false>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, uin, b, uout, a);
+    else
+        hipLaunchKernelGGL((k_sync<false, false>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, uin, b, uout, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_residual(const float* u, const float* b, const StepArgs& a, hipStream_t s) {
+    SyncTiles t = sync_tiles(a.g.N);
+    hipLaunchKernelGGL((k_sync<false, true>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, u, b,
+                       (float*)nullptr, a);
+    return hipGetLastError();
+}
+
+}  // namespace jac

@@ -1,0 +1,72 @@
+"""Write the oracle's expected results for the large workloads.
+
+Calls only the CPU oracle (oracle/) and the input generators (workloads.py);
+nothing from the HIP library.  For each workload it runs the ten
+backward-Euler steps one at a time and stores, per step, the sweep count, the
+bit pattern of rho and the SHA-256 of the N x N float32 field (row-major,
+little-endian).  The GPU parity tests compare the library's fields against
+these hashes bit for bit.
+
+    python -m tests.golden.make_expected C3          # N=8192, r=10, Gaussian
+    python -m tests.golden.make_expected C4 --steps 2
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def field_hash(u: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(u, dtype="<f4").tobytes()).hexdigest()
+
+
+def run(name: str, steps: int | None, M: int = 8) -> dict:
+    cfg = workloads.CONFIGS[name]
+    N, r, kind = cfg["N"], cfg["r"], cfg["source"]
+    steps = steps or cfg["steps"]
+    s = workloads.source(kind, N, r)
+    u = np.zeros((N, N), np.float32)
+    out = dict(config=name, N=N, r=r, source=kind, M=M, tol=1e-5, steps=steps, sweeps=[], rho_bits=[],
+               field_sha256=[], oracle_threads=oracle.get_threads(), seconds=[])
+    for n in range(steps):
+        t0 = time.time()
+        res = oracle.solve(N, r, s, u0=u, steps=1, M=M)
+        if res.status != oracle.OK:
+            raise RuntimeError(f"{name} step {n}: oracle status {res.status}")
+        u = res.u
+        out["sweeps"].append(int(res.sweeps[0]))
+        out["rho_bits"].append(f"{np.float32(res.rho[0]).view(np.uint32):08x}")
+        out["field_sha256"].append(field_hash(u))
+        out["seconds"].append(round(time.time() - t0, 2))
+        print(f"{name} step {n}: sweeps {res.sweeps[0]} rho {res.rho[0]:.6e} ({out['seconds'][-1]} s)", flush=True)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("config")
+    ap.add_argument("--steps", type=int, default=None)
+    args = ap.parse_args()
+    res = run(args.config, args.steps)
+    path = os.path.join(HERE, f"expected_{args.config}.json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    print("wrote", path)
+
+
+if __name__ == "__main__":
+    main()
