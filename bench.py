@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--tile-x", type=int, default=32)
     ap.add_argument("--tile-y", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--profile-every", type=int, default=16,
+                    help="bracket every k-th launch of a class with HIP events (0: none)")
     ap.add_argument("--cpu-steps", type=int, default=2, help="time steps in the CPU sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
@@ -100,7 +102,7 @@ def main():
         one_solve()
     torch.cuda.synchronize()
 
-    sol.profile(True)
+    sol.profile(args.profile_every)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     sweeps = None
@@ -109,15 +111,14 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     cls = DOMINANT_CLASS[args.kernel]
-    k_ms, k_n = sol.profile_read(cls)
-    noop_ms, noop_n = sol.profile_read("noop")
-    sol.profile(False)
+    launch_ms, k_n, k_timed = sol.profile_read(cls)
+    _, noop_n, _ = sol.profile_read("noop")
+    sol.profile(0)
 
     ms_per_step = elapsed / args.steps * 1e3
     total_sweeps = int(sweeps.sum())
     value = N * N * total_sweeps / (ms_per_step / 1e3) / 1e9
     D = 1 if args.kernel == "sync" else args.D
-    launch_ms = k_ms / max(k_n, 1)
     bytes_per_launch = BYTES_PER_POINT_PASS * N * N
     achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
     traffic = None
@@ -150,7 +151,8 @@ def main():
         "pct_hbm_roofline_model": round(100.0 * value * BYTES_PER_POINT_PASS / D / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel_class": cls, "launches": k_n, "avg_launch_us": round(launch_ms * 1e3, 3),
+                     "kernel_class": cls, "launches": k_n, "timed_launches": k_timed,
+                     "avg_launch_us": round(launch_ms * 1e3, 3),
                      "bytes_per_launch": bytes_per_launch, "noop_launches": noop_n},
     }
     if not args.no_cpu:

@@ -69,7 +69,7 @@ enum jac_driver {
 typedef struct {
     int32_t kernel;      /* jac_kernel */
     int32_t driver;      /* jac_driver */
-    int32_t D;           /* sweeps per launch for TBLOCK / ASYNC (1..32); ignored for SYNC */
+    int32_t D;           /* sweeps per launch: TBLOCK 1..16, ASYNC 1..32; ignored for SYNC */
     int32_t tile_x;      /* ASYNC tile width in columns (1..256) */
     int32_t tile_y;      /* ASYNC tile height in rows (1..256) */
     int32_t M;           /* check interval in sweeps (>= 1); the interval is max(M, D) */
@@ -127,16 +127,20 @@ int jac_destroy(jac_t ctx);
 const char* jac_last_error(void);
 
 /*
- * Launch timing.  While enabled, every kernel launch of the library is
- * bracketed by HIP events on the context's stream; jac_profile_read returns
- * the summed device time and the launch count of one kernel class since the
- * last enable.  Classes: 0 right-hand side, 1 sync sweep, 2 sync sweep with
- * check, 3 temporal-blocking launch, 4 block-async launch, 5 residual only,
- * 6 persistent solve, 7 launches issued ahead of a check that stopped the
- * step (they return at once and do no sweep).
+ * Launch timing.  jac_profile(ctx, k) with k > 0 counts every kernel launch of
+ * the library by class and brackets every k-th launch of each class with a
+ * pair of HIP events on the context's stream (a pair costs about 10 us of
+ * dispatch gap, so k = 1 slows small kernels noticeably); k = 0 turns it off.
+ * Enabling resets the counters.  jac_profile_read returns, for one class, the
+ * summed device time of the bracketed launches, the number of launches and
+ * the number bracketed.  Classes: 0 right-hand side, 1 sync sweep, 2 sync
+ * sweep with check, 3 temporal-blocking launch, 4 block-async launch,
+ * 5 residual only, 6 persistent solve, 7 launches issued ahead of a check that
+ * stopped the step (they return at once and do no sweep), 8 one-block
+ * reductions of a check or of ||b_A||.
  */
-int jac_profile(jac_t ctx, int enable);
-int jac_profile_read(jac_t ctx, int kclass, double* ms_total, int64_t* launches);
+int jac_profile(jac_t ctx, int every);
+int jac_profile_read(jac_t ctx, int kclass, double* ms_timed, int64_t* launches, int64_t* timed_launches);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ JAC_OK, JAC_EINVAL, JAC_ENOMEM, JAC_EDEVICE, JAC_ENOCONV, JAC_ENAN = 0, -1, -2, 
 JAC_SYNC, JAC_TBLOCK, JAC_ASYNC = 0, 1, 2
 JAC_LAUNCH, JAC_GRAPH, JAC_PERSISTENT = 0, 1, 2
 KCLASS = {"rhs": 0, "sync": 1, "sync_check": 2, "tblock": 3, "async": 4, "residual": 5, "persistent": 6,
-          "noop": 7}
+          "noop": 7, "reduce": 8}
 STATUS_NAMES = {0: "JAC_OK", -1: "JAC_EINVAL", -2: "JAC_ENOMEM", -3: "JAC_EDEVICE", -4: "JAC_ENOCONV",
                 -5: "JAC_ENAN"}
 
@@ -53,6 +53,11 @@ def load_library():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run `python -m jacobi_stencil_amd.build`")
+        # torch's HIP runtime must be loaded first: libjacobi's dependency on
+        # libamdhip64.so.7 then binds to it, and the process has one runtime
+        # whose streams and memory both sides share.
+        import torch  # noqa: F401
+
         lib = ctypes.CDLL(LIB_PATH)
         vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
         lib.jac_opts_default.argtypes = [ctypes.POINTER(jac_opts)]
@@ -71,7 +76,7 @@ def load_library():
         lib.jac_last_error.restype = ctypes.c_char_p
         lib.jac_profile.argtypes = [vp, ctypes.c_int]
         lib.jac_profile_read.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
-                                         ctypes.POINTER(i64)]
+                                         ctypes.POINTER(i64), ctypes.POINTER(i64)]
         for name in EXPORTS:
             if name not in ("jac_opts_default", "jac_workspace_bytes", "jac_last_error"):
                 getattr(lib, name).restype = ctypes.c_int
@@ -154,18 +159,20 @@ def jac_destroy(ctx) -> int:
     return load_library().jac_destroy(ctx)
 
 
-def jac_profile(ctx, enable: bool) -> int:
-    return load_library().jac_profile(ctx, 1 if enable else 0)
+def jac_profile(ctx, every: int) -> int:
+    """every = 0: off; k > 0: count all launches, time every k-th of each class."""
+    return load_library().jac_profile(ctx, int(every))
 
 
 def jac_profile_read(ctx, kclass):
-    """Returns (status, ms_total, launches); kclass is an int or a KCLASS name."""
+    """Returns (status, ms_timed, launches, timed_launches); kclass is an int or a KCLASS name."""
     if isinstance(kclass, str):
         kclass = KCLASS[kclass]
     ms = ctypes.c_double(0)
     n = ctypes.c_int64(0)
-    st = load_library().jac_profile_read(ctx, int(kclass), ctypes.byref(ms), ctypes.byref(n))
-    return st, float(ms.value), int(n.value)
+    nt = ctypes.c_int64(0)
+    st = load_library().jac_profile_read(ctx, int(kclass), ctypes.byref(ms), ctypes.byref(n), ctypes.byref(nt))
+    return st, float(ms.value), int(n.value), int(nt.value)
 
 
 # ------------------------------------------------------------------ wrapper
@@ -238,10 +245,11 @@ class Solver:
     def reset(self):
         _check(jac_reset(self.ctx))
 
-    def profile(self, enable: bool):
-        _check(jac_profile(self.ctx, enable))
+    def profile(self, every: int):
+        _check(jac_profile(self.ctx, every))
 
     def profile_read(self, kclass):
-        st, ms, n = jac_profile_read(self.ctx, kclass)
+        """(average ms of the timed launches, all launches, timed launches) of a class."""
+        st, ms, n, nt = jac_profile_read(self.ctx, kclass)
         _check(st)
-        return ms, n
+        return (ms / nt if nt else float("nan")), n, nt

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libjacobi.so")
 
-SOURCES = ["libjacobi.hip", "kernels_sync.hip"]
+SOURCES = ["libjacobi.hip", "kernels_sync.hip", "kernels_tblock.hip"]
 
 # -ffp-contract=off        : no fused multiply-add anywhere in the method's arithmetic
 # -fno-fast-math           : no reassociation, no approximate division
@@ -22,7 +22,7 @@ SOURCES = ["libjacobi.hip", "kernels_sync.hip"]
 # -fhip-fp32-correctly-rounded-divide-sqrt : '/' is the IEEE round-to-nearest quotient
 # -packed-fp32-ops off     : no packed float32 instructions are generated
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -31,19 +31,46 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def torch_lib_dir() -> str:
+    """Directory of the HIP runtime bundled with PyTorch (found without importing torch)."""
+    import importlib.util
+
+    spec = importlib.util.find_spec("torch")
+    if spec is None or not spec.submodule_search_locations:
+        raise RuntimeError("PyTorch is not installed; libjacobi shares its HIP runtime")
+    return os.path.join(list(spec.submodule_search_locations)[0], "lib")
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 target feature; that warning is harmless
     err = "\n".join(l for l in proc.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
     if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
+        raise RuntimeError(f"{cmd[0]} failed ({proc.returncode}):\n{err}")
     if err and verbose:
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object with hipcc, then link the shared library
+    against the HIP runtime bundled with PyTorch (same soname as ROCm's), so the
+    library uses only entry points that runtime has.  The Python binding loads
+    torch first; the dynamic loader then binds libjacobi to that same runtime, so
+    the process has one HIP runtime (one device context, shared streams)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        _run([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tlib = torch_lib_dir()
+    tmp = LIB + ".tmp"
+    _run(["g++", "-shared", "-o", tmp, *objs, "-Wl,--no-undefined", "-L" + tlib, "-l:libamdhip64.so",
+          "-lstdc++"], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -48,19 +48,24 @@ inline Geom make_geom(int N) {
     return g;
 }
 
-// Device scratch words (inside the caller's workspace, after the planes).
-// The accumulators reset themselves: the last block of the kernel that fills
-// one reads it out and writes 0 back, so no clearing pass is ever needed.
+// Device scratch (inside the caller's workspace, after the planes): a header
+// and an array of per-block partial maxima.  A reduction kernel writes a
+// partial per block with a plain store; a one-block kernel that runs next
+// reduces them.  (One atomic per block on a shared word serialises at the
+// memory side: thousands of blocks cost hundreds of microseconds.)
 struct Scratch {
-    uint32_t acc_R;    // bit pattern of max |res| of the running check (0 between checks)
-    uint32_t cnt_R;    // blocks of the running check that have finished
-    uint32_t acc_bA;   // bit pattern of the running max |b_A|
-    uint32_t cnt_bA;
     uint32_t bA_bits;  // ||b_A||_inf of the current step
     uint32_t stop;     // 1 once a check of the current step has decided to stop
-    uint32_t pad[58];
+    uint32_t pad[62];
+    // followed by uint32_t partial[npart_cap]
 };
-static_assert(sizeof(Scratch) == 256, "scratch block is 256 bytes");
+static_assert(sizeof(Scratch) == 256, "scratch header is 256 bytes");
+
+__host__ __device__ inline uint32_t* scratch_partials(Scratch* sc) { return reinterpret_cast<uint32_t*>(sc + 1); }
+
+// Partial-maximum slots a context of size N reserves; every kernel that writes
+// partials is launched with at most this many blocks (checked on the host).
+inline int64_t partial_cap(int N) { return (int64_t)N * N / 1024 + 65536; }
 
 // Host-visible results, in pinned host memory the device writes directly.
 constexpr int kRing = 64;   // check results kept in flight
@@ -124,35 +129,24 @@ __device__ __forceinline__ bool stop_set(const Scratch* sc) {
     return __atomic_load_n(&sc->stop, __ATOMIC_RELAXED) != 0;
 }
 
-// Block-wide max of `m`, then one atomic per block; the last block to finish
-// turns the maximum into R, publishes it and the stop decision, and resets the
-// accumulator.  Every block of the grid must call this exactly once.
+// Block-wide max of `m` stored to the block's partial slot.  Every block of a
+// reducing launch calls this exactly once (idle blocks with m = 0).
 template <int WAVES>
-__device__ __forceinline__ void finish_check(uint32_t m, const StepArgs& a) {
+__device__ __forceinline__ void store_block_max(uint32_t m, Scratch* sc, int64_t slot) {
     __shared__ uint32_t part[WAVES];
     m = wave_max_u32(m);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (WAVES == 1) {
+        if (lane == 0) scratch_partials(sc)[slot] = m;
+        return;
+    }
     if (lane == 0) part[wave] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t bm = part[0];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) bm = bm > part[w] ? bm : part[w];
-        Scratch* sc = a.sc;
-        atomicMax(&sc->acc_R, bm);
-        __threadfence();
-        uint32_t done = atomicAdd(&sc->cnt_R, 1u);
-        if (done == gridDim.x - 1) {
-            __threadfence();
-            uint32_t Rb = atomicMax(&sc->acc_R, 0u);
-            float bA = __uint_as_float(__atomic_load_n(&sc->bA_bits, __ATOMIC_RELAXED));
-            float rho = __uint_as_float(Rb) / bA;
-            uint32_t stop = (rho >= a.tol) ? 0u : 1u;
-            atomicExch(&sc->acc_R, 0u);
-            atomicExch(&sc->cnt_R, 0u);
-            atomicExch(&sc->stop, stop);
-            __atomic_store_n(&a.mail->R[a.slot], Rb, __ATOMIC_RELAXED);
-        }
+        scratch_partials(sc)[slot] = bm;
     }
 }
 
@@ -162,8 +156,21 @@ __device__ __forceinline__ void finish_check(uint32_t m, const StepArgs& a) {
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_ghosts(float* u, const Geom& g, hipStream_t s);
 hipError_t launch_rhs(const float* u, const float* src, float* b, const StepArgs& a, hipStream_t s);
+// Reduce npart partials.  norm: they are |b_A| maxima -- publish ||b_A|| and
+// clear the stop flag.  Otherwise they are |res| maxima of a check -- unless
+// the step has already stopped, publish R in mailbox slot a.slot and set the
+// stop flag when !(R / ||b_A|| >= tol).
+hipError_t launch_reduce(int64_t npart, bool norm, const StepArgs& a, hipStream_t s);
+// Blocks each launch will use (for the host's partial-slot check).
+int64_t rhs_blocks(int N);
+int64_t sync_blocks(int N);
+int64_t tblock_blocks(int N, int D, int H);
+int tblock_rows(int N, int D);
 hipError_t launch_sync(const float* uin, const float* b, float* uout, bool check, const StepArgs& a,
                        hipStream_t s);
 hipError_t launch_residual(const float* u, const float* b, const StepArgs& a, hipStream_t s);
+// D sweeps (1..16) in one pass; H = output rows per wavefront band (< 1: automatic).
+hipError_t launch_tblock(const float* uin, const float* b, float* uout, int D, bool check, const StepArgs& a,
+                         int H, hipStream_t s);
 
 }  // namespace jac

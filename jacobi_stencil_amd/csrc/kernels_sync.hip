@@ -47,9 +47,9 @@ hipError_t launch_ghosts(float* u, const Geom& g, hipStream_t s) {
 
 // ------------------------------------------------------------ right-hand side
 
-// b = u^n + s for every unknown; ||b_A||_inf = max |b + r*g| with g = 100 on
-// row 0.  Also opens the step: clears the stop flag.  One thread per 4 columns
-// of one row; the grid is (column groups) x (rows).
+// b = u^n + s for every unknown, and per-block maxima of |b + r*g| (g = 100
+// on row 0) for ||b_A||_inf.  One thread per 4 columns of one row; the grid
+// is (column groups) x (rows).
 __global__ __launch_bounds__(256) void k_rhs(const float* __restrict__ u, const float* __restrict__ src,
                                              float* __restrict__ b, StepArgs a) {
     const Geom g = a.g;
@@ -81,37 +81,56 @@ __global__ __launch_bounds__(256) void k_rhs(const float* __restrict__ u, const 
                 if (col0 + c < g.N) b[o + c] = vb[c];
         }
     }
-    // block max, one atomic per block, the last block publishes ||b_A||
-    __shared__ uint32_t part[4];
-    m = wave_max_u32(m);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t bm = part[0];
-        for (int w = 1; w < 4; ++w) bm = bm > part[w] ? bm : part[w];
-        Scratch* sc = a.sc;
-        atomicMax(&sc->acc_bA, bm);
-        __threadfence();
-        uint32_t nblk = gridDim.x * gridDim.y;
-        uint32_t done = atomicAdd(&sc->cnt_bA, 1u);
-        if (done == nblk - 1) {
-            __threadfence();
-            uint32_t v = atomicMax(&sc->acc_bA, 0u);
-            atomicExch(&sc->bA_bits, v);
-            atomicExch(&sc->acc_bA, 0u);
-            atomicExch(&sc->cnt_bA, 0u);
-            atomicExch(&sc->acc_R, 0u);
-            atomicExch(&sc->cnt_R, 0u);
-            atomicExch(&sc->stop, 0u);
-            __atomic_store_n(&a.mail->bA_bits, v, __ATOMIC_RELAXED);
-        }
-    }
+    store_block_max<4>(m, a.sc, (int64_t)blockIdx.y * gridDim.x + blockIdx.x);
+}
+
+int64_t rhs_blocks(int N) {
+    const int64_t gx = (N + 1023) / 1024;
+    const int64_t gy = N < 1024 ? N : 1024;
+    return gx * gy;
 }
 
 hipError_t launch_rhs(const float* u, const float* src, float* b, const StepArgs& a, hipStream_t s) {
     const int gx = (a.g.N + 1023) / 1024;
     int gy = a.g.N < 1024 ? a.g.N : 1024;
     hipLaunchKernelGGL(k_rhs, dim3(gx, gy), dim3(256), 0, s, u, src, b, a);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ reductions
+
+constexpr int kReduceThreads = 1024;
+
+__global__ __launch_bounds__(kReduceThreads) void k_reduce(int64_t npart, int norm, StepArgs a) {
+    Scratch* sc = a.sc;
+    if (!norm && sc->stop) return;  // the step stopped at an earlier check
+    const uint32_t* part = scratch_partials(sc);
+    uint32_t m = 0;
+    for (int64_t i = threadIdx.x; i < npart; i += kReduceThreads) {
+        const uint32_t v = part[i];
+        m = m > v ? m : v;
+    }
+    m = wave_max_u32(m);
+    __shared__ uint32_t w[kReduceThreads / 64];
+    if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t bm = w[0];
+        for (int k = 1; k < kReduceThreads / 64; ++k) bm = bm > w[k] ? bm : w[k];
+        if (norm) {
+            sc->bA_bits = bm;
+            sc->stop = 0u;
+            a.mail->bA_bits = bm;
+        } else {
+            const float rho = __uint_as_float(bm) / __uint_as_float(sc->bA_bits);
+            sc->stop = (rho >= a.tol) ? 0u : 1u;
+            a.mail->R[a.slot] = bm;
+        }
+    }
+}
+
+hipError_t launch_reduce(int64_t npart, bool norm, const StepArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(k_reduce, dim3(1), dim3(kReduceThreads), 0, s, npart, norm ? 1 : 0, a);
     return hipGetLastError();
 }
 
@@ -124,7 +143,7 @@ struct SyncTiles {
     int tiles_x, tiles_y, blocks;
 };
 
-static inline SyncTiles sync_tiles(int N) {
+static SyncTiles sync_tiles(int N) {
     SyncTiles t;
     t.tiles_x = (N + 255) / 256;
     t.tiles_y = (N + kSyncWaves * kSyncRows - 1) / (kSyncWaves * kSyncRows);
@@ -231,8 +250,10 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
             }
         }
     }
-    if (CHK) finish_check<kSyncWaves>(m, a);
+    if (CHK) store_block_max<kSyncWaves>(m, a.sc, blockIdx.x);
 }
+
+int64_t sync_blocks(int N) { return sync_tiles(N).blocks; }
 
 hipError_t launch_sync(const float* uin, const float* b, float* uout, bool check, const StepArgs& a,
                        hipStream_t s) {

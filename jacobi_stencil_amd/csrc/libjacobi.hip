@@ -45,18 +45,22 @@ int fail(int code, const std::string& msg) {
 
 constexpr int kMaxN = 65536;
 constexpr int kMaxD = 32;
-constexpr int kClasses = 8;
+constexpr int kMaxTBlockD = 16;
+constexpr int kClasses = 9;
 
 enum KClass {
     KC_RHS = 0, KC_SYNC = 1, KC_SYNC_CHECK = 2, KC_TBLOCK = 3, KC_ASYNC = 4, KC_RESID = 5, KC_PERSIST = 6,
-    KC_NOOP = 7  // launches issued ahead of a check that then stopped the step: they return at once
+    KC_NOOP = 7,   // launches issued ahead of a check that then stopped the step: they return at once
+    KC_REDUCE = 8  // one-block reductions of a check's or a norm's partial maxima
 };
 
-struct Pending {
-    hipEvent_t e0, e1;
+// One launch as seen by the launch timer.
+struct Rec {
     int cls;
-    int64_t group;  // check group within the step, -1 outside a step's sweep loop
-    bool first;     // first launch of its group (the one that carries the check)
+    int64_t step;    // serial of the step it belongs to
+    int64_t group;   // check group within the step, -1 outside the sweep loop
+    bool first;      // first launch of its group (the one that carries the check)
+    hipEvent_t e0, e1;  // timing pair when this launch was sampled, else null
 };
 
 }  // namespace
@@ -70,18 +74,22 @@ struct jac_ctx {
     float* b;
     float* s;
     Scratch* sc;
+    int64_t npart_cap;
     Mailbox* mail;   // pinned host memory written by the device
     int cur;         // u[cur] holds u^n
     hipEvent_t ev[kRing];
     int start_buf[kRing];
     // launch timing
-    bool prof;
+    int prof_every;  // 0: off; k: time every k-th launch of each class
     std::vector<hipEvent_t> free_ev;
-    std::vector<Pending> pending;
-    int64_t cur_group;   // group being enqueued (tags profile entries)
+    std::vector<Rec> recs;
+    int64_t step_serial;
+    int64_t cur_group;
     bool cur_first;
+    int64_t seen[kClasses];
     double ms[kClasses];
     int64_t cnt[kClasses];
+    int64_t timed_n[kClasses];
 };
 
 namespace {
@@ -98,33 +106,36 @@ StepArgs base_args(const jac_ctx* c, float tol) {
     return a;
 }
 
-// Fold finished timing pairs into the per-class totals.  Entries of groups
-// >= keep_from are left pending (their class may still change to KC_NOOP).
-int drain_profile(jac_ctx* c, int64_t keep_from = INT64_MAX) {
+// Fold the records of steps before `keep_step` into the per-class totals.
+int drain_profile(jac_ctx* c, int64_t keep_step = INT64_MAX) {
     size_t w = 0;
-    for (size_t i = 0; i < c->pending.size(); ++i) {
-        Pending& p = c->pending[i];
-        if (p.group >= keep_from) {
-            c->pending[w++] = p;
+    for (size_t i = 0; i < c->recs.size(); ++i) {
+        Rec& p = c->recs[i];
+        if (p.step >= keep_step) {
+            c->recs[w++] = p;
             continue;
         }
-        float ms = 0.0f;
-        JAC_HIP(hipEventSynchronize(p.e1));
-        JAC_HIP(hipEventElapsedTime(&ms, p.e0, p.e1));
-        c->ms[p.cls] += ms;
         c->cnt[p.cls] += 1;
-        c->free_ev.push_back(p.e0);
-        c->free_ev.push_back(p.e1);
+        if (p.e0) {
+            float ms = 0.0f;
+            JAC_HIP(hipEventSynchronize(p.e1));
+            JAC_HIP(hipEventElapsedTime(&ms, p.e0, p.e1));
+            c->ms[p.cls] += ms;
+            c->timed_n[p.cls] += 1;
+            c->free_ev.push_back(p.e0);
+            c->free_ev.push_back(p.e1);
+        }
     }
-    c->pending.resize(w);
+    c->recs.resize(w);
     return JAC_OK;
 }
 
-// A stop at check group gs: every launch after the first of group gs returned
-// at once; re-class them so they do not count as sweeps.
+// A stop at check group gs of the current step: every sweep launch after the
+// first of group gs returned at once; re-class them so they do not count.
 void mark_noops(jac_ctx* c, int64_t gs) {
-    for (Pending& p : c->pending)
-        if (p.group > gs || (p.group == gs && !p.first)) p.cls = KC_NOOP;
+    for (Rec& p : c->recs)
+        if (p.step == c->step_serial && p.cls != KC_REDUCE && (p.group > gs || (p.group == gs && !p.first)))
+            p.cls = KC_NOOP;
 }
 
 int take_event(jac_ctx* c, hipEvent_t* e) {
@@ -137,12 +148,15 @@ int take_event(jac_ctx* c, hipEvent_t* e) {
     return JAC_OK;
 }
 
-// Run `fn` (which enqueues one kernel) bracketed by timing events when
-// profiling is on.
+// Run `fn` (which enqueues one kernel) and, when the launch timer is on,
+// record it -- bracketed by a pair of HIP events if it is sampled.  Events
+// between launches cost ~10 us of dispatch gap each, so only every k-th launch
+// of a class is bracketed.
 template <class F>
 int timed(jac_ctx* c, int cls, F&& fn) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (c->prof) {
+    const bool sample = c->prof_every > 0 && (c->seen[cls]++ % c->prof_every) == 0;
+    if (sample) {
         int st = take_event(c, &e0);
         if (st) return st;
         st = take_event(c, &e1);
@@ -151,11 +165,9 @@ int timed(jac_ctx* c, int cls, F&& fn) {
     }
     hipError_t e = fn();
     if (e != hipSuccess) return fail(JAC_EDEVICE, std::string("kernel launch: ") + hipGetErrorString(e));
-    if (c->prof) {
-        JAC_HIP(hipEventRecord(e1, c->stream));
-        c->pending.push_back({e0, e1, cls, c->cur_group, c->cur_first});
-        c->cur_first = false;
-    }
+    if (sample) JAC_HIP(hipEventRecord(e1, c->stream));
+    if (c->prof_every > 0) c->recs.push_back({cls, c->step_serial, c->cur_group, c->cur_first, e0, e1});
+    if (cls != KC_REDUCE) c->cur_first = false;
     return JAC_OK;
 }
 
@@ -172,7 +184,8 @@ int check_opts(const jac_ctx* c, const jac_opts* o) {
     if (o->kernel != JAC_SYNC && (o->D < 1 || o->D > kMaxD)) return fail(JAC_EINVAL, "D must be in 1..32");
     if (o->kernel == JAC_ASYNC && (o->tile_x < 1 || o->tile_x > 256 || o->tile_y < 1 || o->tile_y > 256))
         return fail(JAC_EINVAL, "tile_x and tile_y must be in 1..256");
-    if (o->kernel != JAC_SYNC) return fail(JAC_EINVAL, "this kernel is not available in this build");
+    if (o->kernel == JAC_TBLOCK && o->D > kMaxTBlockD) return fail(JAC_EINVAL, "TBLOCK needs D in 1..16");
+    if (o->kernel == JAC_ASYNC) return fail(JAC_EINVAL, "this kernel is not available in this build");
     if (o->driver != JAC_LAUNCH) return fail(JAC_EINVAL, "this driver is not available in this build");
     (void)c;
     return JAC_OK;
@@ -185,29 +198,53 @@ int64_t check_interval(const jac_opts* o) {
     return spl > o->M ? spl : o->M;
 }
 
+// Reduce the partial maxima a check launch of `npart` blocks wrote into
+// mailbox slot `slot` (and the device stop flag).
+int enqueue_check_reduce(jac_ctx* c, int64_t npart, float tol, int slot) {
+    if (npart > c->npart_cap) return fail(JAC_EDEVICE, "launch exceeds the partial-maximum slots");
+    StepArgs a = base_args(c, tol);
+    a.slot = slot;
+    return timed(c, KC_REDUCE, [&] { return launch_reduce(npart, false, a, c->stream); });
+}
+
 // Enqueue one launch of `m` sweeps from u[*buf] into the other buffer; with
-// `check` it also measures the residual of its input into mailbox slot `slot`.
+// `check` it also measures the residual of its input and reduces it into
+// mailbox slot `slot`.
 int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, int* buf) {
     StepArgs a = base_args(c, o->tol);
     a.slot = slot;
     const float* in = c->u[*buf];
     float* out = c->u[*buf ^ 1];
     int st = JAC_OK;
+    int64_t npart = 0;
     switch (o->kernel) {
         case JAC_SYNC:
             (void)m;
+            npart = sync_blocks(c->N);
+            if (check && npart > c->npart_cap) return fail(JAC_EDEVICE, "sync grid exceeds partial slots");
             st = timed(c, check ? KC_SYNC_CHECK : KC_SYNC,
                        [&] { return launch_sync(in, c->b, out, check, a, c->stream); });
             break;
+        case JAC_TBLOCK: {
+            const int H = tblock_rows(c->N, m);
+            npart = tblock_blocks(c->N, m, H);
+            if (check && npart > c->npart_cap) return fail(JAC_EDEVICE, "tblock grid exceeds partial slots");
+            st = timed(c, KC_TBLOCK, [&] { return launch_tblock(in, c->b, out, m, check, a, H, c->stream); });
+            break;
+        }
         default:
             return fail(JAC_EINVAL, "kernel not available");
     }
     if (st) return st;
+    if (check) {
+        st = enqueue_check_reduce(c, npart, o->tol, slot);
+        if (st) return st;
+    }
     *buf ^= 1;
     return JAC_OK;
 }
 
-// Enqueue the launches of sweeps [first, first + count) of a group.
+// Enqueue the launches of `count` sweeps; the first may carry a check.
 int enqueue_sweeps(jac_ctx* c, const jac_opts* o, int64_t count, bool check_first, int slot, int* buf) {
     const int spl = sweeps_per_launch(o);
     bool check = check_first;
@@ -221,40 +258,64 @@ int enqueue_sweeps(jac_ctx* c, const jac_opts* o, int64_t count, bool check_firs
     return JAC_OK;
 }
 
+// b = u^n + s and ||b_A|| (which also clears the stop flag).
 int enqueue_rhs(jac_ctx* c, float tol) {
     StepArgs a = base_args(c, tol);
-    return timed(c, KC_RHS, [&] { return launch_rhs(c->u[c->cur], c->s, c->b, a, c->stream); });
+    const int64_t npart = rhs_blocks(c->N);
+    if (npart > c->npart_cap) return fail(JAC_EDEVICE, "rhs grid exceeds partial slots");
+    int st = timed(c, KC_RHS, [&] { return launch_rhs(c->u[c->cur], c->s, c->b, a, c->stream); });
+    if (st) return st;
+    return timed(c, KC_REDUCE, [&] { return launch_reduce(npart, true, a, c->stream); });
+}
+
+// The residual of u[buf] alone (no sweep), reduced into mailbox slot `slot`.
+int enqueue_residual(jac_ctx* c, float tol, int buf, int slot) {
+    StepArgs a = base_args(c, tol);
+    a.slot = slot;
+    const float* in = c->u[buf];
+    int st = timed(c, KC_RESID, [&] { return launch_residual(in, c->b, a, c->stream); });
+    if (st) return st;
+    return enqueue_check_reduce(c, sync_blocks(c->N), tol, slot);
 }
 
 uint32_t read_mail(const volatile uint32_t* p) { return *p; }
 
+float mail_float(const volatile uint32_t* p) {
+    const uint32_t b = *p;
+    float f;
+    std::memcpy(&f, &b, 4);
+    return f;
+}
+
 int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out) {
     const int64_t L = check_interval(o);
+    c->step_serial += 1;
     c->cur_group = -1;
     c->cur_first = false;
+    if (c->prof_every > 0) {
+        int s0 = drain_profile(c, c->step_serial - 1);  // earlier steps have finished
+        if (s0) return s0;
+    }
     int st = enqueue_rhs(c, o->tol);
     if (st) return st;
     int buf = c->cur;
     c->cur_group = 0;
     c->cur_first = true;
-    st = enqueue_sweeps(c, o, L, false, 0, &buf);   // group 0: sweeps 1..L
+    st = enqueue_sweeps(c, o, L, false, 0, &buf);  // group 0: sweeps 1..L
     if (st) return st;
 
-    int64_t g_enq = 1;          // next group to enqueue
+    int64_t g_enq = 1;  // next group to enqueue
     bool final_enqueued = false;
     auto enqueue_group = [&]() -> int {
         const int slot = (int)(g_enq % kRing);
         c->start_buf[slot] = buf;
         c->mail->R[slot] = kEmpty;
-        StepArgs a = base_args(c, o->tol);
-        a.slot = slot;
         c->cur_group = g_enq;
         c->cur_first = true;
         int s2;
         if (g_enq * L >= o->max_sweeps) {
             // the last allowed check: measure only, keep u_{gL} in place
-            const float* in = c->u[buf];
-            s2 = timed(c, KC_RESID, [&] { return launch_residual(in, c->b, a, c->stream); });
+            s2 = enqueue_residual(c, o->tol, buf, slot);
             if (s2) return s2;
             JAC_HIP(hipEventRecord(c->ev[slot], c->stream));
             final_enqueued = true;
@@ -274,7 +335,7 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
     st = enqueue_group();
     if (st) return st;
     for (int64_t g = 1;; ++g) {
-        if (!final_enqueued && g_enq <= g + 1) {
+        if (!final_enqueued && g_enq <= g + 1) {  // keep one interval queued beyond check g
             st = enqueue_group();
             if (st) return st;
         }
@@ -282,25 +343,18 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
         JAC_HIP(hipEventSynchronize(c->ev[slot]));
         const uint32_t Rb = read_mail(&c->mail->R[slot]);
         if (Rb == kEmpty) return fail(JAC_EDEVICE, "a residual check did not report");
-        float R, bAv;
-        const uint32_t bAb = read_mail(&c->mail->bA_bits);
-        std::memcpy(&R, &Rb, 4);
-        std::memcpy(&bAv, &bAb, 4);
-        const float rho = R / bAv;
+        const float R = mail_float(&c->mail->R[slot]);
+        const float rho = R / mail_float(&c->mail->bA_bits);
         const int64_t k = g * L;
         const bool stop = !(rho >= o->tol);
         if (stop || k >= o->max_sweeps) {
-            if (c->prof && stop) mark_noops(c, g);
+            if (c->prof_every > 0 && stop) mark_noops(c, g);
             c->cur = c->start_buf[slot];
             if (sweeps_out) *sweeps_out = k;
             if (rho_out) *rho_out = rho;
             if (std::isnan(rho)) return fail(JAC_ENAN, "rho is NaN");
             if (!stop) return fail(JAC_ENOCONV, "max_sweeps reached before rho < tol");
             return JAC_OK;
-        }
-        if (c->prof && c->pending.size() > 8192) {
-            st = drain_profile(c, g);  // groups before g are decided and finished
-            if (st) return st;
         }
     }
 }
@@ -327,7 +381,8 @@ void jac_opts_default(jac_opts* o) {
 size_t jac_workspace_bytes(int N) {
     if (N < 1 || N > kMaxN) return 0;
     Geom g = make_geom(N);
-    return (size_t)g.plane * 4 * sizeof(float) + sizeof(Scratch);
+    size_t bytes = (size_t)g.plane * 4 * sizeof(float) + sizeof(Scratch) + (size_t)partial_cap(N) * 4;
+    return (bytes + 255) / 256 * 256;
 }
 
 const char* jac_last_error(void) { return g_err.c_str(); }
@@ -365,11 +420,13 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
     c->b = base + 2 * c->g.plane;
     c->s = base + 3 * c->g.plane;
     c->sc = (Scratch*)(base + 4 * c->g.plane);
+    c->npart_cap = partial_cap(N);
     c->cur = 0;
-    c->prof = false;
+    c->prof_every = 0;
+    c->step_serial = 0;
     c->cur_group = -1;
     c->cur_first = false;
-    for (int i = 0; i < kClasses; ++i) { c->ms[i] = 0.0; c->cnt[i] = 0; }
+    for (int i = 0; i < kClasses; ++i) { c->ms[i] = 0.0; c->cnt[i] = 0; c->seen[i] = 0; c->timed_n[i] = 0; }
     for (int i = 0; i < kRing; ++i) c->ev[i] = nullptr;
     c->mail = nullptr;
 
@@ -384,7 +441,8 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
         if (hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming) != hipSuccess)
             return cleanup_fail(fail(JAC_EDEVICE, "hipEventCreateWithFlags failed"));
 
-    hipError_t e = launch_fill(base, c->g.plane * 4 + (int64_t)(sizeof(Scratch) / 4), 0.0f, c->stream);
+    hipError_t e = launch_fill(base, c->g.plane * 4 + (int64_t)(sizeof(Scratch) / 4) + c->npart_cap, 0.0f,
+                               c->stream);
     if (e == hipSuccess) e = launch_ghosts(c->u[0], c->g, c->stream);
     if (e == hipSuccess) e = launch_ghosts(c->u[1], c->g, c->stream);
     if (e == hipSuccess && source_host)
@@ -401,9 +459,9 @@ int jac_destroy(jac_t c) {
     (void)hipStreamSynchronize(c->stream);
     for (int i = 0; i < kRing; ++i)
         if (c->ev[i]) (void)hipEventDestroy(c->ev[i]);
-    for (Pending& p : c->pending) {
-        (void)hipEventDestroy(p.e0);
-        (void)hipEventDestroy(p.e1);
+    for (Rec& p : c->recs) {
+        if (p.e0) (void)hipEventDestroy(p.e0);
+        if (p.e1) (void)hipEventDestroy(p.e1);
     }
     for (hipEvent_t e : c->free_ev) (void)hipEventDestroy(e);
     if (c->mail) (void)hipHostFree(c->mail);
@@ -426,7 +484,7 @@ int jac_solve(jac_t c, int nsteps, const jac_opts* o, int64_t* sweeps, float* rh
         st = run_step(c, o, sweeps ? &sweeps[n] : nullptr, rho ? &rho[n] : nullptr);
         if (st) break;
     }
-    if (c->prof) {
+    if (c->prof_every > 0) {
         int s2 = drain_profile(c);
         if (!st) st = s2;
     }
@@ -438,6 +496,9 @@ int jac_sweep(jac_t c, const jac_opts* o, int64_t nsweeps, float* rho) {
     if (nsweeps < 0) return fail(JAC_EINVAL, "nsweeps must be >= 0");
     int st = check_opts(c, o);
     if (st) return st;
+    c->step_serial += 1;
+    c->cur_group = -1;
+    c->cur_first = false;
     st = enqueue_rhs(c, o->tol);
     if (st) return st;
     int buf = c->cur;
@@ -446,9 +507,7 @@ int jac_sweep(jac_t c, const jac_opts* o, int64_t nsweeps, float* rho) {
     c->cur = buf;
     if (rho) {
         c->mail->R[0] = kEmpty;
-        StepArgs a = base_args(c, o->tol);
-        a.slot = 0;
-        st = timed(c, KC_RESID, [&] { return launch_residual(c->u[c->cur], c->b, a, c->stream); });
+        st = enqueue_residual(c, o->tol, c->cur, 0);
         if (st) return st;
     }
     JAC_HIP(hipStreamSynchronize(c->stream));
@@ -460,7 +519,7 @@ int jac_sweep(jac_t c, const jac_opts* o, int64_t nsweeps, float* rho) {
         std::memcpy(&bAv, &bAb, 4);
         *rho = R / bAv;
     }
-    if (c->prof) return drain_profile(c);
+    if (c->prof_every > 0) return drain_profile(c);
     return JAC_OK;
 }
 
@@ -490,24 +549,24 @@ int jac_reset(jac_t c) {
     return JAC_OK;
 }
 
-int jac_profile(jac_t c, int enable) {
+int jac_profile(jac_t c, int every) {
     if (!c) return fail(JAC_EINVAL, "context is NULL");
-    if (c->prof) {
-        int st = drain_profile(c);
-        if (st) return st;
-    }
-    c->prof = enable != 0;
-    for (int i = 0; i < kClasses; ++i) { c->ms[i] = 0.0; c->cnt[i] = 0; }
+    if (every < 0) return fail(JAC_EINVAL, "every must be >= 0");
+    int st = drain_profile(c);
+    if (st) return st;
+    c->prof_every = every;
+    for (int i = 0; i < kClasses; ++i) { c->ms[i] = 0.0; c->cnt[i] = 0; c->seen[i] = 0; c->timed_n[i] = 0; }
     return JAC_OK;
 }
 
-int jac_profile_read(jac_t c, int kclass, double* ms_total, int64_t* launches) {
+int jac_profile_read(jac_t c, int kclass, double* ms_timed, int64_t* launches, int64_t* timed_launches) {
     if (!c) return fail(JAC_EINVAL, "context is NULL");
     if (kclass < 0 || kclass >= kClasses) return fail(JAC_EINVAL, "unknown kernel class");
     int st = drain_profile(c);
     if (st) return st;
-    if (ms_total) *ms_total = c->ms[kclass];
+    if (ms_timed) *ms_timed = c->ms[kclass];
     if (launches) *launches = c->cnt[kclass];
+    if (timed_launches) *timed_launches = c->timed_n[kclass];
     return JAC_OK;
 }
 

@@ -45,10 +45,12 @@ def test_workspace_bytes():
     assert jac.jac_workspace_bytes(65537) == 0
     n1 = jac.jac_workspace_bytes(1)
     assert n1 > 0 and n1 % 256 == 0
-    # four planes of (N+128) rows, pitch rounded to 64 floats, plus a 256-byte scratch block
+    # four planes of (N+128) rows, pitch rounded to 64 floats, a 256-byte scratch
+    # header and one partial-maximum slot per 1024 unknowns plus 65536
     N = 8192
     P = (N + 128 + 63) // 64 * 64
-    assert jac.jac_workspace_bytes(N) == 4 * 4 * P * (N + 128) + 256
+    want = 4 * 4 * P * (N + 128) + 256 + 4 * (N * N // 1024 + 65536)
+    assert jac.jac_workspace_bytes(N) == (want + 255) // 256 * 256
 
 
 @pytest.mark.parametrize("N,r,ws", [(0, 1.0, 1 << 20), (-3, 1.0, 1 << 20), (65537, 1.0, 1 << 20),
@@ -87,3 +89,12 @@ def test_library_path_does_not_use_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert not pattern.search(src), f
+
+
+def test_one_hip_runtime_in_process():
+    """The library binds to the HIP runtime torch loaded; a second copy would have
+    its own device context and could not use torch's streams."""
+    jac.load_library()
+    maps = open(f"/proc/{os.getpid()}/maps").read()
+    hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(hip) == 1, hip

@@ -190,14 +190,21 @@ def test_profile_counts_launches():
     s = workloads.gaussian_source(N, r)
     sol = jac.Solver(N, r, s)
     try:
-        sol.profile(True)
+        sol.profile(1)
         _, k, _ = sol.solve(2, opts())
-        ms, n = sol.profile_read("sync")
-        ms_c, n_c = sol.profile_read("sync_check")
-        ms_r, n_r = sol.profile_read("rhs")
+        ms, n, nt = sol.profile_read("sync")
+        ms_c, n_c, _ = sol.profile_read("sync_check")
+        _, n_r, _ = sol.profile_read("rhs")
+        _, n_noop, _ = sol.profile_read("noop")
+        _, n_red, _ = sol.profile_read("reduce")
     finally:
         sol.close()
-    assert n_r == 2
-    # every sweep is a launch; the speculative interval after a stop adds launches that return at once
-    assert n + n_c >= int(k.sum())
+    assert n_r == 2 and nt == n
+    checks = int(k.sum()) // 8
+    # each step: group 0 has 8 plain sweeps, groups 1..g-1 one checking + 7 plain,
+    # the stopping check runs, and what was queued after it returns at once
+    assert n_c == checks
+    assert n == 8 * 2 + 7 * (checks - 2)
+    assert n_noop == 2 * (7 + 8)
+    assert n_red == 2 + checks + 2  # two norms, every check, the no-op groups' reductions
     assert ms > 0 and ms_c > 0

@@ -1,0 +1,146 @@
+"""Kernel (b), exact temporal blocking, against the oracle bit for bit (page
+"stencil-jacobian.vercel.app", section 02: after D sweeps the tile holds exactly
+what D synchronous sweeps would produce).  A launch does D sweeps; the check
+interval is M = 8, or D when D > 8, and launches of min(D, left) sweeps keep
+the checks on the oracle's sweep counts."""
+import numpy as np
+import pytest
+
+import jacobi_stencil_amd as jac
+import oracle
+import workloads
+from tests.gpu_helpers import assert_same, bits, field_hash, lib_solve, load_expected, opts, say
+
+pytestmark = pytest.mark.gpu
+
+TB = jac.JAC_TBLOCK
+
+
+def interval(D, M=8):
+    return max(M, D)
+
+
+@pytest.mark.parametrize("D", list(range(1, 17)))
+@pytest.mark.parametrize("N", [70, 300])
+def test_every_depth_bitwise(D, N):
+    r = 10.0
+    say("tblock depth", D, N)
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=2, M=interval(D))
+    assert_same(lib_solve(N, r, s, 2, opts(kernel=TB, D=D)), ref, f"D={D} N={N}")
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 9, 15, 63, 64, 65, 127, 129, 224, 240, 248, 249, 255, 256,
+                               257, 481, 513])
+@pytest.mark.parametrize("D", [2, 4, 8])
+def test_small_and_ragged_grids_bitwise(N, D):
+    """Window widths 248/240 (D 2-4 / 8) and band heights meet N at every offset."""
+    r = 1.0
+    say("tblock small", N, D)
+    s = workloads.point_source(N, r)
+    ref = oracle.solve(N, r, s, steps=2, M=interval(D))
+    assert_same(lib_solve(N, r, s, 2, opts(kernel=TB, D=D)), ref, f"N={N} D={D}")
+
+
+@pytest.mark.parametrize("D", [3, 5, 12])
+def test_random_fields_bitwise(D):
+    N, r = 181, 100.0
+    say("tblock random", D)
+    s = workloads.random_source(N, r, D)
+    u0 = workloads.random_field(N, D)
+    ref = oracle.solve(N, r, s, u0=u0, steps=1, M=interval(D))
+    assert_same(lib_solve(N, r, s, 1, opts(kernel=TB, D=D), u0=u0), ref, f"D={D}")
+
+
+@pytest.mark.parametrize("D", [2, 4, 8])
+def test_config_c1_bitwise(D):
+    say("tblock C1", D)
+    s = workloads.point_source(512, 1.0)
+    ref = oracle.solve(512, 1.0, s)
+    assert_same(lib_solve(512, 1.0, s, 10, opts(kernel=TB, D=D)), ref, f"C1 D={D}")
+
+
+@pytest.mark.parametrize("D", [4, 8])
+@pytest.mark.parametrize("r", [1.0, 10.0])
+def test_config_c5_bitwise(D, r):
+    say("tblock C5", D, r)
+    s = workloads.gaussian_source(256, r)
+    ref = oracle.solve(256, r, s)
+    assert_same(lib_solve(256, r, s, 10, opts(kernel=TB, D=D)), ref, f"C5 D={D} r={r}")
+
+
+@pytest.mark.parametrize("D", [2, 4, 8])
+def test_config_c2_against_stored_oracle(D):
+    """N = 2048, r = 10: D in {2, 4, 8} with M = 8 keeps the oracle's counts."""
+    exp = load_expected("C2")
+    assert exp is not None
+    say("tblock C2", D)
+    N, r = exp["N"], exp["r"]
+    sol = jac.Solver(N, r, workloads.source(exp["source"], N, r))
+    try:
+        for n in range(exp["steps"]):
+            _, k, rho = sol.step(opts(kernel=TB, D=D))
+            assert k == exp["sweeps"][n]
+            assert f"{np.float32(rho).view(np.uint32):08x}" == exp["rho_bits"][n]
+            assert field_hash(sol.field()) == exp["field_sha256"][n], f"step {n}"
+    finally:
+        sol.close()
+
+
+@pytest.mark.parametrize("D", [4, 8])
+def test_config_c3_against_stored_oracle(D):
+    """N = 8192, r = 10, the benchmark workload."""
+    exp = load_expected("C3")
+    assert exp is not None
+    say("tblock C3", D)
+    N, r = exp["N"], exp["r"]
+    sol = jac.Solver(N, r, workloads.source(exp["source"], N, r))
+    try:
+        for n in range(exp["steps"]):
+            _, k, rho = sol.step(opts(kernel=TB, D=D))
+            assert k == exp["sweeps"][n]
+            assert f"{np.float32(rho).view(np.uint32):08x}" == exp["rho_bits"][n]
+            assert field_hash(sol.field()) == exp["field_sha256"][n], f"step {n}"
+    finally:
+        sol.close()
+
+
+def test_fixed_sweep_counts_not_multiple_of_D():
+    """jac_sweep with n = qD + p: q launches of D and one of p sweeps."""
+    N, r = 143, 10.0
+    say("tblock fixed sweeps")
+    s = workloads.random_source(N, r, 4)
+    u0 = workloads.random_field(N, 4)
+    b = oracle.rhs(u0, s)
+    sol = jac.Solver(N, r, s)
+    try:
+        for n in (1, 5, 8, 13):
+            sol.set_field(u0)
+            rho = sol.sweep(n, opts(kernel=TB, D=5), want_rho=True)
+            want = u0
+            for _ in range(n):
+                want = oracle.sweep(want, b, r)
+            assert np.array_equal(bits(sol.field()), bits(want)), f"n={n}"
+            assert np.float32(rho) == oracle.residual(want, b, r) / oracle.rhs_norm(b, r)
+    finally:
+        sol.close()
+
+
+def test_noconv_keeps_checked_iterate():
+    N, r = 90, 100.0
+    say("tblock noconv")
+    s = workloads.point_source(N, r)
+    for cap, D in ((20, 4), (16, 16), (64, 8)):
+        ref = oracle.solve(N, r, s, steps=2, max_sweeps=cap, M=interval(D))
+        assert ref.status == oracle.ENOCONV
+        assert_same(lib_solve(N, r, s, 2, opts(kernel=TB, D=D, max_sweeps=cap)), ref, f"cap {cap} D {D}")
+
+
+def test_d_out_of_range_rejected():
+    sol = jac.Solver(16, 1.0)
+    try:
+        for D in (0, 17):
+            st, _, _ = jac.jac_step(sol.ctx, opts(kernel=TB, D=D))
+            assert st == jac.JAC_EINVAL
+    finally:
+        sol.close()
