@@ -120,6 +120,16 @@ int jac_set_field(jac_t ctx, const float* host_in);
 /* Set the field back to u^0 = 0 (device-side fill, no host traffic). */
 int jac_reset(jac_t ctx);
 
+/*
+ * Division path of the sweep: 1 if the context divides by d = 1 + 4r through
+ * its correctly rounded reciprocal and one fma correction, 0 if through IEEE
+ * division, < 0 on error.  jac_create takes the first only after checking on
+ * the device that it returns the IEEE quotient bit for bit on all 2^32 float
+ * inputs for this d; environment variable JACOBI_IEEE_DIVISION=1 at create
+ * time forces the second.  Results are identical either way.
+ */
+int jac_fast_division(jac_t ctx);
+
 /* Release the context (not the workspace).  NULL is accepted. */
 int jac_destroy(jac_t ctx);
 

@@ -28,8 +28,8 @@ STATUS_NAMES = {0: "JAC_OK", -1: "JAC_EINVAL", -2: "JAC_ENOMEM", -3: "JAC_EDEVIC
                 -5: "JAC_ENAN"}
 
 EXPORTS = ("jac_opts_default", "jac_workspace_bytes", "jac_create", "jac_step", "jac_solve", "jac_sweep",
-           "jac_get_field", "jac_set_field", "jac_reset", "jac_destroy", "jac_last_error", "jac_profile",
-           "jac_profile_read")
+           "jac_get_field", "jac_set_field", "jac_reset", "jac_fast_division", "jac_destroy", "jac_last_error",
+           "jac_profile", "jac_profile_read")
 
 
 class jac_opts(ctypes.Structure):
@@ -71,6 +71,7 @@ def load_library():
         lib.jac_get_field.argtypes = [vp, vp]
         lib.jac_set_field.argtypes = [vp, vp]
         lib.jac_reset.argtypes = [vp]
+        lib.jac_fast_division.argtypes = [vp]
         lib.jac_destroy.argtypes = [vp]
         lib.jac_last_error.argtypes = []
         lib.jac_last_error.restype = ctypes.c_char_p
@@ -153,6 +154,10 @@ def jac_set_field(ctx, field) -> int:
 
 def jac_reset(ctx) -> int:
     return load_library().jac_reset(ctx)
+
+
+def jac_fast_division(ctx) -> int:
+    return load_library().jac_fast_division(ctx)
 
 
 def jac_destroy(ctx) -> int:
@@ -244,6 +249,13 @@ class Solver:
 
     def reset(self):
         _check(jac_reset(self.ctx))
+
+    @property
+    def fast_division(self) -> bool:
+        v = jac_fast_division(self.ctx)
+        if v < 0:
+            _check(v)
+        return bool(v)
 
     def profile(self, every: int):
         _check(jac_profile(self.ctx, every))

@@ -56,7 +56,8 @@ inline Geom make_geom(int N) {
 struct Scratch {
     uint32_t bA_bits;  // ||b_A||_inf of the current step
     uint32_t stop;     // 1 once a check of the current step has decided to stop
-    uint32_t pad[62];
+    uint32_t div_bad;  // inputs on which the constant-divisor quotient missed (set-up check)
+    uint32_t pad[61];
     // followed by uint32_t partial[npart_cap]
 };
 static_assert(sizeof(Scratch) == 256, "scratch header is 256 bytes");
@@ -80,6 +81,8 @@ struct Mailbox {
 struct StepArgs {
     Geom g;
     float r, d, tol;
+    float y;        // RN(1/d), for the constant-divisor quotient
+    int fastdiv;    // 1: that quotient was verified equal to n/d for every float n
     Scratch* sc;
     Mailbox* mail;
     int slot;       // mailbox slot for this kernel's check (if it makes one)
@@ -87,14 +90,34 @@ struct StepArgs {
 
 // ---------------------------------------------------------------- device
 
-__device__ __forceinline__ float jacobi_update(float uE, float uW, float uN, float uS,
-                                               float b, float r, float d) {
+// n / d, rounded to nearest.  FAST uses the reciprocal y = RN(1/d) and one
+// correction step (Markstein, "Computation of elementary functions on the IBM
+// RISC System/6000 processor", IBM J. Res. Dev. 34(1), 1990): q0 = RN(n*y),
+// e = n - q0*d exactly by one fma, q = RN(q0 + e*y); v_div_fixup then applies
+// the IEEE special cases (signed zeros, infinities, NaN).  The result equals
+// the correctly rounded quotient only where verified: a context uses FAST only
+// after a set-up kernel has compared it with n / d on all 2^32 inputs for its d.
+template <bool FAST>
+__device__ __forceinline__ float div_d(float n, float d, float y) {
+    if constexpr (FAST) {
+        const float q0 = n * y;
+        const float e = __builtin_fmaf(-q0, d, n);
+        const float q = __builtin_fmaf(e, y, q0);
+        return __builtin_amdgcn_div_fixupf(q, d, n);
+    } else {
+        return n / d;
+    }
+}
+
+template <bool FAST>
+__device__ __forceinline__ float jacobi_update(float uE, float uW, float uN, float uS, float b, float r, float d,
+                                               float y) {
     float S = uE + uW;
     S = S + uN;
     S = S + uS;
     float t = r * S;
     float n = b + t;
-    return n / d;
+    return div_d<FAST>(n, d, y);
 }
 
 __device__ __forceinline__ uint32_t residual_bits(float C, float uE, float uW, float uN, float uS,
@@ -156,6 +179,9 @@ __device__ __forceinline__ void store_block_max(uint32_t m, Scratch* sc, int64_t
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_ghosts(float* u, const Geom& g, hipStream_t s);
 hipError_t launch_rhs(const float* u, const float* src, float* b, const StepArgs& a, hipStream_t s);
+// Count the float inputs n (all 2^32) on which div_d<true> differs from n / d
+// into sc->div_bad (NaN results count as equal when both are NaN).
+hipError_t launch_verify_div(float d, float y, Scratch* sc, hipStream_t s);
 // Reduce npart partials.  norm: they are |b_A| maxima -- publish ||b_A|| and
 // clear the stop flag.  Otherwise they are |res| maxima of a check -- unless
 // the step has already stopped, publish R in mailbox slot a.slot and set the

@@ -152,9 +152,9 @@ static SyncTiles sync_tiles(int N) {
 }
 
 // One row of 4 columns: the sweep and/or the residual of the middle row.
-template <bool DO_SWEEP, bool DO_CHECK>
+template <bool DO_SWEEP, bool DO_CHECK, bool FAST>
 __device__ __forceinline__ void sync_row(const float4& up, const float4& mid, const float4& dn, const float4& bb,
-                                         float wl, float er, float r, float d, float4& o4, uint32_t& m,
+                                         float wl, float er, float r, float d, float y, float4& o4, uint32_t& m,
                                          int valid /* columns of the 4 that are unknowns */) {
     if (DO_CHECK) {
         uint32_t v0 = residual_bits(mid.x, mid.y, wl, up.x, dn.x, bb.x, r);
@@ -171,10 +171,10 @@ __device__ __forceinline__ void sync_row(const float4& up, const float4& mid, co
         m = m > v ? m : v;
     }
     if (DO_SWEEP) {
-        o4.x = jacobi_update(mid.y, wl, up.x, dn.x, bb.x, r, d);
-        o4.y = jacobi_update(mid.z, mid.x, up.y, dn.y, bb.y, r, d);
-        o4.z = jacobi_update(mid.w, mid.y, up.z, dn.z, bb.z, r, d);
-        o4.w = jacobi_update(er, mid.z, up.w, dn.w, bb.w, r, d);
+        o4.x = jacobi_update<FAST>(mid.y, wl, up.x, dn.x, bb.x, r, d, y);
+        o4.y = jacobi_update<FAST>(mid.z, mid.x, up.y, dn.y, bb.y, r, d, y);
+        o4.z = jacobi_update<FAST>(mid.w, mid.y, up.z, dn.z, bb.z, r, d, y);
+        o4.w = jacobi_update<FAST>(er, mid.z, up.w, dn.w, bb.w, r, d, y);
     }
 }
 
@@ -183,7 +183,7 @@ __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast
 // One sweep u_{k+1} = J(u_k).  With CHECK the same pass also measures the
 // residual of u_k (the iterate it reads), which costs no extra memory traffic;
 // RESID_ONLY measures the residual and writes nothing.
-template <bool CHECK, bool RESID_ONLY>
+template <bool CHECK, bool RESID_ONLY, bool FAST>
 __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, const float* __restrict__ bin,
                                               float* __restrict__ uout, StepArgs a) {
     constexpr bool SWEEP = !RESID_ONLY;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
     const int wcol = (t % tiles_x) * 256;
     const int col0 = wcol + lane * 4;
     const int row0 = (t / tiles_x) * (kSyncWaves * H) + wave * H;
-    const float r = a.r, d = a.d;
+    const float r = a.r, d = a.d, y = a.y;
     uint32_t m = 0;
     if (t < tiles_x * tiles_y && row0 < N) {
         const int64_t o = g.origin + (int64_t)row0 * P + col0;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
                 const float wl = pu[(int64_t)i * P - 1];
                 const float er = pu[(int64_t)i * P + 4];
                 float4 o4;
-                sync_row<SWEEP, CHK>(up, mid, dn, bb, wl, er, r, d, o4, m, 4);
+                sync_row<SWEEP, CHK, FAST>(up, mid, dn, bb, wl, er, r, d, y, o4, m, 4);
                 if (SWEEP) *reinterpret_cast<float4*>(po + (int64_t)i * P) = o4;
                 up = mid;
                 mid = dn;
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
                 const float wl = pu[(int64_t)i * P - 1];
                 const float er = pu[(int64_t)i * P + 4];
                 float4 o4;
-                sync_row<SWEEP, CHK>(up, mid, dn, bb, wl, er, r, d, o4, m, valid);
+                sync_row<SWEEP, CHK, FAST>(up, mid, dn, bb, wl, er, r, d, y, o4, m, valid);
                 if (SWEEP) {
                     float* q = po + (int64_t)i * P;
                     if (valid == 4) {
@@ -258,17 +258,47 @@ int64_t sync_blocks(int N) { return sync_tiles(N).blocks; }
 hipError_t launch_sync(const float* uin, const float* b, float* uout, bool check, const StepArgs& a,
                        hipStream_t s) {
     SyncTiles t = sync_tiles(a.g.N);
-    if (check)
-        hipLaunchKernelGGL((k_sync<true, false>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, uin, b, uout, a);
-    else
-        hipLaunchKernelGGL((k_sync<false, false>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, uin, b, uout, a);
+    const dim3 grid(t.blocks), block(64 * kSyncWaves);
+    if (check) {
+        if (a.fastdiv)
+            hipLaunchKernelGGL((k_sync<true, false, true>), grid, block, 0, s, uin, b, uout, a);
+        else
+            hipLaunchKernelGGL((k_sync<true, false, false>), grid, block, 0, s, uin, b, uout, a);
+    } else {
+        if (a.fastdiv)
+            hipLaunchKernelGGL((k_sync<false, false, true>), grid, block, 0, s, uin, b, uout, a);
+        else
+            hipLaunchKernelGGL((k_sync<false, false, false>), grid, block, 0, s, uin, b, uout, a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_residual(const float* u, const float* b, const StepArgs& a, hipStream_t s) {
     SyncTiles t = sync_tiles(a.g.N);
-    hipLaunchKernelGGL((k_sync<false, true>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, u, b,
+    hipLaunchKernelGGL((k_sync<false, true, false>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, u, b,
                        (float*)nullptr, a);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ division check
+
+__global__ __launch_bounds__(256) void k_verify_div(float d, float y, Scratch* sc) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    uint32_t bad = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += stride) {
+        const float n = __uint_as_float((uint32_t)i);
+        const float q = div_d<false>(n, d, y);
+        const float f = div_d<true>(n, d, y);
+        const bool same = __float_as_uint(q) == __float_as_uint(f) || (q != q && f != f);
+        bad += same ? 0u : 1u;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) bad += (uint32_t)__shfl_xor((int)bad, o, 64);
+    if ((threadIdx.x & 63) == 0 && bad) atomicAdd(&sc->div_bad, bad);  // only where it failed
+}
+
+hipError_t launch_verify_div(float d, float y, Scratch* sc, hipStream_t s) {
+    hipLaunchKernelGGL(k_verify_div, dim3(8192), dim3(256), 0, s, d, y, sc);
     return hipGetLastError();
 }
 

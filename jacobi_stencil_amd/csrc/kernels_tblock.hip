@@ -48,15 +48,16 @@ struct TBLane {
     bool core[4];    // column is an unknown this wavefront stores
 };
 
+template <bool FAST>
 __device__ __forceinline__ float4 level_update(const float4& up, const float4& mid, const float4& dn,
-                                               const float4& bb, float r, float d) {
+                                               const float4& bb, float r, float d, float y) {
     const float wl = from_left(mid.w);
     const float er = from_right(mid.x);
     float4 o;
-    o.x = jacobi_update(mid.y, wl, up.x, dn.x, bb.x, r, d);
-    o.y = jacobi_update(mid.z, mid.x, up.y, dn.y, bb.y, r, d);
-    o.z = jacobi_update(mid.w, mid.y, up.z, dn.z, bb.z, r, d);
-    o.w = jacobi_update(er, mid.z, up.w, dn.w, bb.w, r, d);
+    o.x = jacobi_update<FAST>(mid.y, wl, up.x, dn.x, bb.x, r, d, y);
+    o.y = jacobi_update<FAST>(mid.z, mid.x, up.y, dn.y, bb.y, r, d, y);
+    o.z = jacobi_update<FAST>(mid.w, mid.y, up.z, dn.z, bb.z, r, d, y);
+    o.w = jacobi_update<FAST>(er, mid.z, up.w, dn.w, bb.w, r, d, y);
     return o;
 }
 
@@ -89,13 +90,13 @@ __device__ __forceinline__ void impose_ring(float4& v, int i, int N, const TBLan
     }
 }
 
-template <int D, bool CHK, bool EDGE>
+template <int D, bool CHK, bool EDGE, bool FAST>
 __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const float* __restrict__ bin,
                                             float* __restrict__ uout, const StepArgs& a, const TBLane& L,
                                             bool lane_loads, int y0, int last, float4 (*ring)[64]) {
     constexpr int R = D + 1;
     const int N = a.g.N, P = a.g.P;
-    const float r = a.r, d = a.d;
+    const float r = a.r, d = a.d, y = a.y;
     const int lane = threadIdx.x & 63;
     const int j0 = y0 - D, j1 = last + D;
     const float* pu = uin + a.g.origin + L.c0;
@@ -137,7 +138,7 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
                     m = m > v ? m : v;
                 }
             }
-            float4 v = level_update(up[t - 1], mid[t - 1], nw, bb, r, d);
+            float4 v = level_update<FAST>(up[t - 1], mid[t - 1], nw, bb, r, d, y);
             if (EDGE) impose_ring(v, j - t, N, L);
             up[t - 1] = mid[t - 1];
             mid[t - 1] = nw;
@@ -159,7 +160,7 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     return m;
 }
 
-template <int D, bool CHK>
+template <int D, bool CHK, bool FAST>
 __global__ __launch_bounds__(64) void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
                                                float* __restrict__ uout, StepArgs a, int H) {
     constexpr int Dp = (D + 3) & ~3;
@@ -190,9 +191,9 @@ __global__ __launch_bounds__(64) void k_tblock(const float* __restrict__ uin, co
         const bool lane_loads = L.c0 < N && L.c0 + 4 > 0;
         const bool edge = X < 0 || X + 256 > N || y0 - D < 0 || last + D >= N;
         if (edge)
-            m = tb_band<D, CHK, true>(uin, bin, uout, a, L, lane_loads, y0, last, ring);
+            m = tb_band<D, CHK, true, FAST>(uin, bin, uout, a, L, lane_loads, y0, last, ring);
         else
-            m = tb_band<D, CHK, false>(uin, bin, uout, a, L, lane_loads, y0, last, ring);
+            m = tb_band<D, CHK, false, FAST>(uin, bin, uout, a, L, lane_loads, y0, last, ring);
     }
     if (CHK) store_block_max<1>(m, a.sc, blockIdx.x);
 }
@@ -221,10 +222,17 @@ static hipError_t launch_tb_d(const float* uin, const float* b, float* uout, boo
     const int N = a.g.N;
     const int tiles = ((N + Wout - 1) / Wout) * ((N + H - 1) / H);
     const int blocks = (tiles + 7) / 8 * 8;
-    if (check)
-        hipLaunchKernelGGL((k_tblock<D, true>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H);
-    else
-        hipLaunchKernelGGL((k_tblock<D, false>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H);
+    if (check) {
+        if (a.fastdiv)
+            hipLaunchKernelGGL((k_tblock<D, true, true>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H);
+        else
+            hipLaunchKernelGGL((k_tblock<D, true, false>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H);
+    } else {
+        if (a.fastdiv)
+            hipLaunchKernelGGL((k_tblock<D, false, true>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H);
+        else
+            hipLaunchKernelGGL((k_tblock<D, false, false>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H);
+    }
     return hipGetLastError();
 }
 

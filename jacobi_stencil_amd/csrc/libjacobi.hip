@@ -20,6 +20,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -67,7 +68,8 @@ struct Rec {
 
 struct jac_ctx {
     int N;
-    float r, d;
+    float r, d, y;
+    int fastdiv;     // 1: the constant-divisor quotient was verified for this d
     Geom g;
     hipStream_t stream;
     float* u[2];
@@ -99,6 +101,8 @@ StepArgs base_args(const jac_ctx* c, float tol) {
     a.g = c->g;
     a.r = c->r;
     a.d = c->d;
+    a.y = c->y;
+    a.fastdiv = c->fastdiv;
     a.tol = tol;
     a.sc = c->sc;
     a.mail = c->mail;
@@ -411,7 +415,9 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
     {
         float four_r = 4.0f * r;
         c->d = 1.0f + four_r;
+        c->y = 1.0f / c->d;  // correctly rounded on the host (SSE division)
     }
+    c->fastdiv = 0;
     c->g = make_geom(N);
     c->stream = (hipStream_t)stream;
     float* base = (float*)workspace;
@@ -448,8 +454,17 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
     if (e == hipSuccess && source_host)
         e = hipMemcpy2DAsync(c->s + c->g.origin, (size_t)c->g.P * 4, source_host, (size_t)N * 4, (size_t)N * 4,
                              (size_t)N, hipMemcpyHostToDevice, c->stream);
+    // The sweep divides by the constant d.  Use the reciprocal-and-correct
+    // quotient only if it equals the IEEE quotient on every float input.
+    const char* ieee_env = std::getenv("JACOBI_IEEE_DIVISION");
+    const bool want_fast = !(ieee_env && ieee_env[0] == '1');
+    if (e == hipSuccess && want_fast) e = launch_verify_div(c->d, c->y, c->sc, c->stream);
+    uint32_t bad = 1;
+    if (e == hipSuccess && want_fast)
+        e = hipMemcpyAsync(&bad, &c->sc->div_bad, 4, hipMemcpyDeviceToHost, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
     if (e != hipSuccess) return cleanup_fail(fail(JAC_EDEVICE, std::string("set-up: ") + hipGetErrorString(e)));
+    c->fastdiv = (want_fast && bad == 0) ? 1 : 0;
     *out = c;
     return JAC_OK;
 }
@@ -547,6 +562,11 @@ int jac_reset(jac_t c) {
     c->cur = 0;
     JAC_HIP(hipStreamSynchronize(c->stream));
     return JAC_OK;
+}
+
+int jac_fast_division(jac_t c) {
+    if (!c) return fail(JAC_EINVAL, "context is NULL");
+    return c->fastdiv;
 }
 
 int jac_profile(jac_t c, int every) {
