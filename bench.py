@@ -40,10 +40,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="C3")
-    ap.add_argument("--kernel", default="sync", choices=sorted(KERNELS))
-    ap.add_argument("--D", type=int, default=1)
+    ap.add_argument("--kernel", default="tblock", choices=sorted(KERNELS))
+    ap.add_argument("--D", type=int, default=8)
     ap.add_argument("--tile-x", type=int, default=32)
     ap.add_argument("--tile-y", type=int, default=8)
+    ap.add_argument("--band-rows", type=int, default=0, help="TBLOCK rows per band (0: automatic)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--profile-every", type=int, default=16,
                     help="bracket every k-th launch of a class with HIP events (0: none)")
@@ -92,7 +93,7 @@ def main():
     stream = torch.cuda.current_stream()
     sol = jac.Solver(N, r, s, stream=stream)
     opts = jac.jac_opts_default(kernel=KERNELS[args.kernel], D=args.D, tile_x=args.tile_x,
-                                tile_y=args.tile_y)
+                                tile_y=args.tile_y, band_rows=args.band_rows)
 
     def one_solve():
         sol.reset()

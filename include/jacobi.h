@@ -74,11 +74,11 @@ typedef struct {
     int32_t tile_y;      /* ASYNC tile height in rows (1..256) */
     int32_t M;           /* check interval in sweeps (>= 1); the interval is max(M, D) */
     float tol;           /* rho threshold (> 0) */
-    int32_t reserved;    /* must be 0 */
+    int32_t band_rows;   /* TBLOCK: output rows per wavefront band (0: chosen from N and D) */
     int64_t max_sweeps;  /* per step; a failed check at or past it ends with JAC_ENOCONV */
 } jac_opts;
 
-/* SYNC, LAUNCH, D = 1, 32 x 8 tiles, M = 8, tol = 1e-5, max_sweeps = 1e6. */
+/* SYNC, LAUNCH, D = 1, 32 x 8 tiles, M = 8, tol = 1e-5, band_rows = 0, max_sweeps = 1e6. */
 void jac_opts_default(jac_opts* opts);
 
 /* Bytes of device workspace a context of size N needs (u twice, b, dt*f,

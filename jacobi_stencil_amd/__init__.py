@@ -35,7 +35,7 @@ EXPORTS = ("jac_opts_default", "jac_workspace_bytes", "jac_create", "jac_step", 
 class jac_opts(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("driver", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("tile_x", ctypes.c_int32), ("tile_y", ctypes.c_int32), ("M", ctypes.c_int32),
-                ("tol", ctypes.c_float), ("reserved", ctypes.c_int32), ("max_sweeps", ctypes.c_int64)]
+                ("tol", ctypes.c_float), ("band_rows", ctypes.c_int32), ("max_sweeps", ctypes.c_int64)]
 
 
 class JacobiError(RuntimeError):

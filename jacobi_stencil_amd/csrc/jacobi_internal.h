@@ -191,11 +191,13 @@ hipError_t launch_reduce(int64_t npart, bool norm, const StepArgs& a, hipStream_
 int64_t rhs_blocks(int N);
 int64_t sync_blocks(int N);
 int64_t tblock_blocks(int N, int D, int H);
-int tblock_rows(int N, int D);
+// Automatic band height for a grid of `resident_waves` wavefront slots.
+int tblock_rows(int N, int D, int resident_waves);
+int tblock_waves_per_cu(int D, bool fast);
 hipError_t launch_sync(const float* uin, const float* b, float* uout, bool check, const StepArgs& a,
                        hipStream_t s);
 hipError_t launch_residual(const float* u, const float* b, const StepArgs& a, hipStream_t s);
-// D sweeps (1..16) in one pass; H = output rows per wavefront band (< 1: automatic).
+// D sweeps (1..16) in one pass; H = output rows per wavefront band (>= 1).
 hipError_t launch_tblock(const float* uin, const float* b, float* uout, int D, bool check, const StepArgs& a,
                          int H, hipStream_t s);
 

@@ -90,74 +90,117 @@ __device__ __forceinline__ void impose_ring(float4& v, int i, int N, const TBLan
     }
 }
 
+// The streaming state of one wavefront: for every level t < D three row
+// registers whose roles rotate (up = row i-1, mid = row i, new = row i+1 of
+// that level, as seen by level t+1), the prefetched next row, the ring slot.
 template <int D, bool CHK, bool EDGE, bool FAST>
-__device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const float* __restrict__ bin,
-                                            float* __restrict__ uout, const StepArgs& a, const TBLane& L,
-                                            bool lane_loads, int y0, int last, float4 (*ring)[64]) {
-    constexpr int R = D + 1;
-    const int N = a.g.N, P = a.g.P;
-    const float r = a.r, d = a.d, y = a.y;
-    const int lane = threadIdx.x & 63;
-    const int j0 = y0 - D, j1 = last + D;
-    const float* pu = uin + a.g.origin + L.c0;
-    const float* pb = bin + a.g.origin + L.c0;
-    float* po = uout + a.g.origin + L.c0;
-    const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    bool store_lane = L.core[0];
+struct TBStream {
+    const float* pu;
+    const float* pb;
+    float* po;
+    float r, d, y;
+    int N, P, j0, j1, y0, last;
+    bool lane_loads, store_lane;
+    TBLane L;
+    float4 (*ring)[64];
+    float4 nu, nb;  // row j+1 of u_k and b, loaded one row ahead
+    int s;          // ring slot of the current row
+    uint32_t m;     // running max |res| (CHK)
 
-    float4 up[D], mid[D];
-#pragma unroll
-    for (int t = 0; t < D; ++t) { up[t] = zero; mid[t] = zero; }
-    uint32_t m = 0;
-
-    float4 nu = zero, nb = zero;
-    if (lane_loads) {
-        nu = *reinterpret_cast<const float4*>(pu + (int64_t)j0 * P);
-        nb = *reinterpret_cast<const float4*>(pb + (int64_t)j0 * P);
-    }
-    int s = 0;  // ring slot of row j
-    for (int j = j0; j <= j1; ++j) {
-        const float4 cur = nu;
+    // One row j: read it, push every level one row further, store level D.
+    // UP/MID/NEW are the level registers in this row's rotation.  RAMP: the
+    // first rows of the band, where level t only starts once 2t rows are in.
+    template <bool RAMP>
+    __device__ __forceinline__ void row(int j, float4 (&UP)[D], float4 (&MID)[D], float4 (&NEW)[D]) {
+        constexpr int R = D + 1;
+        const int lane = threadIdx.x & 63;
+        NEW[0] = nu;
         const float4 cb = nb;
         if (lane_loads && j < j1) {  // fetch the next row while this one is worked on
             nu = *reinterpret_cast<const float4*>(pu + (int64_t)(j + 1) * P);
             nb = *reinterpret_cast<const float4*>(pb + (int64_t)(j + 1) * P);
         }
         ring[s][lane] = cb;
-        float4 nw = cur;  // level 0, row j
+        const int depth = j - j0;  // level t is exact from row j0 + 2t on
+        float4 out;
 #pragma unroll
         for (int t = 1; t <= D; ++t) {
-            int st = s - t;
-            if (st < 0) st += R;
-            const float4 bb = ring[st][lane];
-            if (CHK && t == 1) {
-                // residual of u_k on row j-1, from the same stencil level 1 reads
-                const int i = j - 1;
-                if (i >= y0 && i <= last) {
-                    uint32_t v = level_residual(up[0], mid[0], nw, bb, r, L);
-                    m = m > v ? m : v;
+            if (!RAMP || 2 * t <= depth) {
+                int st = s - t;
+                if (st < 0) st += R;
+                const float4 bb = ring[st][lane];
+                if (CHK && t == 1) {
+                    // residual of u_k on row j-1, from the stencil level 1 reads
+                    const int i = j - 1;
+                    if (i >= y0 && i <= last) {
+                        const uint32_t v = level_residual(UP[0], MID[0], NEW[0], bb, r, L);
+                        m = m > v ? m : v;
+                    }
                 }
+                float4 v = level_update<FAST>(UP[t - 1], MID[t - 1], NEW[t - 1], bb, r, d, y);
+                if (EDGE) impose_ring(v, j - t, N, L);
+                if (t < D) NEW[t] = v;
+                else out = v;
             }
-            float4 v = level_update<FAST>(up[t - 1], mid[t - 1], nw, bb, r, d, y);
-            if (EDGE) impose_ring(v, j - t, N, L);
-            up[t - 1] = mid[t - 1];
-            mid[t - 1] = nw;
-            nw = v;
         }
         const int i = j - D;
         if (i >= y0 && i <= last && store_lane) {
             float* q = po + (int64_t)i * P;
             if (L.core[3]) {
-                *reinterpret_cast<float4*>(q) = nw;
+                *reinterpret_cast<float4*>(q) = out;
             } else {
-                q[0] = nw.x;
-                if (L.core[1]) q[1] = nw.y;
-                if (L.core[2]) q[2] = nw.z;
+                q[0] = out.x;
+                if (L.core[1]) q[1] = out.y;
+                if (L.core[2]) q[2] = out.z;
             }
         }
         s = (s + 1 == R) ? 0 : s + 1;
     }
-    return m;
+};
+
+template <int D, bool CHK, bool EDGE, bool FAST>
+__device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const float* __restrict__ bin,
+                                            float* __restrict__ uout, const StepArgs& a, const TBLane& L,
+                                            bool lane_loads, int y0, int last, float4 (*ring)[64]) {
+    TBStream<D, CHK, EDGE, FAST> st;
+    st.N = a.g.N;
+    st.P = a.g.P;
+    st.r = a.r;
+    st.d = a.d;
+    st.y = a.y;
+    st.j0 = y0 - D;
+    st.j1 = last + D;
+    st.y0 = y0;
+    st.last = last;
+    st.pu = uin + a.g.origin + L.c0;
+    st.pb = bin + a.g.origin + L.c0;
+    st.po = uout + a.g.origin + L.c0;
+    st.lane_loads = lane_loads;
+    st.store_lane = L.core[0];
+    st.L = L;
+    st.ring = ring;
+    st.s = 0;
+    st.m = 0;
+    const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    st.nu = zero;
+    st.nb = zero;
+    if (lane_loads) {
+        st.nu = *reinterpret_cast<const float4*>(st.pu + (int64_t)st.j0 * st.P);
+        st.nb = *reinterpret_cast<const float4*>(st.pb + (int64_t)st.j0 * st.P);
+    }
+    float4 A[D], B[D], C[D];
+#pragma unroll
+    for (int t = 0; t < D; ++t) { A[t] = zero; B[t] = zero; C[t] = zero; }
+    // three rows per trip, the level registers rotating A -> B -> C; the
+    // trips that still fill the pipeline test which levels are exact yet
+    for (int j = st.j0; j <= st.j1; j += 3) {
+        st.template row<false>(j, A, B, C);
+        if (j + 1 > st.j1) break;
+        st.template row<false>(j + 1, B, C, A);
+        if (j + 2 > st.j1) break;
+        st.template row<false>(j + 2, C, A, B);
+    }
+    return st.m;
 }
 
 template <int D, bool CHK, bool FAST>
@@ -198,13 +241,50 @@ __global__ __launch_bounds__(64) void k_tblock(const float* __restrict__ uin, co
     if (CHK) store_block_max<1>(m, a.sc, blockIdx.x);
 }
 
-int tblock_rows(int N, int D) {
-    // band height: long enough that the D extra rows above and below stay a
-    // small fraction, short enough to give every SIMD several wavefronts
-    (void)D;
-    if (N >= 4096) return 128;
-    if (N >= 1024) return 64;
-    return 32;
+// Resident wavefronts per CU for the checking variant of depth D (the one with
+// the most registers), from the runtime's occupancy calculator.
+template <int D>
+static int tb_waves_per_cu(bool fast) {
+    int n = 0;
+    hipError_t e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tblock<D, true, true>, 64, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tblock<D, true, false>, 64, 0);
+    return (e == hipSuccess && n > 0) ? n : 4;
+}
+
+int tblock_waves_per_cu(int D, bool fast) {
+    switch (D) {
+        case 1: return tb_waves_per_cu<1>(fast);
+        case 2: return tb_waves_per_cu<2>(fast);
+        case 3: return tb_waves_per_cu<3>(fast);
+        case 4: return tb_waves_per_cu<4>(fast);
+        case 5: return tb_waves_per_cu<5>(fast);
+        case 6: return tb_waves_per_cu<6>(fast);
+        case 7: return tb_waves_per_cu<7>(fast);
+        case 8: return tb_waves_per_cu<8>(fast);
+        case 9: return tb_waves_per_cu<9>(fast);
+        case 10: return tb_waves_per_cu<10>(fast);
+        case 11: return tb_waves_per_cu<11>(fast);
+        case 12: return tb_waves_per_cu<12>(fast);
+        case 13: return tb_waves_per_cu<13>(fast);
+        case 14: return tb_waves_per_cu<14>(fast);
+        case 15: return tb_waves_per_cu<15>(fast);
+        case 16: return tb_waves_per_cu<16>(fast);
+        default: return 4;
+    }
+}
+
+// Band height: the shortest bands (most parallelism) such that the whole grid
+// is one round of resident wavefronts -- a second, partly filled round would
+// leave most SIMDs idle at the end -- but at least 16 rows, so the D rows the
+// band re-reads above and below stay a moderate fraction.
+int tblock_rows(int N, int D, int resident_waves) {
+    const int Dp = (D + 3) & ~3;
+    const int Wout = 256 - 2 * Dp;
+    const int strips = (N + Wout - 1) / Wout;
+    int bands = resident_waves / strips;
+    if (bands < 1) bands = 1;
+    int H = (N + bands - 1) / bands;
+    return H < 16 ? 16 : H;
 }
 
 int64_t tblock_blocks(int N, int D, int H) {
@@ -238,7 +318,6 @@ static hipError_t launch_tb_d(const float* uin, const float* b, float* uout, boo
 
 hipError_t launch_tblock(const float* uin, const float* b, float* uout, int D, bool check, const StepArgs& a,
                          int H, hipStream_t s) {
-    if (H < 1) H = tblock_rows(a.g.N, D);
     switch (D) {
         case 1: return launch_tb_d<1>(uin, b, uout, check, a, H, s);
         case 2: return launch_tb_d<2>(uin, b, uout, check, a, H, s);

@@ -70,6 +70,8 @@ struct jac_ctx {
     int N;
     float r, d, y;
     int fastdiv;     // 1: the constant-divisor quotient was verified for this d
+    int cus;         // compute units of the device
+    int tb_rows[kMaxTBlockD + 1];  // automatic band height per depth (0: not yet computed)
     Geom g;
     hipStream_t stream;
     float* u[2];
@@ -184,7 +186,7 @@ int check_opts(const jac_ctx* c, const jac_opts* o) {
     if (o->M < 1) return fail(JAC_EINVAL, "M must be >= 1");
     if (!(o->tol > 0.0f) || !std::isfinite(o->tol)) return fail(JAC_EINVAL, "tol must be a positive finite float");
     if (o->max_sweeps < 1) return fail(JAC_EINVAL, "max_sweeps must be >= 1");
-    if (o->reserved != 0) return fail(JAC_EINVAL, "reserved must be 0");
+    if (o->band_rows < 0 || o->band_rows > 65536) return fail(JAC_EINVAL, "band_rows must be in 0..65536");
     if (o->kernel != JAC_SYNC && (o->D < 1 || o->D > kMaxD)) return fail(JAC_EINVAL, "D must be in 1..32");
     if (o->kernel == JAC_ASYNC && (o->tile_x < 1 || o->tile_x > 256 || o->tile_y < 1 || o->tile_y > 256))
         return fail(JAC_EINVAL, "tile_x and tile_y must be in 1..256");
@@ -230,9 +232,12 @@ int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, i
                        [&] { return launch_sync(in, c->b, out, check, a, c->stream); });
             break;
         case JAC_TBLOCK: {
-            const int H = tblock_rows(c->N, m);
+            if (o->band_rows == 0 && c->tb_rows[m] == 0)
+                c->tb_rows[m] = tblock_rows(c->N, m, c->cus * tblock_waves_per_cu(m, c->fastdiv != 0));
+            const int H = o->band_rows > 0 ? o->band_rows : c->tb_rows[m];
             npart = tblock_blocks(c->N, m, H);
-            if (check && npart > c->npart_cap) return fail(JAC_EDEVICE, "tblock grid exceeds partial slots");
+            if (check && npart > c->npart_cap)
+                return fail(JAC_EINVAL, "band_rows too small for this N: too many wavefront bands");
             st = timed(c, KC_TBLOCK, [&] { return launch_tblock(in, c->b, out, m, check, a, H, c->stream); });
             break;
         }
@@ -378,7 +383,7 @@ void jac_opts_default(jac_opts* o) {
     o->tile_y = 8;
     o->M = 8;
     o->tol = 1e-5f;
-    o->reserved = 0;
+    o->band_rows = 0;
     o->max_sweeps = 1000000;
 }
 
@@ -418,6 +423,8 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
         c->y = 1.0f / c->d;  // correctly rounded on the host (SSE division)
     }
     c->fastdiv = 0;
+    c->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+    for (int i = 0; i <= kMaxTBlockD; ++i) c->tb_rows[i] = 0;
     c->g = make_geom(N);
     c->stream = (hipStream_t)stream;
     float* base = (float*)workspace;

@@ -20,9 +20,9 @@ def say(*args):
 
 
 def opts(kernel=jac.JAC_SYNC, driver=jac.JAC_LAUNCH, D=1, tile_x=32, tile_y=8, M=8, tol=1e-5,
-         max_sweeps=10**6):
+         max_sweeps=10**6, band_rows=0):
     return jac.jac_opts_default(kernel=kernel, driver=driver, D=D, tile_x=tile_x, tile_y=tile_y, M=M,
-                                tol=tol, max_sweeps=max_sweeps)
+                                tol=tol, max_sweeps=max_sweeps, band_rows=band_rows)
 
 
 def lib_solve(N, r, s, steps, o, u0=None, allow=(jac.JAC_ENOCONV, jac.JAC_ENAN)):

@@ -37,7 +37,7 @@ def test_opts_layout():
     assert jac.jac_opts.max_sweeps.offset == 32
     o = jac.jac_opts_default()
     assert (o.kernel, o.driver, o.D, o.tile_x, o.tile_y, o.M) == (jac.JAC_SYNC, jac.JAC_LAUNCH, 1, 32, 8, 8)
-    assert o.tol == pytest.approx(1e-5) and o.max_sweeps == 10**6 and o.reserved == 0
+    assert o.tol == pytest.approx(1e-5) and o.max_sweeps == 10**6 and o.band_rows == 0
 
 
 def test_workspace_bytes():

@@ -144,3 +144,13 @@ def test_d_out_of_range_rejected():
             assert st == jac.JAC_EINVAL
     finally:
         sol.close()
+
+
+@pytest.mark.parametrize("H", [1, 2, 3, 7, 33, 1000])
+def test_band_heights_bitwise(H):
+    """Any band height (rows per wavefront) gives the same bits."""
+    N, r, D = 150, 10.0, 6
+    say("tblock band", H)
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=2)
+    assert_same(lib_solve(N, r, s, 2, opts(kernel=TB, D=D, band_rows=H)), ref, f"H={H}")
