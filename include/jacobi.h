@@ -137,6 +137,17 @@ int jac_destroy(jac_t ctx);
 const char* jac_last_error(void);
 
 /*
+ * Bandwidth probe (measurement only, no context needed): on `stream`,
+ * kind 0 copies a to c, kind 1 writes c = a + b (two reads, one write per
+ * element, the traffic mix of a sweep); n floats, a multiple of 4, arrays
+ * 16-byte aligned device memory owned by the caller; `blocks` workgroups of
+ * 256 threads stride over the arrays; nontemporal != 0 marks the stores
+ * nontemporal.  Asynchronous: time it with events on the stream.
+ */
+int jac_stream_probe(float* c, const float* a, const float* b, size_t n, int kind, int nontemporal,
+                     int blocks, void* stream);
+
+/*
  * Launch timing.  jac_profile(ctx, k) with k > 0 counts every kernel launch of
  * the library by class and brackets every k-th launch of each class with a
  * pair of HIP events on the context's stream (a pair costs about 10 us of

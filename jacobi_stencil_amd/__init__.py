@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "JAC_OK", -1: "JAC_EINVAL", -2: "JAC_ENOMEM", -3: "JAC_EDEVIC
 
 EXPORTS = ("jac_opts_default", "jac_workspace_bytes", "jac_create", "jac_step", "jac_solve", "jac_sweep",
            "jac_get_field", "jac_set_field", "jac_reset", "jac_fast_division", "jac_destroy", "jac_last_error",
-           "jac_profile", "jac_profile_read")
+           "jac_profile", "jac_profile_read", "jac_stream_probe")
 
 
 class jac_opts(ctypes.Structure):
@@ -72,6 +72,7 @@ def load_library():
         lib.jac_set_field.argtypes = [vp, vp]
         lib.jac_reset.argtypes = [vp]
         lib.jac_fast_division.argtypes = [vp]
+        lib.jac_stream_probe.argtypes = [vp, vp, vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
         lib.jac_destroy.argtypes = [vp]
         lib.jac_last_error.argtypes = []
         lib.jac_last_error.restype = ctypes.c_char_p
@@ -178,6 +179,14 @@ def jac_profile_read(ctx, kclass):
     nt = ctypes.c_int64(0)
     st = load_library().jac_profile_read(ctx, int(kclass), ctypes.byref(ms), ctypes.byref(n), ctypes.byref(nt))
     return st, float(ms.value), int(n.value), int(nt.value)
+
+
+def jac_stream_probe(c_ptr: int, a_ptr: int, b_ptr: int, n: int, kind: int, nontemporal: bool, blocks: int,
+                     stream_ptr: int) -> int:
+    """Bandwidth probe on raw device pointers: kind 0 copy, 1 add."""
+    return load_library().jac_stream_probe(ctypes.c_void_p(c_ptr), ctypes.c_void_p(a_ptr),
+                                           ctypes.c_void_p(b_ptr), int(n), int(kind), 1 if nontemporal else 0,
+                                           int(blocks), ctypes.c_void_p(stream_ptr))
 
 
 # ------------------------------------------------------------------ wrapper

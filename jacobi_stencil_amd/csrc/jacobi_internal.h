@@ -187,6 +187,9 @@ hipError_t launch_verify_div(float d, float y, Scratch* sc, hipStream_t s);
 // the step has already stopped, publish R in mailbox slot a.slot and set the
 // stop flag when !(R / ||b_A|| >= tol).
 hipError_t launch_reduce(int64_t npart, bool norm, const StepArgs& a, hipStream_t s);
+// Bandwidth probe: kind 0 copy (c = a), kind 1 add (c = a + b); n floats.
+hipError_t launch_probe(float* c, const float* a, const float* b, int64_t n, int kind, bool nontemporal,
+                        int blocks, hipStream_t s);
 // Blocks each launch will use (for the host's partial-slot check).
 int64_t rhs_blocks(int N);
 int64_t sync_blocks(int N);

@@ -108,9 +108,7 @@ struct TBStream {
     uint32_t m;     // running max |res| (CHK)
 
     // One row j: read it, push every level one row further, store level D.
-    // UP/MID/NEW are the level registers in this row's rotation.  RAMP: the
-    // first rows of the band, where level t only starts once 2t rows are in.
-    template <bool RAMP>
+    // UP/MID/NEW are the level registers in this row's rotation.
     __device__ __forceinline__ void row(int j, float4 (&UP)[D], float4 (&MID)[D], float4 (&NEW)[D]) {
         constexpr int R = D + 1;
         const int lane = threadIdx.x & 63;
@@ -121,11 +119,10 @@ struct TBStream {
             nb = *reinterpret_cast<const float4*>(pb + (int64_t)(j + 1) * P);
         }
         ring[s][lane] = cb;
-        const int depth = j - j0;  // level t is exact from row j0 + 2t on
         float4 out;
 #pragma unroll
         for (int t = 1; t <= D; ++t) {
-            if (!RAMP || 2 * t <= depth) {
+            {
                 int st = s - t;
                 if (st < 0) st += R;
                 const float4 bb = ring[st][lane];
@@ -193,18 +190,28 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     for (int t = 0; t < D; ++t) { A[t] = zero; B[t] = zero; C[t] = zero; }
     // three rows per trip, the level registers rotating A -> B -> C; the
     // trips that still fill the pipeline test which levels are exact yet
+    // Three rows per trip, the level registers rotating A -> B -> C.  The
+    // first 2D rows also compute levels that are not exact yet (level t is
+    // exact from the (2t)-th row of the band on); they are never stored, and
+    // skipping them costs more in registers than it saves.
     for (int j = st.j0; j <= st.j1; j += 3) {
-        st.template row<false>(j, A, B, C);
+        st.row(j, A, B, C);
         if (j + 1 > st.j1) break;
-        st.template row<false>(j + 1, B, C, A);
+        st.row(j + 1, B, C, A);
         if (j + 2 > st.j1) break;
-        st.template row<false>(j + 2, C, A, B);
+        st.row(j + 2, C, A, B);
     }
     return st.m;
 }
 
+// Register budget: D <= 8 fits 128 VGPRs, four wavefronts per SIMD; deeper
+// pipelines get two.
+template <int D>
+constexpr int tb_waves_per_simd() { return D <= 8 ? 4 : 2; }
+
 template <int D, bool CHK, bool FAST>
-__global__ __launch_bounds__(64) void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(tb_waves_per_simd<D>())))
+void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
                                                float* __restrict__ uout, StepArgs a, int H) {
     constexpr int Dp = (D + 3) & ~3;
     constexpr int Wout = 256 - 2 * Dp;

@@ -571,6 +571,17 @@ int jac_reset(jac_t c) {
     return JAC_OK;
 }
 
+int jac_stream_probe(float* c, const float* a, const float* b, size_t n, int kind, int nontemporal,
+                     int blocks, void* stream) {
+    if (!c || !a || (kind == 1 && !b)) return fail(JAC_EINVAL, "NULL array");
+    if (kind != 0 && kind != 1) return fail(JAC_EINVAL, "kind must be 0 (copy) or 1 (add)");
+    if (n % 4 != 0 || ((uintptr_t)a | (uintptr_t)c | (uintptr_t)(b ? b : a)) % 16 != 0)
+        return fail(JAC_EINVAL, "n must be a multiple of 4 and the arrays 16-byte aligned");
+    if (blocks < 1 || blocks > (1 << 20)) return fail(JAC_EINVAL, "blocks must be in 1..2^20");
+    JAC_HIP(launch_probe(c, a, b, (int64_t)n, kind, nontemporal != 0, blocks, (hipStream_t)stream));
+    return JAC_OK;
+}
+
 int jac_fast_division(jac_t c) {
     if (!c) return fail(JAC_EINVAL, "context is NULL");
     return c->fastdiv;
