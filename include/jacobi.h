@@ -70,7 +70,7 @@ typedef struct {
     int32_t kernel;      /* jac_kernel */
     int32_t driver;      /* jac_driver */
     int32_t D;           /* sweeps per launch: TBLOCK 1..16, ASYNC 1..32; ignored for SYNC */
-    int32_t tile_x;      /* ASYNC tile width in columns (1..256) */
+    int32_t tile_x;      /* ASYNC tile width in columns (1..256; tile_x * tile_y <= 4096) */
     int32_t tile_y;      /* ASYNC tile height in rows (1..256) */
     int32_t M;           /* check interval in sweeps (>= 1); the interval is max(M, D) */
     float tol;           /* rho threshold (> 0) */

@@ -66,7 +66,7 @@ __host__ __device__ inline uint32_t* scratch_partials(Scratch* sc) { return rein
 
 // Partial-maximum slots a context of size N reserves; every kernel that writes
 // partials is launched with at most this many blocks (checked on the host).
-inline int64_t partial_cap(int N) { return (int64_t)N * N / 1024 + 65536; }
+inline int64_t partial_cap(int N) { return (int64_t)N * N / 64 + 65536; }
 
 // Host-visible results, in pinned host memory the device writes directly.
 constexpr int kRing = 64;   // check results kept in flight
@@ -194,6 +194,11 @@ hipError_t launch_probe(float* c, const float* a, const float* b, int64_t n, int
 int64_t rhs_blocks(int N);
 int64_t sync_blocks(int N);
 int64_t tblock_blocks(int N, int D, int H);
+int64_t async_blocks(int N, int tx, int ty);
+// Block-asynchronous launch: tiles tx x ty (each 1..256, tx*ty <= 4096), a
+// frozen one-cell halo, D in-tile sweeps.
+hipError_t launch_async(const float* uin, const float* b, float* uout, int tx, int ty, int D, bool check,
+                        const StepArgs& a, hipStream_t s);
 // Automatic band height for a grid of `resident_waves` wavefront slots.
 int tblock_rows(int N, int D, int resident_waves);
 int tblock_waves_per_cu(int D, bool fast);

@@ -1,0 +1,139 @@
+// kernels_async.hip -- block-asynchronous relaxation (kernel c).
+//
+// The method (page "stencil-jacobian.vercel.app", section 01 "block-
+// asynchronous" and section 02, after Anzt et al.; also Islam & Wang,
+// "Hierarchical Jacobi Iteration for Structured Matrices on GPUs using Shared
+// Memory", section 3): each block loads its tile plus a one-cell halo into
+// on-chip memory and performs D Jacobi sweeps on the tile with the halo
+// frozen, then writes the tile back.  Values read across a tile edge are up to
+// D-1 sweeps old; with D = 1 this is the synchronous sweep.
+//
+// Here: tiles of tile_x columns by tile_y rows start at unknown (0, 0), the
+// last ones in each direction clipped to the grid.  The halo comes from the
+// iterate the launch reads (u_k, ping-pong between launches), so a launch is a
+// deterministic function of u_k and the result does not depend on scheduling.
+// One workgroup of 256 threads per tile; the tile and its halo live twice in
+// LDS (in-tile ping-pong; the halo is copied into both and never written);
+// each thread keeps b for its points in registers; a barrier separates the
+// in-tile sweeps.  Every point update uses the same float32 operations, in the
+// same order, as the synchronous sweep.
+#include "jacobi_internal.h"
+
+namespace jac {
+
+constexpr int kAsyncThreads = 256;
+constexpr int kAsyncMaxPts = 4096;                          // tile_x * tile_y
+constexpr int kAsyncPerThread = kAsyncMaxPts / kAsyncThreads;  // points per thread, at most
+
+template <bool CHK, bool FAST>
+__global__ __launch_bounds__(kAsyncThreads) void k_async(const float* __restrict__ uin,
+                                                         const float* __restrict__ bin,
+                                                         float* __restrict__ uout, StepArgs a, int tx,
+                                                         int ty, int D) {
+    extern __shared__ float lds[];
+    if (a.sc->stop) return;  // a previous check already stopped the step
+    const Geom g = a.g;
+    const int N = g.N, P = g.P;
+    const int ntx = (N + tx - 1) / tx, nty = (N + ty - 1) / ty;
+    const int t = xcd_logical_block(blockIdx.x, gridDim.x);
+    uint32_t m = 0;
+    if (t < ntx * nty) {
+        const int x0 = (t % ntx) * tx, y0 = (t / ntx) * ty;
+        const int w = (x0 + tx <= N) ? tx : N - x0;  // clipped tile
+        const int h = (y0 + ty <= N) ? ty : N - y0;
+        const int lp = w + 2;                        // LDS row pitch: tile plus halo
+        const int ln = lp * (h + 2);
+        float* A = lds;
+        float* B = lds + ln;
+        const float r = a.r, d = a.d, y = a.y;
+        // tile and halo: LDS (a, c) is unknown (y0 + a - 1, x0 + c - 1); the
+        // halo ring is a neighbour tile's u_k or the ghost ring
+        const float* src = uin + g.origin + (int64_t)(y0 - 1) * P + (x0 - 1);
+        for (int k = threadIdx.x; k < ln; k += kAsyncThreads) {
+            const int ra = k / lp, ca = k - ra * lp;
+            const float v = src[(int64_t)ra * P + ca];
+            A[k] = v;
+            B[k] = v;
+        }
+        const int npts = w * h;
+        float bb[kAsyncPerThread];
+#pragma unroll
+        for (int q = 0; q < kAsyncPerThread; ++q) {
+            const int p = threadIdx.x + q * kAsyncThreads;
+            bb[q] = 0.0f;
+            if (p < npts) {
+                const int i = p / w, j = p - (p / w) * w;
+                bb[q] = bin[g.origin + (int64_t)(y0 + i) * P + (x0 + j)];
+            }
+        }
+        __syncthreads();
+        if (CHK) {
+            // residual of u_k on the tile's points (the halo is u_k too)
+#pragma unroll
+            for (int q = 0; q < kAsyncPerThread; ++q) {
+                const int p = threadIdx.x + q * kAsyncThreads;
+                if (p < npts) {
+                    const int i = p / w, j = p - (p / w) * w;
+                    const int c = (i + 1) * lp + (j + 1);
+                    const uint32_t v = residual_bits(A[c], A[c + 1], A[c - 1], A[c - lp], A[c + lp], bb[q], r);
+                    m = m > v ? m : v;
+                }
+            }
+        }
+        float* cur = A;
+        float* nxt = B;
+        for (int s = 0; s < D; ++s) {
+#pragma unroll
+            for (int q = 0; q < kAsyncPerThread; ++q) {
+                const int p = threadIdx.x + q * kAsyncThreads;
+                if (p < npts) {
+                    const int i = p / w, j = p - (p / w) * w;
+                    const int c = (i + 1) * lp + (j + 1);
+                    nxt[c] = jacobi_update<FAST>(cur[c + 1], cur[c - 1], cur[c - lp], cur[c + lp], bb[q], r, d, y);
+                }
+            }
+            __syncthreads();
+            float* tmp = cur;
+            cur = nxt;
+            nxt = tmp;
+        }
+        float* dst = uout + g.origin + (int64_t)y0 * P + x0;
+#pragma unroll
+        for (int q = 0; q < kAsyncPerThread; ++q) {
+            const int p = threadIdx.x + q * kAsyncThreads;
+            if (p < npts) {
+                const int i = p / w, j = p - (p / w) * w;
+                dst[(int64_t)i * P + j] = cur[(i + 1) * lp + (j + 1)];
+            }
+        }
+    }
+    if (CHK) store_block_max<kAsyncThreads / 64>(m, a.sc, blockIdx.x);
+}
+
+int64_t async_blocks(int N, int tx, int ty) {
+    const int64_t tiles = (int64_t)((N + tx - 1) / tx) * ((N + ty - 1) / ty);
+    return (tiles + 7) / 8 * 8;
+}
+
+hipError_t launch_async(const float* uin, const float* b, float* uout, int tx, int ty, int D, bool check,
+                        const StepArgs& a, hipStream_t s) {
+    if (tx < 1 || ty < 1 || tx > 256 || ty > 256 || tx * ty > kAsyncMaxPts) return hipErrorInvalidValue;
+    const int64_t blocks = async_blocks(a.g.N, tx, ty);
+    if (blocks > (int64_t)0x7fffffff) return hipErrorInvalidValue;
+    const size_t lds = (size_t)2 * (tx + 2) * (ty + 2) * sizeof(float);
+    const dim3 grid((unsigned)blocks), block(kAsyncThreads);
+    if (check) {
+        if (a.fastdiv)
+            hipLaunchKernelGGL((k_async<true, true>), grid, block, lds, s, uin, b, uout, a, tx, ty, D);
+        else
+            hipLaunchKernelGGL((k_async<true, false>), grid, block, lds, s, uin, b, uout, a, tx, ty, D);
+    } else {
+        if (a.fastdiv)
+            hipLaunchKernelGGL((k_async<false, true>), grid, block, lds, s, uin, b, uout, a, tx, ty, D);
+        else
+            hipLaunchKernelGGL((k_async<false, false>), grid, block, lds, s, uin, b, uout, a, tx, ty, D);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace jac

@@ -188,10 +188,10 @@ int check_opts(const jac_ctx* c, const jac_opts* o) {
     if (o->max_sweeps < 1) return fail(JAC_EINVAL, "max_sweeps must be >= 1");
     if (o->band_rows < 0 || o->band_rows > 65536) return fail(JAC_EINVAL, "band_rows must be in 0..65536");
     if (o->kernel != JAC_SYNC && (o->D < 1 || o->D > kMaxD)) return fail(JAC_EINVAL, "D must be in 1..32");
-    if (o->kernel == JAC_ASYNC && (o->tile_x < 1 || o->tile_x > 256 || o->tile_y < 1 || o->tile_y > 256))
-        return fail(JAC_EINVAL, "tile_x and tile_y must be in 1..256");
+    if (o->kernel == JAC_ASYNC && (o->tile_x < 1 || o->tile_x > 256 || o->tile_y < 1 || o->tile_y > 256 ||
+                                   o->tile_x * o->tile_y > 4096))
+        return fail(JAC_EINVAL, "tile_x and tile_y must be in 1..256 with tile_x * tile_y <= 4096");
     if (o->kernel == JAC_TBLOCK && o->D > kMaxTBlockD) return fail(JAC_EINVAL, "TBLOCK needs D in 1..16");
-    if (o->kernel == JAC_ASYNC) return fail(JAC_EINVAL, "this kernel is not available in this build");
     if (o->driver != JAC_LAUNCH) return fail(JAC_EINVAL, "this driver is not available in this build");
     (void)c;
     return JAC_OK;
@@ -241,6 +241,13 @@ int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, i
             st = timed(c, KC_TBLOCK, [&] { return launch_tblock(in, c->b, out, m, check, a, H, c->stream); });
             break;
         }
+        case JAC_ASYNC:
+            npart = async_blocks(c->N, o->tile_x, o->tile_y);
+            if (check && npart > c->npart_cap) return fail(JAC_EINVAL, "tile too small for this N");
+            st = timed(c, KC_ASYNC, [&] {
+                return launch_async(in, c->b, out, o->tile_x, o->tile_y, m, check, a, c->stream);
+            });
+            break;
         default:
             return fail(JAC_EINVAL, "kernel not available");
     }

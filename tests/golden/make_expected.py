@@ -9,6 +9,7 @@ these hashes bit for bit.
 
     python -m tests.golden.make_expected C3          # N=8192, r=10, Gaussian
     python -m tests.golden.make_expected C4 --steps 2
+    python -m tests.golden.make_expected C3 --mode async --D 8 --tile 32 16
 """
 from __future__ import annotations
 
@@ -34,17 +35,18 @@ def field_hash(u: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(u, dtype="<f4").tobytes()).hexdigest()
 
 
-def run(name: str, steps: int | None, M: int = 8) -> dict:
+def run(name: str, steps: int | None, M: int = 8, mode: str = "sync", D: int = 1, tile=(32, 8)) -> dict:
     cfg = workloads.CONFIGS[name]
     N, r, kind = cfg["N"], cfg["r"], cfg["source"]
     steps = steps or cfg["steps"]
     s = workloads.source(kind, N, r)
     u = np.zeros((N, N), np.float32)
-    out = dict(config=name, N=N, r=r, source=kind, M=M, tol=1e-5, steps=steps, sweeps=[], rho_bits=[],
-               field_sha256=[], oracle_threads=oracle.get_threads(), seconds=[])
+    out = dict(config=name, N=N, r=r, source=kind, M=M, tol=1e-5, steps=steps, mode=mode, D=D, tile=list(tile),
+               sweeps=[], rho_bits=[], field_sha256=[], oracle_threads=oracle.get_threads(), seconds=[])
+    omode = oracle.ASYNC if mode == "async" else oracle.SYNC
     for n in range(steps):
         t0 = time.time()
-        res = oracle.solve(N, r, s, u0=u, steps=1, M=M)
+        res = oracle.solve(N, r, s, u0=u, steps=1, M=M, mode=omode, D=D, tx=tile[0], ty=tile[1])
         if res.status != oracle.OK:
             raise RuntimeError(f"{name} step {n}: oracle status {res.status}")
         u = res.u
@@ -60,9 +62,13 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("config")
     ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--mode", choices=("sync", "async"), default="sync")
+    ap.add_argument("--D", type=int, default=1)
+    ap.add_argument("--tile", type=int, nargs=2, default=(32, 8))
     args = ap.parse_args()
-    res = run(args.config, args.steps)
-    path = os.path.join(HERE, f"expected_{args.config}.json")
+    res = run(args.config, args.steps, mode=args.mode, D=args.D, tile=tuple(args.tile))
+    tag = args.config if args.mode == "sync" else f"{args.config}_async_D{args.D}_{args.tile[0]}x{args.tile[1]}"
+    path = os.path.join(HERE, f"expected_{tag}.json")
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
     print("wrote", path)

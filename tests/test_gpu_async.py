@@ -1,0 +1,138 @@
+"""Kernel (c), block-asynchronous relaxation.
+
+The result depends on the tile shape and on D, and the oracle models exactly
+that (tiles from the top-left unknown, a one-cell halo frozen at the launch's
+input iterate, D in-tile Jacobi sweeps; page "stencil-jacobian.vercel.app",
+section 02), so the kernel is held to the oracle bit for bit.  The page's own
+acceptance for the asynchronous method -- every step reaches rho < 1e-5 and the
+field stays close to the synchronous solution -- is checked too."""
+import numpy as np
+import pytest
+
+import jacobi_stencil_amd as jac
+import oracle
+import workloads
+from tests.gpu_helpers import assert_same, bits, field_hash, lib_solve, load_expected, opts, say
+
+pytestmark = pytest.mark.gpu
+
+AS = jac.JAC_ASYNC
+
+
+def interval(D, M=8):
+    return max(M, D)
+
+
+def async_ref(N, r, s, steps, D, tx, ty, u0=None, max_sweeps=10**6):
+    return oracle.solve(N, r, s, u0=u0, steps=steps, M=8, mode=oracle.ASYNC, D=D, tx=tx, ty=ty,
+                        max_sweeps=max_sweeps)
+
+
+@pytest.mark.parametrize("tile", [(32, 8), (32, 16), (64, 16), (7, 5), (1, 1), (256, 16), (13, 64)])
+@pytest.mark.parametrize("D", [1, 2, 4, 8])
+def test_tiles_and_depths_bitwise(tile, D):
+    N, r = 150, 10.0
+    tx, ty = tile
+    say("async", tile, D)
+    s = workloads.gaussian_source(N, r)
+    ref = async_ref(N, r, s, 2, D, tx, ty)
+    assert_same(lib_solve(N, r, s, 2, opts(kernel=AS, D=D, tile_x=tx, tile_y=ty)), ref, f"{tile} D={D}")
+
+
+@pytest.mark.parametrize("D", [3, 12, 16, 32])
+def test_deep_and_odd_depths_bitwise(D):
+    N, r = 97, 100.0
+    say("async deep", D)
+    s = workloads.point_source(N, r)
+    ref = async_ref(N, r, s, 2, D, 32, 16)
+    assert_same(lib_solve(N, r, s, 2, opts(kernel=AS, D=D, tile_x=32, tile_y=16)), ref, f"D={D}")
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 31, 33, 65, 255, 257])
+def test_partial_tiles_bitwise(N):
+    r = 1.0
+    say("async partial", N)
+    s = workloads.point_source(N, r)
+    ref = async_ref(N, r, s, 2, 4, 32, 8)
+    assert_same(lib_solve(N, r, s, 2, opts(kernel=AS, D=4, tile_x=32, tile_y=8)), ref, f"N={N}")
+
+
+def test_d1_equals_synchronous():
+    """Section 02: with D = 1 the block-async kernel reproduces the synchronous iterates."""
+    N, r = 129, 10.0
+    say("async d1")
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=3)
+    assert_same(lib_solve(N, r, s, 3, opts(kernel=AS, D=1, tile_x=32, tile_y=8)), ref, "D=1")
+
+
+def test_random_fields_bitwise():
+    N, r = 140, 10.0
+    say("async random")
+    s = workloads.random_source(N, r, 7)
+    u0 = workloads.random_field(N, 7)
+    ref = async_ref(N, r, s, 1, 6, 32, 16, u0=u0)
+    assert_same(lib_solve(N, r, s, 1, opts(kernel=AS, D=6, tile_x=32, tile_y=16), u0=u0), ref, "random")
+
+
+@pytest.mark.parametrize("r", [1.0, 10.0])
+def test_config_c5_bitwise(r):
+    say("async C5", r)
+    s = workloads.gaussian_source(256, r)
+    ref = async_ref(256, r, s, 10, 8, 32, 16)
+    assert_same(lib_solve(256, r, s, 10, opts(kernel=AS, D=8, tile_x=32, tile_y=16)), ref, f"C5 r={r}")
+
+
+def test_page_tolerance_against_synchronous_solution():
+    """Every step reaches rho < 1e-5 and the final field is within 1e-4 * ||b_A|| of
+    the synchronous solution; the extra-sweep ratio is reported."""
+    N, r = 512, 10.0
+    say("async tolerance")
+    s = workloads.gaussian_source(N, r)
+    st, u, k, rho = lib_solve(N, r, s, 10, opts(kernel=AS, D=8, tile_x=32, tile_y=16))
+    assert st == jac.JAC_OK and np.all(rho < 1e-5)
+    sync = oracle.solve(N, r, s)
+    # ||b_A|| of the last step, from the last synchronous u^n
+    prev = oracle.solve(N, r, s, steps=9)
+    bA = float(oracle.rhs_norm(oracle.rhs(prev.u, s), r))
+    assert np.max(np.abs(u.astype(np.float64) - sync.u)) <= 1e-4 * bA
+    ratio = k.sum() / sync.sweeps.sum()
+    print(f"[async] D8@32x16 r=10 N=512 sweep ratio s = {ratio:.3f}")
+    assert 1.0 < ratio < 2.0
+
+
+def test_noconv_keeps_checked_iterate():
+    N, r = 90, 100.0
+    say("async noconv")
+    s = workloads.point_source(N, r)
+    ref = async_ref(N, r, s, 2, 8, 32, 8, max_sweeps=40)
+    assert ref.status == oracle.ENOCONV
+    assert_same(lib_solve(N, r, s, 2, opts(kernel=AS, D=8, tile_x=32, tile_y=8, max_sweeps=40)), ref, "noconv")
+
+
+def test_bad_tiles_rejected():
+    sol = jac.Solver(64, 1.0)
+    try:
+        for tx, ty in ((0, 8), (8, 0), (257, 1), (128, 64)):
+            st, _, _ = jac.jac_step(sol.ctx, opts(kernel=AS, D=4, tile_x=tx, tile_y=ty))
+            assert st == jac.JAC_EINVAL, (tx, ty)
+    finally:
+        sol.close()
+
+
+@pytest.mark.parametrize("name", ["C3_async_D8_32x16"])
+def test_large_config_against_stored_oracle(name):
+    """N = 8192, r = 10: D = 8 at 32 x 16 tiles, every step against the oracle's hashes."""
+    exp = load_expected(name)
+    assert exp is not None
+    say("async golden", name)
+    N, r = exp["N"], exp["r"]
+    sol = jac.Solver(N, r, workloads.source(exp["source"], N, r))
+    try:
+        for n in range(exp["steps"]):
+            _, k, rho = sol.step(opts(kernel=AS, D=exp["D"], tile_x=exp["tile"][0], tile_y=exp["tile"][1]))
+            assert k == exp["sweeps"][n], f"step {n}"
+            assert f"{np.float32(rho).view(np.uint32):08x}" == exp["rho_bits"][n]
+            assert field_hash(sol.field()) == exp["field_sha256"][n], f"step {n}"
+    finally:
+        sol.close()
