@@ -63,7 +63,9 @@ enum jac_kernel {
 enum jac_driver {
     JAC_LAUNCH = 0,      /* host enqueues each launch; reads each check back */
     JAC_GRAPH = 1,       /* one HIP graph per check interval, replayed */
-    JAC_PERSISTENT = 2   /* one cooperative kernel per solve: device-side loop and decision */
+    JAC_PERSISTENT = 2   /* one cooperative kernel per jac_solve: every step, check and decision on the
+                            device; SYNC and TBLOCK use 2-D tiles staged in LDS with a D-cell ghost zone,
+                            ASYNC its own tiles; same results as JAC_LAUNCH */
 };
 
 typedef struct {
@@ -74,7 +76,7 @@ typedef struct {
     int32_t tile_y;      /* ASYNC tile height in rows (1..256) */
     int32_t M;           /* check interval in sweeps (>= 1); the interval is max(M, D) */
     float tol;           /* rho threshold (> 0) */
-    int32_t band_rows;   /* TBLOCK: output rows per wavefront band (0: chosen from N and D) */
+    int32_t band_rows;   /* TBLOCK: rows per wavefront band (LAUNCH), tile side (PERSISTENT); 0: automatic */
     int64_t max_sweeps;  /* per step; a failed check at or past it ends with JAC_ENOCONV */
 } jac_opts;
 
@@ -110,7 +112,8 @@ int jac_solve(jac_t ctx, int nsteps, const jac_opts* opts, int64_t* sweeps, floa
 
 /* Throughput entry: b = u^n + s, then exactly nsweeps sweeps with no checks;
  * the field is left at the last iterate.  If rho != NULL it receives the rho
- * of that iterate (one extra residual pass). */
+ * of that iterate (one extra residual pass).  Launches one by one whatever
+ * opts->driver says. */
 int jac_sweep(jac_t ctx, const jac_opts* opts, int64_t nsweeps, float* rho);
 
 /* Copy the current field to / from host memory (N*N floats).  Blocking. */

@@ -57,12 +57,26 @@ struct Scratch {
     uint32_t bA_bits;  // ||b_A||_inf of the current step
     uint32_t stop;     // 1 once a check of the current step has decided to stop
     uint32_t div_bad;  // inputs on which the constant-divisor quotient missed (set-up check)
-    uint32_t pad[61];
+    uint32_t pad0[13];
+    // grid barrier of the persistent kernel (cleared before each launch), each
+    // word on its own 64-byte line
+    uint32_t bar_release;  // generation block 0 has released
+    uint32_t pad1[15];
+    uint32_t bar_unused;
+    uint32_t pad2[15];
+    uint32_t bar_error;    // set when a barrier wait timed out; every block then leaves
+    uint32_t pad3[15];
     // followed by uint32_t partial[npart_cap]
 };
 static_assert(sizeof(Scratch) == 256, "scratch header is 256 bytes");
 
-__host__ __device__ inline uint32_t* scratch_partials(Scratch* sc) { return reinterpret_cast<uint32_t*>(sc + 1); }
+// Persistent-kernel barrier flags: one 128-byte line per block, after the header.
+constexpr int kMaxPersistBlocks = 2048;
+constexpr int kFlagStride = 32;  // uint32 words per flag line
+__host__ __device__ inline uint32_t* scratch_flags(Scratch* sc) { return reinterpret_cast<uint32_t*>(sc + 1); }
+__host__ __device__ inline uint32_t* scratch_partials(Scratch* sc) {
+    return scratch_flags(sc) + (size_t)kMaxPersistBlocks * kFlagStride;
+}
 
 // Partial-maximum slots a context of size N reserves; every kernel that writes
 // partials is launched with at most this many blocks (checked on the host).
@@ -195,6 +209,13 @@ int64_t rhs_blocks(int N);
 int64_t sync_blocks(int N);
 int64_t tblock_blocks(int N, int D, int H);
 int64_t async_blocks(int N, int tx, int ty);
+// The whole solve of nsteps steps in one cooperative kernel (see
+// kernels_persist.hip).  `out` is pinned host memory for nsteps records of
+// persist_out_bytes() each; `partial` needs 2 x grid slots.
+hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, const float* s, uint32_t* partial,
+                          void* out, int nsteps, int cur0, bool async_mode, int D, int L, int tile_x, int tile_y,
+                          int side, int64_t max_sweeps, int cus, int* grid_used, hipStream_t stream);
+size_t persist_out_bytes();
 // Block-asynchronous launch: tiles tx x ty (each 1..256, tx*ty <= 4096), a
 // frozen one-cell halo, D in-tile sweeps.
 hipError_t launch_async(const float* uin, const float* b, float* uout, int tx, int ty, int D, bool check,

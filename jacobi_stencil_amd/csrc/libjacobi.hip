@@ -71,6 +71,8 @@ struct jac_ctx {
     float r, d, y;
     int fastdiv;     // 1: the constant-divisor quotient was verified for this d
     int cus;         // compute units of the device
+    void* pout;      // pinned records of the persistent driver
+    int pout_cap;
     int tb_rows[kMaxTBlockD + 1];  // automatic band height per depth (0: not yet computed)
     Geom g;
     hipStream_t stream;
@@ -192,7 +194,7 @@ int check_opts(const jac_ctx* c, const jac_opts* o) {
                                    o->tile_x * o->tile_y > 4096))
         return fail(JAC_EINVAL, "tile_x and tile_y must be in 1..256 with tile_x * tile_y <= 4096");
     if (o->kernel == JAC_TBLOCK && o->D > kMaxTBlockD) return fail(JAC_EINVAL, "TBLOCK needs D in 1..16");
-    if (o->driver != JAC_LAUNCH) return fail(JAC_EINVAL, "this driver is not available in this build");
+    if (o->driver == JAC_GRAPH) return fail(JAC_EINVAL, "this driver is not available in this build");
     (void)c;
     return JAC_OK;
 }
@@ -375,6 +377,64 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
     }
 }
 
+// The whole solve in one cooperative kernel: the device runs every step,
+// check and decision; the host reads the per-step records at the end.
+struct PersistRec {
+    int64_t sweeps;
+    uint32_t R_bits, bA_bits;
+    int32_t status, cur;
+};
+
+int run_persistent(jac_ctx* c, const jac_opts* o, int nsteps, int64_t* sweeps, float* rho) {
+    if (nsteps == 0) return JAC_OK;
+    if (persist_out_bytes() != sizeof(PersistRec)) return fail(JAC_EDEVICE, "persistent record layout mismatch");
+    if (nsteps > c->pout_cap) {
+        if (c->pout) JAC_HIP(hipHostFree(c->pout));
+        c->pout = nullptr;
+        c->pout_cap = 0;
+        JAC_HIP(hipHostMalloc(&c->pout, sizeof(PersistRec) * (size_t)nsteps, hipHostMallocDefault));
+        c->pout_cap = nsteps;
+    }
+    PersistRec* rec = reinterpret_cast<PersistRec*>(c->pout);
+    for (int n = 0; n < nsteps; ++n) rec[n] = PersistRec{0, 0, 0, 1, c->cur};
+    const bool async_mode = o->kernel == JAC_ASYNC;
+    const int D = o->kernel == JAC_SYNC ? 1 : o->D;
+    const int L = (int)check_interval(o);
+    StepArgs a = base_args(c, o->tol);
+    int grid = 0;
+    c->cur_group = -1;
+    int st = timed(c, KC_PERSIST, [&] {
+        return launch_persist(a, c->u[0], c->u[1], c->b, c->s, scratch_partials(c->sc), c->pout, nsteps, c->cur,
+                              async_mode, D, L, o->tile_x, o->tile_y, o->band_rows, o->max_sweeps, c->cus, &grid,
+                              c->stream);
+    });
+    if (st) return st;
+    if (2 * (int64_t)grid > c->npart_cap) return fail(JAC_EDEVICE, "persistent grid exceeds partial slots");
+    JAC_HIP(hipStreamSynchronize(c->stream));
+    uint32_t bar_error = 0;
+    JAC_HIP(hipMemcpy(&bar_error, &c->sc->bar_error, 4, hipMemcpyDeviceToHost));
+    if (bar_error) return fail(JAC_EDEVICE, "persistent kernel: a grid barrier wait timed out");
+    int status = JAC_OK;
+    for (int n = 0; n < nsteps; ++n) {
+        const volatile PersistRec* r = &rec[n];
+        if (r->status == 1) break;
+        float R, bA;
+        const uint32_t Rb = r->R_bits, bAb = r->bA_bits;
+        std::memcpy(&R, &Rb, 4);
+        std::memcpy(&bA, &bAb, 4);
+        if (sweeps) sweeps[n] = r->sweeps;
+        if (rho) rho[n] = R / bA;
+        c->cur = r->cur;
+        if (r->status != 0) {
+            status = r->status;
+            break;
+        }
+    }
+    if (status == JAC_ENAN) return fail(JAC_ENAN, "rho is NaN");
+    if (status == JAC_ENOCONV) return fail(JAC_ENOCONV, "max_sweeps reached before rho < tol");
+    return JAC_OK;
+}
+
 }  // namespace
 
 // ============================================================== C interface
@@ -397,7 +457,8 @@ void jac_opts_default(jac_opts* o) {
 size_t jac_workspace_bytes(int N) {
     if (N < 1 || N > kMaxN) return 0;
     Geom g = make_geom(N);
-    size_t bytes = (size_t)g.plane * 4 * sizeof(float) + sizeof(Scratch) + (size_t)partial_cap(N) * 4;
+    size_t bytes = (size_t)g.plane * 4 * sizeof(float) + sizeof(Scratch) +
+                   (size_t)kMaxPersistBlocks * kFlagStride * 4 + (size_t)partial_cap(N) * 4;
     return (bytes + 255) / 256 * 256;
 }
 
@@ -431,6 +492,8 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
     }
     c->fastdiv = 0;
     c->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+    c->pout = nullptr;
+    c->pout_cap = 0;
     for (int i = 0; i <= kMaxTBlockD; ++i) c->tb_rows[i] = 0;
     c->g = make_geom(N);
     c->stream = (hipStream_t)stream;
@@ -461,8 +524,10 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
         if (hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming) != hipSuccess)
             return cleanup_fail(fail(JAC_EDEVICE, "hipEventCreateWithFlags failed"));
 
-    hipError_t e = launch_fill(base, c->g.plane * 4 + (int64_t)(sizeof(Scratch) / 4) + c->npart_cap, 0.0f,
-                               c->stream);
+    hipError_t e = launch_fill(base,
+                               c->g.plane * 4 + (int64_t)(sizeof(Scratch) / 4) +
+                                   (int64_t)kMaxPersistBlocks * kFlagStride + c->npart_cap,
+                               0.0f, c->stream);
     if (e == hipSuccess) e = launch_ghosts(c->u[0], c->g, c->stream);
     if (e == hipSuccess) e = launch_ghosts(c->u[1], c->g, c->stream);
     if (e == hipSuccess && source_host)
@@ -494,6 +559,7 @@ int jac_destroy(jac_t c) {
     }
     for (hipEvent_t e : c->free_ev) (void)hipEventDestroy(e);
     if (c->mail) (void)hipHostFree(c->mail);
+    if (c->pout) (void)hipHostFree(c->pout);
     delete c;
     return JAC_OK;
 }
@@ -509,9 +575,13 @@ int jac_solve(jac_t c, int nsteps, const jac_opts* o, int64_t* sweeps, float* rh
         if (sweeps) sweeps[n] = 0;
         if (rho) rho[n] = NAN;
     }
-    for (int n = 0; n < nsteps; ++n) {
-        st = run_step(c, o, sweeps ? &sweeps[n] : nullptr, rho ? &rho[n] : nullptr);
-        if (st) break;
+    if (o->driver == JAC_PERSISTENT) {
+        st = run_persistent(c, o, nsteps, sweeps, rho);
+    } else {
+        for (int n = 0; n < nsteps; ++n) {
+            st = run_step(c, o, sweeps ? &sweeps[n] : nullptr, rho ? &rho[n] : nullptr);
+            if (st) break;
+        }
     }
     if (c->prof_every > 0) {
         int s2 = drain_profile(c);

@@ -46,10 +46,11 @@ def test_workspace_bytes():
     n1 = jac.jac_workspace_bytes(1)
     assert n1 > 0 and n1 % 256 == 0
     # four planes of (N+128) rows, pitch rounded to 64 floats, a 256-byte scratch
-    # header and one partial-maximum slot per 64 unknowns plus 65536
+    # header, 2048 barrier flag lines of 128 bytes, and one partial-maximum slot
+    # per 64 unknowns plus 65536
     N = 8192
     P = (N + 128 + 63) // 64 * 64
-    want = 4 * 4 * P * (N + 128) + 256 + 4 * (N * N // 64 + 65536)
+    want = 4 * 4 * P * (N + 128) + 256 + 4 * 2048 * 32 + 4 * (N * N // 64 + 65536)
     assert jac.jac_workspace_bytes(N) == (want + 255) // 256 * 256
 
 

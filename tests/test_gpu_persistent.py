@@ -1,0 +1,105 @@
+"""The persistent driver: the whole solve in one cooperative kernel with the
+residual, the decision and the time loop on the device (page "stencil-jacobian.
+vercel.app", section 04, the host round trip as the cost to remove; the
+CPU-free model of the arXiv 2610.15878 summary).  Results must equal the
+oracle's exactly as with per-launch issue: SYNC and TBLOCK bit for bit with the
+synchronous oracle, ASYNC with the oracle's block-async model."""
+import numpy as np
+import pytest
+
+import jacobi_stencil_amd as jac
+import oracle
+import workloads
+from tests.gpu_helpers import assert_same, field_hash, lib_solve, load_expected, opts, say
+
+pytestmark = pytest.mark.gpu
+
+PER = jac.JAC_PERSISTENT
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 7, 33, 64, 65, 70, 129, 256, 257, 300])
+def test_sync_small_grids_bitwise(N):
+    r = 10.0
+    say("persist sync", N)
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=3)
+    assert_same(lib_solve(N, r, s, 3, opts(driver=PER)), ref, f"N={N}")
+
+
+@pytest.mark.parametrize("D", list(range(1, 17)))
+def test_tblock_every_depth_bitwise(D):
+    N, r = 150, 10.0
+    say("persist tblock", D)
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=2, M=max(8, D))
+    assert_same(lib_solve(N, r, s, 2, opts(kernel=jac.JAC_TBLOCK, D=D, driver=PER)), ref, f"D={D}")
+
+
+@pytest.mark.parametrize("tile,D", [((32, 8), 8), ((32, 16), 8), ((7, 5), 3), ((64, 16), 12)])
+def test_async_bitwise(tile, D):
+    N, r = 150, 10.0
+    say("persist async", tile, D)
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=2, M=8, mode=oracle.ASYNC, D=D, tx=tile[0], ty=tile[1])
+    got = lib_solve(N, r, s, 2, opts(kernel=jac.JAC_ASYNC, D=D, tile_x=tile[0], tile_y=tile[1], driver=PER))
+    assert_same(got, ref, f"{tile} D={D}")
+
+
+@pytest.mark.parametrize("kernel,D", [(jac.JAC_SYNC, 1), (jac.JAC_TBLOCK, 8)])
+@pytest.mark.parametrize("r", [1.0, 10.0])
+def test_config_c5_bitwise(kernel, D, r):
+    """N = 256, the launch-bound workload, ten steps in one kernel."""
+    say("persist C5", kernel, D, r)
+    s = workloads.gaussian_source(256, r)
+    ref = oracle.solve(256, r, s)
+    assert_same(lib_solve(256, r, s, 10, opts(kernel=kernel, D=D, driver=PER)), ref, f"C5 {kernel} r={r}")
+
+
+def test_config_c1_bitwise():
+    say("persist C1")
+    s = workloads.point_source(512, 1.0)
+    ref = oracle.solve(512, 1.0, s)
+    assert_same(lib_solve(512, 1.0, s, 10, opts(kernel=jac.JAC_TBLOCK, D=8, driver=PER)), ref, "C1")
+
+
+def test_config_c2_against_stored_oracle():
+    """N = 2048: more tiles than resident blocks, so blocks loop over tiles."""
+    exp = load_expected("C2")
+    say("persist C2")
+    N, r = exp["N"], exp["r"]
+    sol = jac.Solver(N, r, workloads.source(exp["source"], N, r))
+    try:
+        _, k, rho = sol.solve(exp["steps"], opts(kernel=jac.JAC_TBLOCK, D=8, driver=PER))
+        assert k.tolist() == exp["sweeps"]
+        assert [f"{v:08x}" for v in rho.view(np.uint32)] == exp["rho_bits"]
+        assert field_hash(sol.field()) == exp["field_sha256"][-1]
+    finally:
+        sol.close()
+
+
+def test_one_call_equals_step_by_step():
+    N, r = 200, 10.0
+    say("persist steps")
+    s = workloads.gaussian_source(N, r)
+    st, whole, k_whole, _ = lib_solve(N, r, s, 5, opts(kernel=jac.JAC_TBLOCK, D=4, driver=PER))
+    sol = jac.Solver(N, r, s)
+    try:
+        ks = [sol.step(opts(kernel=jac.JAC_TBLOCK, D=4, driver=PER))[1] for _ in range(5)]
+        assert ks == k_whole.tolist()
+        assert np.array_equal(sol.field().view(np.uint32), whole.view(np.uint32))
+    finally:
+        sol.close()
+
+
+def test_noconv_and_nan():
+    N, r = 90, 100.0
+    say("persist noconv")
+    s = workloads.point_source(N, r)
+    for cap in (1, 40, 41):
+        ref = oracle.solve(N, r, s, steps=2, max_sweeps=cap)
+        assert_same(lib_solve(N, r, s, 2, opts(driver=PER, max_sweeps=cap)), ref, f"cap {cap}")
+    s2 = workloads.point_source(33, 1.0)
+    s2[4, 4] = np.nan
+    ref = oracle.solve(33, 1.0, s2, steps=2)
+    st, u, k, rho = lib_solve(33, 1.0, s2, 2, opts(driver=PER))
+    assert st == jac.JAC_ENAN and k.tolist() == ref.sweeps.tolist()
