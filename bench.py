@@ -29,6 +29,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BYTES_PER_POINT_PASS = 12.0    # read u_k, read b, write the next iterate
+# non-packed float32 VALU: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# fewest VALU instructions per point-update: 3 adds, 1 mul, 1 add, and the
+# verified constant-divisor quotient (1 mul, 2 fma, 1 div_fixup)
+VALU_OPS_PER_UPDATE = 9
 METRIC = "Gpoint-updates/s + time-to-solution (10 steps), N=8192 r=10; % HBM roofline"
 KERNELS = {"sync": 0, "tblock": 1, "async": 2}
 DOMINANT_CLASS = {"sync": "sync", "tblock": "tblock", "async": "async"}
@@ -206,6 +211,19 @@ def main():
         if key in t and t[key].get("source_sha256") == _kernel_source_hash():
             traffic = t[key]["bytes_per_launch"]
 
+    common = {"traffic": traffic, "kernel_class": cls, "launches": k_n, "timed_launches": k_timed,
+              "avg_launch_us": round(launch_ms * 1e3, 3), "algorithmic_bytes_per_launch": bytes_per_launch,
+              "noop_launches": noop_n}
+    hbm = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    if args.kernel == "sync":
+        roofline = dict(hbm, **common)
+    else:
+        # D sweeps per launch: bound by VALU instruction issue (SQ counters), not by HBM
+        tops = N * N * D * VALU_OPS_PER_UPDATE / (launch_ms / 1e3) / 1e12
+        roofline = dict({"bound": "alu", "achieved": round(tops, 2), "peak": round(VALU_PEAK_TOPS, 2),
+                         "unit": "TVALUop/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
+                         "valu_ops_per_update": VALU_OPS_PER_UPDATE, "hbm_view": hbm}, **common)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -228,11 +246,7 @@ def main():
         "sweeps_per_step": sweeps.tolist(),
         "pct_hbm_roofline_model": round(100.0 * value * BYTES_PER_POINT_PASS / D / HBM_PEAK_GBS, 2),
         "stream_probe_gbs": probe,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel_class": cls, "launches": k_n, "timed_launches": k_timed,
-                     "avg_launch_us": round(launch_ms * 1e3, 3),
-                     "bytes_per_launch": bytes_per_launch, "noop_launches": noop_n},
+        "roofline": roofline,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_steps)
