@@ -62,7 +62,7 @@ enum jac_kernel {
 /* How the launches of a step are issued. */
 enum jac_driver {
     JAC_LAUNCH = 0,      /* host enqueues each launch; reads each check back */
-    JAC_GRAPH = 1,       /* one HIP graph per check interval, replayed */
+    JAC_GRAPH = 1,       /* each check interval captured once as a HIP graph and replayed */
     JAC_PERSISTENT = 2   /* one cooperative kernel per jac_solve: every step, check and decision on the
                             device; SYNC and TBLOCK use 2-D tiles staged in LDS with a D-cell ghost zone,
                             ASYNC its own tiles; same results as JAC_LAUNCH */

@@ -57,7 +57,8 @@ struct Scratch {
     uint32_t bA_bits;  // ||b_A||_inf of the current step
     uint32_t stop;     // 1 once a check of the current step has decided to stop
     uint32_t div_bad;  // inputs on which the constant-divisor quotient missed (set-up check)
-    uint32_t pad0[13];
+    uint32_t check_seq;  // checks reduced so far in this step (the mailbox slot of the next)
+    uint32_t pad0[12];
     // grid barrier of the persistent kernel (cleared before each launch), each
     // word on its own 64-byte line
     uint32_t bar_release;  // generation block 0 has released
@@ -99,7 +100,7 @@ struct StepArgs {
     int fastdiv;    // 1: that quotient was verified equal to n/d for every float n
     Scratch* sc;
     Mailbox* mail;
-    int slot;       // mailbox slot for this kernel's check (if it makes one)
+    int slot;       // mailbox slot for this kernel's check; < 0: the device's check counter
 };
 
 // ---------------------------------------------------------------- device
@@ -196,9 +197,10 @@ hipError_t launch_rhs(const float* u, const float* src, float* b, const StepArgs
 // Count the float inputs n (all 2^32) on which div_d<true> differs from n / d
 // into sc->div_bad (NaN results count as equal when both are NaN).
 hipError_t launch_verify_div(float d, float y, Scratch* sc, hipStream_t s);
-// Reduce npart partials.  norm: they are |b_A| maxima -- publish ||b_A|| and
-// clear the stop flag.  Otherwise they are |res| maxima of a check -- unless
-// the step has already stopped, publish R in mailbox slot a.slot and set the
+// Reduce npart partials.  norm: they are |b_A| maxima -- publish ||b_A||, clear
+// the stop flag and the check counter.  Otherwise they are |res| maxima of a
+// check -- unless the step has already stopped, publish R in mailbox slot
+// a.slot (a.slot < 0: slot check_seq % kRing), count the check, and set the
 // stop flag when !(R / ||b_A|| >= tol).
 hipError_t launch_reduce(int64_t npart, bool norm, const StepArgs& a, hipStream_t s);
 // Bandwidth probe: kind 0 copy (c = a), kind 1 add (c = a + b); n floats.

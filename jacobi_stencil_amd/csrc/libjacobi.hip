@@ -73,6 +73,14 @@ struct jac_ctx {
     int cus;         // compute units of the device
     void* pout;      // pinned records of the persistent driver
     int pout_cap;
+    // graph driver: one captured check interval per start buffer, for the
+    // options they were captured with
+    hipStream_t cap_stream;
+    bool graphs_valid;
+    jac_opts graph_key;
+    hipGraphExec_t g_first[2];  // sweeps 1..L of a step (no check), by start buffer
+    hipGraphExec_t g_group[2];  // one checking interval, by start buffer
+    int g_flips_first, g_flips_group;  // buffer parity change across each graph
     int tb_rows[kMaxTBlockD + 1];  // automatic band height per depth (0: not yet computed)
     Geom g;
     hipStream_t stream;
@@ -194,7 +202,6 @@ int check_opts(const jac_ctx* c, const jac_opts* o) {
                                    o->tile_x * o->tile_y > 4096))
         return fail(JAC_EINVAL, "tile_x and tile_y must be in 1..256 with tile_x * tile_y <= 4096");
     if (o->kernel == JAC_TBLOCK && o->D > kMaxTBlockD) return fail(JAC_EINVAL, "TBLOCK needs D in 1..16");
-    if (o->driver == JAC_GRAPH) return fail(JAC_EINVAL, "this driver is not available in this build");
     (void)c;
     return JAC_OK;
 }
@@ -305,8 +312,85 @@ float mail_float(const volatile uint32_t* p) {
     return f;
 }
 
+// ---- graph driver: capture one interval of launches, replay it
+
+void drop_graphs(jac_ctx* c) {
+    for (int i = 0; i < 2; ++i) {
+        if (c->g_first[i]) (void)hipGraphExecDestroy(c->g_first[i]);
+        if (c->g_group[i]) (void)hipGraphExecDestroy(c->g_group[i]);
+        c->g_first[i] = c->g_group[i] = nullptr;
+    }
+    c->graphs_valid = false;
+}
+
+bool same_graph_key(const jac_opts* a, const jac_opts* b) {
+    return a->kernel == b->kernel && a->D == b->D && a->M == b->M && a->tile_x == b->tile_x &&
+           a->tile_y == b->tile_y && a->band_rows == b->band_rows && a->tol == b->tol;
+}
+
+// Capture the launches of one interval starting from u[start] on a private
+// stream.  The checking launch's reduction takes its mailbox slot from the
+// device's check counter, so the graph replays with constant arguments.
+int capture_interval(jac_ctx* c, const jac_opts* o, int start, bool check, hipGraphExec_t* out, int* flips) {
+    if (!c->cap_stream) JAC_HIP(hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
+    const hipStream_t saved = c->stream;
+    const int saved_prof = c->prof_every;
+    c->stream = c->cap_stream;
+    c->prof_every = 0;
+    int st = JAC_OK;
+    hipError_t e = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal);
+    int buf = start;
+    if (e == hipSuccess) {
+        const int64_t L = check_interval(o);
+        if (check) {
+            const int64_t first = std::min<int64_t>(L, sweeps_per_launch(o));
+            st = enqueue_sweeps(c, o, first, true, -1, &buf);
+            if (!st) st = enqueue_sweeps(c, o, L - first, false, -1, &buf);
+        } else {
+            st = enqueue_sweeps(c, o, L, false, -1, &buf);
+        }
+    }
+    hipGraph_t graph = nullptr;
+    if (e == hipSuccess) {
+        hipError_t e2 = hipStreamEndCapture(c->cap_stream, &graph);
+        if (e2 != hipSuccess && !st) st = fail(JAC_EDEVICE, std::string("hipStreamEndCapture: ") + hipGetErrorString(e2));
+    }
+    c->stream = saved;
+    c->prof_every = saved_prof;
+    if (e != hipSuccess) return fail(JAC_EDEVICE, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
+    if (st) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+    }
+    e = hipGraphInstantiate(out, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(JAC_EDEVICE, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+    *flips = buf != start;
+    return JAC_OK;
+}
+
+int graph_for(jac_ctx* c, const jac_opts* o, bool check, int start, hipGraphExec_t* g, int* flips) {
+    if (!c->graphs_valid || !same_graph_key(&c->graph_key, o)) {
+        drop_graphs(c);
+        c->graph_key = *o;
+        c->graphs_valid = true;
+    }
+    hipGraphExec_t* slot = check ? &c->g_group[start] : &c->g_first[start];
+    int* fl = check ? &c->g_flips_group : &c->g_flips_first;
+    if (!*slot) {
+        int st = capture_interval(c, o, start, check, slot, fl);
+        if (st) return st;
+    }
+    *g = *slot;
+    *flips = *fl;
+    return JAC_OK;
+}
+
+// One step through the launch or the graph driver.  Check g (g >= 1) examines
+// u_{gL}; its R lands in mailbox slot (g - 1) % kRing.
 int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out) {
     const int64_t L = check_interval(o);
+    const bool graph = o->driver == JAC_GRAPH;
     c->step_serial += 1;
     c->cur_group = -1;
     c->cur_first = false;
@@ -319,14 +403,24 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
     int buf = c->cur;
     c->cur_group = 0;
     c->cur_first = true;
-    st = enqueue_sweeps(c, o, L, false, 0, &buf);  // group 0: sweeps 1..L
-    if (st) return st;
+    if (graph) {  // group 0: sweeps 1..L
+        hipGraphExec_t gx;
+        int flips;
+        st = graph_for(c, o, false, buf, &gx, &flips);
+        if (st) return st;
+        JAC_HIP(hipGraphLaunch(gx, c->stream));
+        buf ^= flips;
+    } else {
+        st = enqueue_sweeps(c, o, L, false, 0, &buf);
+        if (st) return st;
+    }
 
     int64_t g_enq = 1;  // next group to enqueue
     bool final_enqueued = false;
     auto enqueue_group = [&]() -> int {
-        const int slot = (int)(g_enq % kRing);
-        c->start_buf[slot] = buf;
+        const int ev = (int)(g_enq % kRing);
+        const int slot = (int)((g_enq - 1) % kRing);
+        c->start_buf[ev] = buf;
         c->mail->R[slot] = kEmpty;
         c->cur_group = g_enq;
         c->cur_first = true;
@@ -335,14 +429,22 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
             // the last allowed check: measure only, keep u_{gL} in place
             s2 = enqueue_residual(c, o->tol, buf, slot);
             if (s2) return s2;
-            JAC_HIP(hipEventRecord(c->ev[slot], c->stream));
+            JAC_HIP(hipEventRecord(c->ev[ev], c->stream));
             final_enqueued = true;
+        } else if (graph) {
+            hipGraphExec_t gx;
+            int flips;
+            s2 = graph_for(c, o, true, buf, &gx, &flips);
+            if (s2) return s2;
+            JAC_HIP(hipGraphLaunch(gx, c->stream));
+            JAC_HIP(hipEventRecord(c->ev[ev], c->stream));
+            buf ^= flips;
         } else {
             // one launch that checks u_{gL} and starts the next interval, then the rest
             const int64_t first = std::min<int64_t>(L, sweeps_per_launch(o));
             s2 = enqueue_sweeps(c, o, first, true, slot, &buf);
             if (s2) return s2;
-            JAC_HIP(hipEventRecord(c->ev[slot], c->stream));
+            JAC_HIP(hipEventRecord(c->ev[ev], c->stream));
             s2 = enqueue_sweeps(c, o, L - first, false, slot, &buf);
             if (s2) return s2;
         }
@@ -357,8 +459,9 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
             st = enqueue_group();
             if (st) return st;
         }
-        const int slot = (int)(g % kRing);
-        JAC_HIP(hipEventSynchronize(c->ev[slot]));
+        const int ev = (int)(g % kRing);
+        const int slot = (int)((g - 1) % kRing);
+        JAC_HIP(hipEventSynchronize(c->ev[ev]));
         const uint32_t Rb = read_mail(&c->mail->R[slot]);
         if (Rb == kEmpty) return fail(JAC_EDEVICE, "a residual check did not report");
         const float R = mail_float(&c->mail->R[slot]);
@@ -367,12 +470,16 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
         const bool stop = !(rho >= o->tol);
         if (stop || k >= o->max_sweeps) {
             if (c->prof_every > 0 && stop) mark_noops(c, g);
-            c->cur = c->start_buf[slot];
+            c->cur = c->start_buf[ev];
             if (sweeps_out) *sweeps_out = k;
             if (rho_out) *rho_out = rho;
             if (std::isnan(rho)) return fail(JAC_ENAN, "rho is NaN");
             if (!stop) return fail(JAC_ENOCONV, "max_sweeps reached before rho < tol");
             return JAC_OK;
+        }
+        if (c->prof_every > 0 && c->recs.size() > 8192) {
+            st = drain_profile(c, c->step_serial);  // keep this step's records (their class may change)
+            if (st) return st;
         }
     }
 }
@@ -494,6 +601,10 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
     c->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
     c->pout = nullptr;
     c->pout_cap = 0;
+    c->cap_stream = nullptr;
+    c->graphs_valid = false;
+    for (int i = 0; i < 2; ++i) { c->g_first[i] = nullptr; c->g_group[i] = nullptr; }
+    c->g_flips_first = c->g_flips_group = 0;
     for (int i = 0; i <= kMaxTBlockD; ++i) c->tb_rows[i] = 0;
     c->g = make_geom(N);
     c->stream = (hipStream_t)stream;
@@ -560,6 +671,11 @@ int jac_destroy(jac_t c) {
     for (hipEvent_t e : c->free_ev) (void)hipEventDestroy(e);
     if (c->mail) (void)hipHostFree(c->mail);
     if (c->pout) (void)hipHostFree(c->pout);
+    for (int i = 0; i < 2; ++i) {
+        if (c->g_first[i]) (void)hipGraphExecDestroy(c->g_first[i]);
+        if (c->g_group[i]) (void)hipGraphExecDestroy(c->g_group[i]);
+    }
+    if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
     delete c;
     return JAC_OK;
 }

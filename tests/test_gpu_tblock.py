@@ -154,3 +154,22 @@ def test_band_heights_bitwise(H):
     s = workloads.gaussian_source(N, r)
     ref = oracle.solve(N, r, s, steps=2)
     assert_same(lib_solve(N, r, s, 2, opts(kernel=TB, D=D, band_rows=H)), ref, f"H={H}")
+
+
+@pytest.mark.parametrize("kernel,D", [(TB, 8), (jac.JAC_SYNC, 1)])
+def test_config_c4_against_stored_oracle(kernel, D):
+    """N = 18432, r = 100, point source, ten steps (14160 sweeps), every step
+    against the oracle's stored field hash."""
+    exp = load_expected("C4")
+    assert exp is not None
+    say("C4", kernel, D)
+    N, r = exp["N"], exp["r"]
+    sol = jac.Solver(N, r, workloads.source(exp["source"], N, r))
+    try:
+        for n in range(exp["steps"]):
+            _, k, rho = sol.step(opts(kernel=kernel, D=D))
+            assert k == exp["sweeps"][n], f"step {n}"
+            assert f"{np.float32(rho).view(np.uint32):08x}" == exp["rho_bits"][n]
+            assert field_hash(sol.field()) == exp["field_sha256"][n], f"step {n}"
+    finally:
+        sol.close()
