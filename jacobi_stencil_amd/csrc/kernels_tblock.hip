@@ -120,9 +120,10 @@ struct TBStream {
         }
         ring[s][lane] = cb;
         float4 out;
+        const int depth = j - j0;  // level t is exact from the (2t)-th row of the band on
 #pragma unroll
         for (int t = 1; t <= D; ++t) {
-            {
+            if (2 * t <= depth) {
                 int st = s - t;
                 if (st < 0) st += R;
                 const float4 bb = ring[st][lane];
@@ -188,12 +189,9 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     float4 A[D], B[D], C[D];
 #pragma unroll
     for (int t = 0; t < D; ++t) { A[t] = zero; B[t] = zero; C[t] = zero; }
-    // three rows per trip, the level registers rotating A -> B -> C; the
-    // trips that still fill the pipeline test which levels are exact yet
-    // Three rows per trip, the level registers rotating A -> B -> C.  The
-    // first 2D rows also compute levels that are not exact yet (level t is
-    // exact from the (2t)-th row of the band on); they are never stored, and
-    // skipping them costs more in registers than it saves.
+    // Three rows per trip, the level registers rotating A -> B -> C.  While
+    // the pipeline fills (the first 2D rows of the band) a row computes only
+    // the levels that are already exact.
     for (int j = st.j0; j <= st.j1; j += 3) {
         st.row(j, A, B, C);
         if (j + 1 > st.j1) break;
