@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--profile-every", type=int, default=16,
                     help="bracket every k-th launch of a class with HIP events (0: none)")
-    ap.add_argument("--cpu-steps", type=int, default=2, help="time steps in the CPU sample")
+    ap.add_argument("--cpu-steps", type=int, default=10, help="time steps in the CPU sample")
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="array size of the bandwidth probe, MiB (0: skip)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),

@@ -154,6 +154,28 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
+// Lane i receives lane i-1's value (lane 0 receives 0): DPP wave_shr:1.
+__device__ __forceinline__ float from_left(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xF, 0xF, true));
+}
+// Lane i receives lane i+1's value (lane 63 receives 0): DPP wave_shl:1.
+__device__ __forceinline__ float from_right(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x130, 0xF, 0xF, true));
+}
+
+// 16-byte loads and stores; _nt marks them nontemporal (streamed data that
+// this kernel reads or writes once: keeps it from displacing reused lines).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ld4_nt(const float* p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st4_nt(float* p, const float4& v) {
+    const f32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p));
+}
+
 // Blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous
 // range of logical tiles so that vertically adjacent tiles (which share halo
 // rows) sit behind the same L2.  nblocks must be a multiple of 8; logical ids

@@ -58,8 +58,8 @@ __global__ __launch_bounds__(256) void k_rhs(const float* __restrict__ u, const 
     for (int i = blockIdx.y; i < g.N; i += gridDim.y) {
         if (col0 >= g.N) break;
         const int64_t o = g.origin + (int64_t)i * g.P + col0;
-        float4 uu = *reinterpret_cast<const float4*>(u + o);
-        float4 ss = *reinterpret_cast<const float4*>(src + o);
+        float4 uu = ld4_nt(u + o);
+        float4 ss = ld4_nt(src + o);
         float4 bb;
         bb.x = uu.x + ss.x;
         bb.y = uu.y + ss.y;
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void k_rhs(const float* __restrict__ u, const 
             }
         }
         if (col0 + 4 <= g.N) {
-            *reinterpret_cast<float4*>(b + o) = bb;
+            st4_nt(b + o, bb);
         } else {
             for (int c = 0; c < 4; ++c)
                 if (col0 + c < g.N) b[o + c] = vb[c];
@@ -182,8 +182,6 @@ __device__ __forceinline__ void sync_row(const float4& up, const float4& mid, co
     }
 }
 
-__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-
 // One sweep u_{k+1} = J(u_k).  With CHECK the same pass also measures the
 // residual of u_k (the iterate it reads), which costs no extra memory traffic;
 // RESID_ONLY measures the residual and writes nothing.
@@ -211,20 +209,42 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
         const float* pb = bin + o;
         float* po = uout + o;
         if (wcol + 256 <= N && row0 + H <= N) {
-            // interior wavefront: 256 full columns, H full rows
+            // interior wavefront: 256 full columns, H full rows.  West/east
+            // neighbours come from the adjacent lanes (DPP); lanes 0 and 63 take
+            // the columns just outside the wavefront, loaded for all H rows up
+            // front (lane i holds row i).  Rows and b stream with nontemporal
+            // loads, except the two rows shared with the bands above and below.
+            const int erow = lane < H ? lane : 0;
+            const float wedge = uin[g.origin + (int64_t)(row0 + erow) * P + wcol - 1];
+            const float eedge = uin[g.origin + (int64_t)(row0 + erow) * P + wcol + 256];
             float4 up = ld4(pu - P);
-            float4 mid = ld4(pu);
+            float4 mid = ld4_nt(pu);
+            // rows in groups of four: the loads of a group are all in flight
+            // before its first row is computed
 #pragma unroll
-            for (int i = 0; i < H; ++i) {
-                const float4 dn = ld4(pu + (int64_t)(i + 1) * P);
-                const float4 bb = ld4(pb + (int64_t)i * P);
-                const float wl = pu[(int64_t)i * P - 1];
-                const float er = pu[(int64_t)i * P + 4];
-                float4 o4;
-                sync_row<SWEEP, CHK, FAST>(up, mid, dn, bb, wl, er, r, d, y, o4, m, 4);
-                if (SWEEP) *reinterpret_cast<float4*>(po + (int64_t)i * P) = o4;
-                up = mid;
-                mid = dn;
+            for (int i0 = 0; i0 < H; i0 += 4) {
+                float4 dn[4], bb[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int i = i0 + k;
+                    dn[k] = (i == H - 1) ? ld4(pu + (int64_t)(i + 1) * P) : ld4_nt(pu + (int64_t)(i + 1) * P);
+                    bb[k] = ld4_nt(pb + (int64_t)i * P);
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int i = i0 + k;
+                    float wl = from_left(mid.w);
+                    float er = from_right(mid.x);
+                    const float ws = __shfl(wedge, i, 64);
+                    const float es = __shfl(eedge, i, 64);
+                    wl = lane == 0 ? ws : wl;
+                    er = lane == 63 ? es : er;
+                    float4 o4;
+                    sync_row<SWEEP, CHK, FAST>(up, mid, dn[k], bb[k], wl, er, r, d, y, o4, m, 4);
+                    if (SWEEP) st4_nt(po + (int64_t)i * P, o4);
+                    up = mid;
+                    mid = dn[k];
+                }
             }
         } else if (col0 < N) {
             // edge wavefront: ragged rows and/or columns
