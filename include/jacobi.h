@@ -124,14 +124,25 @@ int jac_set_field(jac_t ctx, const float* host_in);
 int jac_reset(jac_t ctx);
 
 /*
- * Division path of the sweep: 1 if the context divides by d = 1 + 4r through
- * its correctly rounded reciprocal and one fma correction, 0 if through IEEE
- * division, < 0 on error.  jac_create takes the first only after checking on
- * the device that it returns the IEEE quotient bit for bit on all 2^32 float
- * inputs for this d; environment variable JACOBI_IEEE_DIVISION=1 at create
- * time forces the second.  Results are identical either way.
+ * Division by d = 1 + 4r in the sweep.  The fast path multiplies by the
+ * correctly rounded reciprocal and applies one fma correction; it has no
+ * special-case fixup and differs from IEEE division only on numerators that
+ * are Inf, NaN or -0.  jac_create enables it only after checking on the device
+ * that it returns the IEEE quotient bit for bit on every other float input for
+ * this d; environment variable JACOBI_IEEE_DIVISION=1 at create time disables
+ * it.  Even then, each step (each jac_sweep, each persistent solve) uses it
+ * only if the host can show that no such numerator occurs: the source holds no
+ * -0, Inf or NaN, and a bound on |u| carried from step to step (a weighted-mean
+ * bound, reset by jac_reset and jac_set_field) keeps every numerator finite;
+ * otherwise that work divides by IEEE division.  Results are identical either
+ * way.  Returns 1 if the fast path is enabled for the context, 0 if not,
+ * < 0 on error.
  */
 int jac_fast_division(jac_t ctx);
+
+/* Division path the most recent step, sweep or persistent solve took: 1 the
+ * fast path, 0 IEEE division (also before any work), < 0 on error. */
+int jac_last_division(jac_t ctx);
 
 /* Release the context (not the workspace).  NULL is accepted. */
 int jac_destroy(jac_t ctx);

@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "JAC_OK", -1: "JAC_EINVAL", -2: "JAC_ENOMEM", -3: "JAC_EDEVIC
                 -5: "JAC_ENAN"}
 
 EXPORTS = ("jac_opts_default", "jac_workspace_bytes", "jac_create", "jac_step", "jac_solve", "jac_sweep",
-           "jac_get_field", "jac_set_field", "jac_reset", "jac_fast_division", "jac_destroy", "jac_last_error",
+           "jac_get_field", "jac_set_field", "jac_reset", "jac_fast_division", "jac_last_division", "jac_destroy",
+           "jac_last_error",
            "jac_profile", "jac_profile_read", "jac_stream_probe")
 
 
@@ -72,6 +73,7 @@ def load_library():
         lib.jac_set_field.argtypes = [vp, vp]
         lib.jac_reset.argtypes = [vp]
         lib.jac_fast_division.argtypes = [vp]
+        lib.jac_last_division.argtypes = [vp]
         lib.jac_stream_probe.argtypes = [vp, vp, vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
         lib.jac_destroy.argtypes = [vp]
         lib.jac_last_error.argtypes = []
@@ -159,6 +161,10 @@ def jac_reset(ctx) -> int:
 
 def jac_fast_division(ctx) -> int:
     return load_library().jac_fast_division(ctx)
+
+
+def jac_last_division(ctx) -> int:
+    return load_library().jac_last_division(ctx)
 
 
 def jac_destroy(ctx) -> int:
@@ -262,6 +268,14 @@ class Solver:
     @property
     def fast_division(self) -> bool:
         v = jac_fast_division(self.ctx)
+        if v < 0:
+            _check(v)
+        return bool(v)
+
+    @property
+    def last_division_fast(self) -> bool:
+        """True if the most recent step, sweep or solve divided by the fast path."""
+        v = jac_last_division(self.ctx)
         if v < 0:
             _check(v)
         return bool(v)

@@ -97,7 +97,7 @@ struct StepArgs {
     Geom g;
     float r, d, tol;
     float y;        // RN(1/d), for the constant-divisor quotient
-    int fastdiv;    // 1: that quotient was verified equal to n/d for every float n
+    int fastdiv;    // 1: divide by the constant-divisor quotient (see div_d)
     Scratch* sc;
     Mailbox* mail;
     int slot;       // mailbox slot for this kernel's check; < 0: the device's check counter
@@ -108,17 +108,17 @@ struct StepArgs {
 // n / d, rounded to nearest.  FAST uses the reciprocal y = RN(1/d) and one
 // correction step (Markstein, "Computation of elementary functions on the IBM
 // RISC System/6000 processor", IBM J. Res. Dev. 34(1), 1990): q0 = RN(n*y),
-// e = n - q0*d exactly by one fma, q = RN(q0 + e*y); v_div_fixup then applies
-// the IEEE special cases (signed zeros, infinities, NaN).  The result equals
-// the correctly rounded quotient only where verified: a context uses FAST only
-// after a set-up kernel has compared it with n / d on all 2^32 inputs for its d.
+// e = n - q0*d exactly by one fma, q = RN(q0 + e*y).  It has no special-case
+// fixup, so it is not the IEEE quotient for n = +-Inf, NaN or -0 (Inf gives
+// NaN, -0 gives +0).  A context uses FAST only (1) after a set-up kernel has
+// found it equal to n / d on every other float n for its d, and (2) for work
+// in which the host has shown that no numerator is Inf, NaN or -0.
 template <bool FAST>
 __device__ __forceinline__ float div_d(float n, float d, float y) {
     if constexpr (FAST) {
         const float q0 = n * y;
         const float e = __builtin_fmaf(-q0, d, n);
-        const float q = __builtin_fmaf(e, y, q0);
-        return __builtin_amdgcn_div_fixupf(q, d, n);
+        return __builtin_fmaf(e, y, q0);
     } else {
         return n / d;
     }
@@ -216,8 +216,8 @@ __device__ __forceinline__ void store_block_max(uint32_t m, Scratch* sc, int64_t
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_ghosts(float* u, const Geom& g, hipStream_t s);
 hipError_t launch_rhs(const float* u, const float* src, float* b, const StepArgs& a, hipStream_t s);
-// Count the float inputs n (all 2^32) on which div_d<true> differs from n / d
-// into sc->div_bad (NaN results count as equal when both are NaN).
+// Count the float inputs n (all 2^32 except Inf, NaN and -0) on which
+// div_d<true> differs from n / d into sc->div_bad.
 hipError_t launch_verify_div(float d, float y, Scratch* sc, hipStream_t s);
 // Reduce npart partials.  norm: they are |b_A| maxima -- publish ||b_A||, clear
 // the stop flag and the check counter.  Otherwise they are |res| maxima of a

@@ -310,11 +310,13 @@ __global__ __launch_bounds__(256) void k_verify_div(float d, float y, Scratch* s
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     uint32_t bad = 0;
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += stride) {
-        const float n = __uint_as_float((uint32_t)i);
+        const uint32_t bits = (uint32_t)i;
+        // the numerators the host keeps away from the fast quotient: Inf, NaN, -0
+        if ((bits & 0x7F800000u) == 0x7F800000u || bits == 0x80000000u) continue;
+        const float n = __uint_as_float(bits);
         const float q = div_d<false>(n, d, y);
         const float f = div_d<true>(n, d, y);
-        const bool same = __float_as_uint(q) == __float_as_uint(f) || (q != q && f != f);
-        bad += same ? 0u : 1u;
+        bad += __float_as_uint(q) == __float_as_uint(f) ? 0u : 1u;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) bad += (uint32_t)__shfl_xor((int)bad, o, 64);

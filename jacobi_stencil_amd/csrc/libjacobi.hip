@@ -18,6 +18,7 @@
 #include "jacobi_internal.h"
 
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -70,6 +71,11 @@ struct jac_ctx {
     int N;
     float r, d, y;
     int fastdiv;     // 1: the constant-divisor quotient was verified for this d
+    int fast_now;    // division path of the work being enqueued (see division_path)
+    bool src_plain;  // the source is finite and holds no -0
+    double smax;     // max |s|
+    double ubound;   // upper bound on max |u| over u^n and its ghost ring (Inf: none)
+    int graph_fast;  // division path the cached graphs were captured with
     int cus;         // compute units of the device
     void* pout;      // pinned records of the persistent driver
     int pout_cap;
@@ -108,13 +114,43 @@ struct jac_ctx {
 
 namespace {
 
+// Division path for the next piece of work: `steps` rounds of (b = u + s,
+// then at most `sweeps` sweeps).  The fast quotient is exact on every float
+// numerator except Inf, NaN and -0, so it is taken only where none can occur.
+// -0: n = b + r*S is -0 only if b is (a rounded sum is -0 only when both
+// terms are), and b = u + s only if s is -- the source has none.  Inf/NaN:
+// each update is a weighted mean, u' = (b + r*(uE+uW+uN+uS)) / (1 + 4r), so
+// with U bounding |u| and B = U + max|s| bounding |b|, |u| stays below
+// max(U, B) = B up to at most 8 roundings per sweep, a factor below
+// (1 + 2^-20) per sweep; then no intermediate of the update exceeds
+// B' + 4r B', B' the grown bound, and if that is finite no numerator overflows.
+// The bound only grows: it is refreshed from the sweeps actually run after
+// each step, and reset by jac_reset / jac_set_field.
+int division_path(const jac_ctx* c, int steps, double sweeps, double* u_after = nullptr) {
+    if (!c->fastdiv || !c->src_plain) return 0;
+    double U = c->ubound;
+    const double grow = std::exp(sweeps * std::ldexp(1.0, -20));
+    for (int n = 0; n < steps; ++n) {
+        const double B = (U + c->smax) * grow;
+        if (!((B + 4.0 * (double)c->r * B) * 1.001 < (double)FLT_MAX)) return 0;
+        U = B;
+    }
+    if (u_after) *u_after = U;
+    return 1;
+}
+
+// Refresh the bound after work that ran `sweeps` sweeps after one RHS.
+void grow_ubound(jac_ctx* c, double sweeps) {
+    c->ubound = (c->ubound + c->smax) * std::exp(sweeps * std::ldexp(1.0, -20));
+}
+
 StepArgs base_args(const jac_ctx* c, float tol) {
     StepArgs a;
     a.g = c->g;
     a.r = c->r;
     a.d = c->d;
     a.y = c->y;
-    a.fastdiv = c->fastdiv;
+    a.fastdiv = c->fast_now;
     a.tol = tol;
     a.sc = c->sc;
     a.mail = c->mail;
@@ -370,10 +406,11 @@ int capture_interval(jac_ctx* c, const jac_opts* o, int start, bool check, hipGr
 }
 
 int graph_for(jac_ctx* c, const jac_opts* o, bool check, int start, hipGraphExec_t* g, int* flips) {
-    if (!c->graphs_valid || !same_graph_key(&c->graph_key, o)) {
+    if (!c->graphs_valid || !same_graph_key(&c->graph_key, o) || c->graph_fast != c->fast_now) {
         drop_graphs(c);
         c->graph_key = *o;
         c->graphs_valid = true;
+        c->graph_fast = c->fast_now;
     }
     hipGraphExec_t* slot = check ? &c->g_group[start] : &c->g_first[start];
     int* fl = check ? &c->g_flips_group : &c->g_flips_first;
@@ -391,6 +428,8 @@ int graph_for(jac_ctx* c, const jac_opts* o, bool check, int start, hipGraphExec
 int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out) {
     const int64_t L = check_interval(o);
     const bool graph = o->driver == JAC_GRAPH;
+    // sweeps this step may run: up to max_sweeps, plus the interval queued beyond a check
+    c->fast_now = division_path(c, 1, (double)o->max_sweeps + 2.0 * (double)L);
     c->step_serial += 1;
     c->cur_group = -1;
     c->cur_first = false;
@@ -507,6 +546,7 @@ int run_persistent(jac_ctx* c, const jac_opts* o, int nsteps, int64_t* sweeps, f
     const bool async_mode = o->kernel == JAC_ASYNC;
     const int D = o->kernel == JAC_SYNC ? 1 : o->D;
     const int L = (int)check_interval(o);
+    c->fast_now = division_path(c, nsteps, (double)o->max_sweeps + 2.0 * (double)L);
     StepArgs a = base_args(c, o->tol);
     int grid = 0;
     c->cur_group = -1;
@@ -532,6 +572,7 @@ int run_persistent(jac_ctx* c, const jac_opts* o, int nsteps, int64_t* sweeps, f
         if (sweeps) sweeps[n] = r->sweeps;
         if (rho) rho[n] = R / bA;
         c->cur = r->cur;
+        grow_ubound(c, (double)r->sweeps);
         if (r->status != 0) {
             status = r->status;
             break;
@@ -598,6 +639,22 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
         c->y = 1.0f / c->d;  // correctly rounded on the host (SSE division)
     }
     c->fastdiv = 0;
+    c->fast_now = 0;
+    c->graph_fast = -1;
+    c->ubound = 100.0;  // u^0 = 0 and the top ghost row
+    c->smax = 0.0;
+    c->src_plain = true;
+    if (source_host) {
+        for (int64_t i = 0; i < (int64_t)N * N; ++i) {
+            const float v = source_host[i];
+            const double a = std::fabs((double)v);
+            if (!std::isfinite(a) || (v == 0.0f && std::signbit(v))) {
+                c->src_plain = false;
+                break;
+            }
+            if (a > c->smax) c->smax = a;
+        }
+    }
     c->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
     c->pout = nullptr;
     c->pout_cap = 0;
@@ -695,10 +752,14 @@ int jac_solve(jac_t c, int nsteps, const jac_opts* o, int64_t* sweeps, float* rh
         st = run_persistent(c, o, nsteps, sweeps, rho);
     } else {
         for (int n = 0; n < nsteps; ++n) {
-            st = run_step(c, o, sweeps ? &sweeps[n] : nullptr, rho ? &rho[n] : nullptr);
+            int64_t k = 0;
+            st = run_step(c, o, &k, rho ? &rho[n] : nullptr);
+            if (sweeps) sweeps[n] = k;
+            grow_ubound(c, (double)(k > 0 ? k : o->max_sweeps));
             if (st) break;
         }
     }
+    if (st == JAC_ENAN || st == JAC_EDEVICE) c->ubound = INFINITY;  // the field may hold anything
     if (c->prof_every > 0) {
         int s2 = drain_profile(c);
         if (!st) st = s2;
@@ -714,12 +775,17 @@ int jac_sweep(jac_t c, const jac_opts* o, int64_t nsweeps, float* rho) {
     c->step_serial += 1;
     c->cur_group = -1;
     c->cur_first = false;
+    c->fast_now = division_path(c, 1, (double)nsweeps);
     st = enqueue_rhs(c, o->tol);
     if (st) return st;
     int buf = c->cur;
     st = enqueue_sweeps(c, o, nsweeps, false, 0, &buf);
-    if (st) return st;
+    if (st) {
+        c->ubound = INFINITY;
+        return st;
+    }
     c->cur = buf;
+    grow_ubound(c, (double)nsweeps);
     if (rho) {
         c->mail->R[0] = kEmpty;
         st = enqueue_residual(c, o->tol, c->cur, 0);
@@ -748,9 +814,19 @@ int jac_get_field(jac_t c, float* host_out) {
 
 int jac_set_field(jac_t c, const float* host_in) {
     if (!c || !host_in) return fail(JAC_EINVAL, "NULL argument");
+    c->ubound = INFINITY;
+    double m = 100.0;  // the top ghost row
+    for (int64_t i = 0; i < (int64_t)c->N * c->N; ++i) {
+        const double v = std::fabs((double)host_in[i]);
+        if (!(v <= m)) {
+            if (!std::isfinite(v)) { m = INFINITY; break; }
+            m = v;
+        }
+    }
     JAC_HIP(hipMemcpy2DAsync(c->u[c->cur] + c->g.origin, (size_t)c->g.P * 4, host_in, (size_t)c->N * 4,
                              (size_t)c->N * 4, (size_t)c->N, hipMemcpyHostToDevice, c->stream));
     JAC_HIP(hipStreamSynchronize(c->stream));
+    c->ubound = m;
     return JAC_OK;
 }
 
@@ -761,6 +837,7 @@ int jac_reset(jac_t c) {
     JAC_HIP(launch_ghosts(c->u[1], c->g, c->stream));
     c->cur = 0;
     JAC_HIP(hipStreamSynchronize(c->stream));
+    c->ubound = 100.0;
     return JAC_OK;
 }
 
@@ -778,6 +855,11 @@ int jac_stream_probe(float* c, const float* a, const float* b, size_t n, int kin
 int jac_fast_division(jac_t c) {
     if (!c) return fail(JAC_EINVAL, "context is NULL");
     return c->fastdiv;
+}
+
+int jac_last_division(jac_t c) {
+    if (!c) return fail(JAC_EINVAL, "context is NULL");
+    return c->fast_now;
 }
 
 int jac_profile(jac_t c, int every) {
