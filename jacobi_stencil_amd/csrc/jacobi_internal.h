@@ -176,6 +176,32 @@ __device__ __forceinline__ void st4_nt(float* p, const float4& v) {
     __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p));
 }
 
+// Buffer accesses through a raw resource descriptor (stride 0).  The hardware
+// range-checks every lane's offset: a lane whose offset is kOOB loads zeros and
+// its stores are dropped.  A loop can then issue the same memory instructions
+// on every path -- lanes or rows that must not touch memory are masked by their
+// offset rather than by a branch -- so the wait before a loaded value is used
+// counts only the instructions issued after that load, not every store too.
+// In-range offsets (voffset + soffset) must stay below kOOB = 2 GiB.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kRawBufferWord3 = 0x00020000;  // 32-bit data format, the gfx9 raw-buffer setting
+constexpr int kAuxNT = 2;                    // nontemporal (streaming) cache policy
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)kOOB, kRawBufferWord3);
+}
+__device__ __forceinline__ float4 bld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void bst4_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const float4& v) {
+    const f32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), r, (int)voff, (int)soff, kAuxNT);
+}
+__device__ __forceinline__ void bst1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, (int)soff, 0);
+}
+
 // Blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous
 // range of logical tiles so that vertically adjacent tiles (which share halo
 // rows) sit behind the same L2.  nblocks must be a multiple of 8; logical ids

@@ -31,6 +31,8 @@
 // others skip that work.
 #include "jacobi_internal.h"
 
+#include <type_traits>
+
 namespace jac {
 
 struct TBLane {
@@ -81,17 +83,118 @@ __device__ __forceinline__ void impose_ring(float4& v, int i, int N, const TBLan
     }
 }
 
+// Row I/O of a wavefront's band, in one of two forms chosen by depth (both
+// measured at 8192^2; the choice changes no result).
+//
+// TBGlobalIO: flat loads and stores; lanes and rows that must not touch memory
+// skip them by a branch; nontemporal loads.  Fastest for the shallow depths,
+// which are bound by memory bandwidth.
+//
+// TBBufferIO: buffer loads and stores issued on every row; a lane outside the
+// grid, a column that is not stored or a row outside the band's output is
+// masked by an out-of-range offset.  The memory instructions in flight are then
+// the same on every path, so the wait for the prefetched row does not also wait
+// for the row just stored; loads go through the caches normally, so the halo
+// rows and columns that neighbouring bands re-read can hit in L2.  Fastest for
+// the deep depths, which are bound by the arithmetic.
+struct TBGlobalIO {
+    const float* pu;
+    const float* pb;
+    float* po;
+    int P;
+    bool lane_loads, store_lane;
+
+    __device__ __forceinline__ void init(const float* uin, const float* bin, float* uout, const StepArgs& a,
+                                         const TBLane& L, int X, bool loads, int j0, int y0) {
+        (void)X;
+        (void)j0;
+        (void)y0;
+        P = a.g.P;
+        pu = uin + a.g.origin + L.c0;
+        pb = bin + a.g.origin + L.c0;
+        po = uout + a.g.origin + L.c0;
+        lane_loads = loads;
+        store_lane = L.core[0];
+    }
+    // row j of u_k and b into (nu, nb); rows past j1 are not needed
+    __device__ __forceinline__ void load(float4& nu, float4& nb, int j, int j0, int j1) {
+        (void)j0;
+        if (lane_loads && j <= j1) {
+            nu = ld4_nt(pu + (int64_t)j * P);
+            nb = ld4_nt(pb + (int64_t)j * P);
+        }
+    }
+    template <bool EDGE>
+    __device__ __forceinline__ void store(const float4& out, int i, bool row_out, int y0, const TBLane& L) {
+        (void)y0;
+        if (row_out && store_lane) {
+            float* q = po + (int64_t)i * P;
+            if (L.core[3]) {
+                st4_nt(q, out);
+            } else {
+                q[0] = out.x;
+                if (L.core[1]) q[1] = out.y;
+                if (L.core[2]) q[2] = out.z;
+            }
+        }
+    }
+};
+
+struct TBBufferIO {
+    __amdgpu_buffer_rsrc_t ru, rb;  // u_k and b, from row j0 and window column X
+    __amdgpu_buffer_rsrc_t ro;      // output, from row y0 and window column X
+    uint32_t vload;                 // the lane's byte offset in a row; kOOB: lane wholly outside [0, N)
+    uint32_t vst4;                  // 16-byte store offset of a lane whose 4 columns are all stored
+    uint32_t vst1[4];               // dword store offsets of a partly stored lane's columns (EDGE)
+    uint32_t rowb;                  // row pitch in bytes
+
+    __device__ __forceinline__ void init(const float* uin, const float* bin, float* uout, const StepArgs& a,
+                                         const TBLane& L, int X, bool loads, int j0, int y0) {
+        const int P = a.g.P;
+        rowb = (uint32_t)P * 4u;
+        ru = make_rsrc(uin + a.g.origin + (int64_t)j0 * P + X);
+        rb = make_rsrc(bin + a.g.origin + (int64_t)j0 * P + X);
+        ro = make_rsrc(uout + a.g.origin + (int64_t)y0 * P + X);
+        const uint32_t lb = (uint32_t)(threadIdx.x & 63) * 16u;
+        vload = loads ? lb : kOOB;
+        const bool full = L.core[0] && L.core[1] && L.core[2] && L.core[3];
+        vst4 = full ? lb : kOOB;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vst1[c] = (!full && L.core[c]) ? lb + 4u * c : kOOB;
+    }
+    // row j of u_k and b into (nu, nb); row j1 + 1 lies inside the padded
+    // plane and is loaded and left unused
+    __device__ __forceinline__ void load(float4& nu, float4& nb, int j, int j0, int j1) {
+        (void)j1;
+        const uint32_t so = (uint32_t)(j - j0) * rowb;
+        nu = bld4(ru, vload, so);
+        nb = bld4(rb, vload, so);
+    }
+    template <bool EDGE>
+    __device__ __forceinline__ void store(const float4& out, int i, bool row_out, int y0, const TBLane& L) {
+        (void)L;
+        const uint32_t so = row_out ? (uint32_t)(i - y0) * rowb : 0u;
+        bst4_nt(ro, row_out ? vst4 : kOOB, so, out);
+        if (EDGE) {
+            bst1(ro, row_out ? vst1[0] : kOOB, so, out.x);
+            bst1(ro, row_out ? vst1[1] : kOOB, so, out.y);
+            bst1(ro, row_out ? vst1[2] : kOOB, so, out.z);
+            bst1(ro, row_out ? vst1[3] : kOOB, so, out.w);
+        }
+    }
+};
+
+template <int D>
+using TBIO = typename std::conditional<(D >= 5), TBBufferIO, TBGlobalIO>::type;
+
 // The streaming state of one wavefront: for every level t < D three row
 // registers whose roles rotate (up = row i-1, mid = row i, new = row i+1 of
 // that level, as seen by level t+1), the prefetched next row, the ring slot.
 template <int D, bool CHK, bool EDGE, bool FAST>
 struct TBStream {
-    const float* pu;
-    const float* pb;
-    float* po;
+    TBIO<D> io;
     float r, d, y;
-    int N, P, j0, j1, y0, last;
-    bool lane_loads, store_lane;
+    int N, j0, j1, y0, last;
     TBLane L;
     float4 (*ring)[64];
     float4 nu, nb;  // row j+1 of u_k and b, loaded one row ahead
@@ -105,10 +208,7 @@ struct TBStream {
         const int lane = threadIdx.x & 63;
         NEW[0] = nu;
         const float4 cb = nb;
-        if (lane_loads && j < j1) {  // fetch the next row while this one is worked on
-            nu = ld4_nt(pu + (int64_t)(j + 1) * P);
-            nb = ld4_nt(pb + (int64_t)(j + 1) * P);
-        }
+        io.load(nu, nb, j + 1, j0, j1);  // fetch the next row while this one is worked on
         ring[s][lane] = cb;
         float4 out;
         const int depth = j - j0;  // level t is exact from the (2t)-th row of the band on
@@ -133,27 +233,17 @@ struct TBStream {
             }
         }
         const int i = j - D;
-        if (i >= y0 && i <= last && store_lane) {
-            float* q = po + (int64_t)i * P;
-            if (L.core[3]) {
-                st4_nt(q, out);
-            } else {
-                q[0] = out.x;
-                if (L.core[1]) q[1] = out.y;
-                if (L.core[2]) q[2] = out.z;
-            }
-        }
+        io.template store<EDGE>(out, i, i >= y0 && i <= last, y0, L);
         s = (s + 1 == R) ? 0 : s + 1;
     }
 };
 
 template <int D, bool CHK, bool EDGE, bool FAST>
 __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const float* __restrict__ bin,
-                                            float* __restrict__ uout, const StepArgs& a, const TBLane& L,
+                                            float* __restrict__ uout, const StepArgs& a, const TBLane& L, int X,
                                             bool lane_loads, int y0, int last, float4 (*ring)[64]) {
     TBStream<D, CHK, EDGE, FAST> st;
     st.N = a.g.N;
-    st.P = a.g.P;
     st.r = a.r;
     st.d = a.d;
     st.y = a.y;
@@ -161,11 +251,7 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     st.j1 = last + D;
     st.y0 = y0;
     st.last = last;
-    st.pu = uin + a.g.origin + L.c0;
-    st.pb = bin + a.g.origin + L.c0;
-    st.po = uout + a.g.origin + L.c0;
-    st.lane_loads = lane_loads;
-    st.store_lane = L.core[0];
+    st.io.init(uin, bin, uout, a, L, X, lane_loads, st.j0, y0);
     st.L = L;
     st.ring = ring;
     st.s = 0;
@@ -173,10 +259,7 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     st.nu = zero;
     st.nb = zero;
-    if (lane_loads) {
-        st.nu = *reinterpret_cast<const float4*>(st.pu + (int64_t)st.j0 * st.P);
-        st.nb = *reinterpret_cast<const float4*>(st.pb + (int64_t)st.j0 * st.P);
-    }
+    st.io.load(st.nu, st.nb, st.j0, st.j0, st.j1);
     float4 A[D], B[D], C[D];
 #pragma unroll
     for (int t = 0; t < D; ++t) { A[t] = zero; B[t] = zero; C[t] = zero; }
@@ -230,9 +313,9 @@ void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
         const bool lane_loads = L.c0 < N && L.c0 + 4 > 0;
         const bool edge = X < 0 || X + 256 > N || y0 - D < 0 || last + D >= N;
         if (edge)
-            m = tb_band<D, CHK, true, FAST>(uin, bin, uout, a, L, lane_loads, y0, last, ring);
+            m = tb_band<D, CHK, true, FAST>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
         else
-            m = tb_band<D, CHK, false, FAST>(uin, bin, uout, a, L, lane_loads, y0, last, ring);
+            m = tb_band<D, CHK, false, FAST>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
     }
     if (CHK) store_block_max<1>(m, a.sc, blockIdx.x);
 }
