@@ -25,6 +25,8 @@ _LIB = os.path.join(_HERE, "libjacobi_oracle.so")
 
 SYNC = 0
 ASYNC = 2
+# depth controllers for ASYNC (page "stencil-jacobian.vercel.app", section 02)
+STATIC, G_ASC, G_DESC, SCHED = 0, 1, 2, 3
 OK, EINVAL, ENOMEM, ENOCONV, ENAN = 0, -1, -2, -4, -5
 
 # -ffp-contract=off: GCC fuses a*b+c by default for GNU dialects; the pages fix
@@ -67,13 +69,20 @@ def _load():
         lib.orc_residual.argtypes = [ctypes.c_int, ctypes.c_float, f32p, f32p]
         lib.orc_residual.restype = ctypes.c_float
         lib.orc_async_launch.argtypes = [ctypes.c_int, ctypes.c_float, f32p, f32p, f32p,
-                                         ctypes.c_int, ctypes.c_int, ctypes.c_int]
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.orc_solve.argtypes = [ctypes.c_int, ctypes.c_float, f32p, f32p, ctypes.c_int,
                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int64, i64p, f32p,
                                   ctypes.c_void_p, ctypes.c_int64,
                                   ctypes.POINTER(ctypes.c_int64)]
         lib.orc_solve.restype = ctypes.c_int
+        lib.orc_solve_ex.argtypes = [ctypes.c_int, ctypes.c_float, f32p, f32p, ctypes.c_int,
+                                     ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_int64, i64p, f32p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.POINTER(ctypes.c_int64)]
+        lib.orc_solve_ex.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -126,23 +135,26 @@ def residual(u, b, r) -> np.float32:
     return np.float32(_load().orc_residual(N, np.float32(r), _grid(u, N), _grid(b, N)))
 
 
-def async_launch(u, b, r, tx, ty, D):
-    """One block-asynchronous launch: tiles tx x ty, frozen one-cell halo, D sweeps."""
+def async_launch(u, b, r, tx, ty, D, o=0):
+    """One block-asynchronous launch: tiles tx x ty, each worked on widened by o
+    overlap cells per side, frozen one-cell halo around that, D sweeps; each
+    tile writes back only its own points."""
     N = np.asarray(u).shape[0]
     out = np.empty((N, N), np.float32)
-    _load().orc_async_launch(N, np.float32(r), _grid(u, N), _grid(b, N), out, int(tx), int(ty), int(D))
+    _load().orc_async_launch(N, np.float32(r), _grid(u, N), _grid(b, N), out, int(tx), int(ty), int(D), int(o))
     return out
 
 
 class Result:
     """Outcome of ``solve``: final field, per-step sweeps and rho, every check's R."""
 
-    def __init__(self, u, sweeps, rho, status, R_log):
+    def __init__(self, u, sweeps, rho, status, R_log, D_log=None):
         self.u = u
         self.sweeps = sweeps
         self.rho = rho
         self.status = status
         self.R_log = R_log
+        self.D_log = D_log  # depth of every check interval (solve with log_cap > 0)
 
     @property
     def total_sweeps(self) -> int:
@@ -150,18 +162,31 @@ class Result:
 
 
 def solve(N, r, s, u0=None, steps=10, tol=1e-5, M=8, mode=SYNC, D=1, tx=32, ty=8,
-          max_sweeps=10**6, log_cap=0) -> Result:
-    """``steps`` backward-Euler steps, each Jacobi-iterated until rho < tol (checked every M)."""
+          max_sweeps=10**6, log_cap=0, o=0, controller=STATIC, schedule=None) -> Result:
+    """``steps`` backward-Euler steps, each Jacobi-iterated until rho < tol (checked every M).
+
+    ASYNC options: tiles tx x ty widened by ``o`` overlap cells; ``controller``
+    picks each interval's depth (STATIC: D; G_ASC / G_DESC: from the previous
+    check's rho, at most D; SCHED: ``schedule[i]`` for the i-th interval)."""
     lib = _load()
     s = _grid(s, N)
     u = np.zeros((N, N), np.float32) if u0 is None else _grid(u0, N).copy()
     sweeps = np.zeros(max(steps, 1), np.int64)
     rho = np.zeros(max(steps, 1), np.float32)
     log = np.zeros(max(log_cap, 1), np.float32)
+    dlog = np.zeros(max(log_cap, 1), np.int32)
     nlog = ctypes.c_int64(0)
-    status = lib.orc_solve(int(N), np.float32(r), s, u, int(steps), np.float32(tol), int(M),
-                           int(mode), int(D), int(tx), int(ty), int(max_sweeps), sweeps, rho,
-                           log.ctypes.data if log_cap > 0 else None, int(log_cap),
-                           ctypes.byref(nlog))
+    sched = None
+    nsched = 0
+    if schedule is not None:
+        sched = np.ascontiguousarray(schedule, dtype=np.int32)
+        nsched = len(sched)
+    status = lib.orc_solve_ex(int(N), np.float32(r), s, u, int(steps), np.float32(tol), int(M),
+                              int(mode), int(D), int(tx), int(ty), int(o), int(controller),
+                              sched.ctypes.data if sched is not None else None, int(nsched),
+                              int(max_sweeps), sweeps, rho,
+                              log.ctypes.data if log_cap > 0 else None,
+                              dlog.ctypes.data if log_cap > 0 else None, int(log_cap),
+                              ctypes.byref(nlog))
     n = min(int(nlog.value), log_cap)
-    return Result(u, sweeps[:steps], rho[:steps], int(status), log[:n].copy())
+    return Result(u, sweeps[:steps], rho[:steps], int(status), log[:n].copy(), dlog[:n].copy())

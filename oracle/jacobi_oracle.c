@@ -163,28 +163,36 @@ static float residual_padded(int N, float r, const float* U, const float* B) {
 /*
  * One block-asynchronous launch.  Tiles of tx columns by ty rows start at the
  * top-left unknown; the last tile in each direction may be partial.  Each tile
- * copies its points and the one-cell ring around them from U (that ring is a
- * neighbour tile's values or the ghost ring, and stays frozen), performs D
- * Jacobi sweeps on its own points only, each sweep reading the tile's previous
- * sweep, and writes its points to V.
+ * owns its points.  It works on its points widened by o cells on each side
+ * (clipped to the grid): the overlapping subdomains of Islam & Wang,
+ * "Hierarchical Jacobi Iteration ... using Shared Memory", section 3.5 (1-D)
+ * and the 2-D extension in section 4; o = 0 is the plain block-async launch of
+ * page "stencil-jacobian.vercel.app", section 02.  It copies that region and
+ * the one-cell ring around it from U (the ring holds neighbouring tiles'
+ * values or the ghost ring, and stays frozen), performs D Jacobi sweeps on the
+ * region, each sweep reading the region's previous sweep, and writes only its
+ * own points to V; the values computed in the overlap are dropped.
  */
 static void async_launch_padded(int N, float r, float d, const float* U, const float* B, float* V,
-                                int tx, int ty, int D) {
+                                int tx, int ty, int D, int o) {
     int ntx = (N + tx - 1) / tx, nty = (N + ty - 1) / ty;
     #pragma omp parallel for schedule(dynamic)
     for (int t = 0; t < ntx * nty; ++t) {
         int x0 = (t % ntx) * tx, y0 = (t / ntx) * ty;
-        int w = (x0 + tx <= N) ? tx : N - x0;
-        int h = (y0 + ty <= N) ? ty : N - y0;
+        int x1 = (x0 + tx <= N) ? x0 + tx : N;   /* owned columns [x0, x1) */
+        int y1 = (y0 + ty <= N) ? y0 + ty : N;   /* owned rows [y0, y1) */
+        int ex0 = x0 - o < 0 ? 0 : x0 - o, ex1 = x1 + o > N ? N : x1 + o;
+        int ey0 = y0 - o < 0 ? 0 : y0 - o, ey1 = y1 + o > N ? N : y1 + o;
+        int w = ex1 - ex0, h = ey1 - ey0;          /* the region worked on */
         size_t lp = (size_t)w + 2;
         size_t ln = lp * ((size_t)h + 2);
         float* cur = (float*)malloc(ln * sizeof(float));
         float* nxt = (float*)malloc(ln * sizeof(float));
         float* bl = (float*)malloc(ln * sizeof(float));
-        /* local (a, c) with a = 0..h+1, c = 0..w+1 is unknown (y0+a-1, x0+c-1) */
+        /* local (a, c) with a = 0..h+1, c = 0..w+1 is unknown (ey0+a-1, ex0+c-1) */
         for (int a = 0; a < h + 2; ++a)
             for (int c = 0; c < w + 2; ++c) {
-                size_t g = at(N, y0 + a - 1, x0 + c - 1);
+                size_t g = at(N, ey0 + a - 1, ex0 + c - 1);
                 cur[(size_t)a * lp + c] = U[g];
                 bl[(size_t)a * lp + c] = B[g];
             }
@@ -197,8 +205,9 @@ static void async_launch_padded(int N, float r, float d, const float* U, const f
                 }
             float* tmp = cur; cur = nxt; nxt = tmp;
         }
-        for (int a = 1; a <= h; ++a)
-            for (int c = 1; c <= w; ++c) V[at(N, y0 + a - 1, x0 + c - 1)] = cur[(size_t)a * lp + c];
+        for (int i = y0; i < y1; ++i)
+            for (int j = x0; j < x1; ++j)
+                V[at(N, i, j)] = cur[(size_t)(i - ey0 + 1) * lp + (size_t)(j - ex0 + 1)];
         free(cur); free(nxt); free(bl);
     }
 }
@@ -261,13 +270,13 @@ float orc_residual(int N, float r, const float* u, const float* b) {
     return m;
 }
 
-void orc_async_launch(int N, float r, const float* u, const float* b, float* out, int tx, int ty, int D) {
+void orc_async_launch(int N, float r, const float* u, const float* b, float* out, int tx, int ty, int D, int o) {
     float* U = alloc_padded(N);
     float* B = alloc_padded(N);
     float* V = alloc_padded(N);
     load_interior(N, U, u);
     load_interior(N, B, b);
-    async_launch_padded(N, r, diag_of(r), U, B, V, tx, ty, D);
+    async_launch_padded(N, r, diag_of(r), U, B, V, tx, ty, D, o);
     store_interior(N, V, out);
     free(U); free(B); free(V);
 }
@@ -275,23 +284,57 @@ void orc_async_launch(int N, float r, const float* u, const float* b, float* out
 /* ---- the time-step loop -------------------------------------------------- */
 
 /*
+ * Depth chosen by the threshold controllers of page "stencil-jacobian.vercel.
+ * app", section 02 (block-async, "G-asc and G-desc"): the depth steps as rho
+ * crosses 1e-2, 1e-3 and 1e-4.  Reading of the page: G-asc starts each time
+ * step at D = 1 and moves through 1, 2, 4, 8 as rho falls below each
+ * threshold; G-desc starts at 8 and moves through 8, 4, 2, 1.  Both are capped
+ * to [1, Dmax] and latched: within a time step the depth never moves back.
+ * rho is compared with the thresholds as binary32 values.
+ */
+static int asc_level(float q) {
+    if (q >= 1e-2f) return 1;
+    if (q >= 1e-3f) return 2;
+    if (q >= 1e-4f) return 4;
+    return 8;
+}
+static int desc_level(float q) {
+    if (q >= 1e-2f) return 8;
+    if (q >= 1e-3f) return 4;
+    if (q >= 1e-4f) return 2;
+    return 1;
+}
+static int clamp_depth(int v, int Dmax) { return v < 1 ? 1 : (v > Dmax ? Dmax : v); }
+
+/*
  * Ten (or `steps`) backward-Euler steps, each iterated to rho < tol.
  *   u_io:    in: u^0 (N x N); out: the last field.
  *   mode:    ORC_SYNC  - point Jacobi, a check after every M sweeps;
- *            ORC_ASYNC - block-async launches of min(D, left) sweeps; the check
- *                        interval is M, or D when D > M.
+ *            ORC_ASYNC - block-async launches of min(D, left) sweeps, tiles
+ *                        tx x ty widened by o overlap cells; the check
+ *                        interval is M, or Dmax when Dmax > M.
+ *   ctrl:    (ORC_ASYNC) how the depth D of each check interval is chosen:
+ *            ORC_STATIC D = Dmax throughout; ORC_G_ASC / ORC_G_DESC from the
+ *            rho of the previous check (see asc_level / desc_level); ORC_SCHED
+ *            the i-th interval of the whole solve uses sched[i] (an interval
+ *            beyond sched_n is an error).
  *   sweeps, rho: per-step sweep count and the rho of the accepted iterate.
  *   R_log:   optional; R of every check in order (at most log_cap entries);
  *            *log_n receives the number of checks made.
+ *   d_log:   optional; the depth of every interval (at most log_cap entries).
  * Returns ORC_OK, ORC_ENOCONV (a failed check at or beyond max_sweeps: the
  * field is that checked iterate) or ORC_ENAN (rho is NaN: the field is that
  * iterate).  Steps after a failure are not run; their entries are 0 / NaN.
  */
-int orc_solve(int N, float r, const float* s, float* u_io, int steps, float tol, int M, int mode,
-              int D, int tx, int ty, int64_t max_sweeps, int64_t* sweeps, float* rho,
-              float* R_log, int64_t log_cap, int64_t* log_n) {
-    if (N < 1 || steps < 0 || M < 1 || D < 1 || tx < 1 || ty < 1 || max_sweeps < 1) return ORC_EINVAL;
+int orc_solve_ex(int N, float r, const float* s, float* u_io, int steps, float tol, int M, int mode,
+                 int Dmax, int tx, int ty, int o, int ctrl, const int* sched, int64_t sched_n,
+                 int64_t max_sweeps, int64_t* sweeps, float* rho,
+                 float* R_log, int* d_log, int64_t log_cap, int64_t* log_n) {
+    if (N < 1 || steps < 0 || M < 1 || Dmax < 1 || tx < 1 || ty < 1 || o < 0 || max_sweeps < 1)
+        return ORC_EINVAL;
     if (mode != ORC_SYNC && mode != ORC_ASYNC) return ORC_EINVAL;
+    if (ctrl < ORC_STATIC || ctrl > ORC_SCHED || (ctrl == ORC_SCHED && !sched)) return ORC_EINVAL;
+    if (mode == ORC_SYNC && ctrl != ORC_STATIC) return ORC_EINVAL;
     float d = diag_of(r);
     float* U0 = alloc_padded(N);
     float* U1 = alloc_padded(N);
@@ -301,7 +344,7 @@ int orc_solve(int N, float r, const float* s, float* u_io, int steps, float tol,
     for (int n = 0; n < steps; ++n) { sweeps[n] = 0; rho[n] = NAN; }
     int64_t nlog = 0;
     int status = ORC_OK;
-    int interval = (mode == ORC_ASYNC && D > M) ? D : M;
+    int interval = (mode == ORC_ASYNC && Dmax > M) ? Dmax : M;
     float* cur = U0;
     float* nxt = U1;
     for (int n = 0; n < steps && status == ORC_OK; ++n) {
@@ -309,7 +352,15 @@ int orc_solve(int N, float r, const float* s, float* u_io, int steps, float tol,
         rhs_padded(N, cur, s, B);
         float bA = rhs_norm_padded(N, r, B);
         int64_t k = 0;
+        int D = Dmax;
+        if (ctrl == ORC_G_ASC) D = 1;
         for (;;) {
+            if (ctrl == ORC_SCHED) {
+                if (nlog >= sched_n) { status = ORC_EINVAL; break; }
+                D = sched[nlog];
+                if (D < 1) { status = ORC_EINVAL; break; }
+            }
+            if (d_log && nlog < log_cap) d_log[nlog] = D;
             int left = interval;
             while (left > 0) {
                 if (mode == ORC_SYNC) {
@@ -317,7 +368,7 @@ int orc_solve(int N, float r, const float* s, float* u_io, int steps, float tol,
                     left -= 1;
                 } else {
                     int m = D < left ? D : left;
-                    async_launch_padded(N, r, d, cur, B, nxt, tx, ty, m);
+                    async_launch_padded(N, r, d, cur, B, nxt, tx, ty, m, o);
                     left -= m;
                 }
                 float* tmp = cur; cur = nxt; nxt = tmp;
@@ -332,10 +383,24 @@ int orc_solve(int N, float r, const float* s, float* u_io, int steps, float tol,
             if (q < tol) break;
             if (isnan(q)) { status = ORC_ENAN; break; }
             if (k >= max_sweeps) { status = ORC_ENOCONV; break; }
+            if (ctrl == ORC_G_ASC) {
+                int t = clamp_depth(asc_level(q), Dmax);
+                if (t > D) D = t;
+            } else if (ctrl == ORC_G_DESC) {
+                int t = clamp_depth(desc_level(q) * Dmax / 8, Dmax);
+                if (t < D) D = t;
+            }
         }
     }
     store_interior(N, cur, u_io);
     if (log_n) *log_n = nlog;
     free(U0); free(U1); free(B);
     return status;
+}
+
+int orc_solve(int N, float r, const float* s, float* u_io, int steps, float tol, int M, int mode,
+              int D, int tx, int ty, int64_t max_sweeps, int64_t* sweeps, float* rho,
+              float* R_log, int64_t log_cap, int64_t* log_n) {
+    return orc_solve_ex(N, r, s, u_io, steps, tol, M, mode, D, tx, ty, 0, ORC_STATIC, NULL, 0, max_sweeps,
+                        sweeps, rho, R_log, NULL, log_cap, log_n);
 }

@@ -73,12 +73,13 @@ def dst_solve(b, r):
     return fft.idstn(bh / lam, type=1, norm="ortho")
 
 
-def block_async_launch(u, b, r, tx, ty, D):
+def block_async_launch(u, b, r, tx, ty, D, o=0):
     """One block-asynchronous launch in float64, written as per-tile Jacobi on a local system.
 
-    For each tile T: x <- (b_T + r*(Adj_TT x + c_T)) / (1+4r), D times, x0 = u_T,
-    where c_T collects the frozen neighbours outside T (other tiles' values of u,
-    or the boundary data).
+    For each tile T, let E be T widened by o cells per side (clipped to the
+    grid): x <- (b_E + r*(Adj_EE x + c_E)) / (1+4r), D times, x0 = u_E, where
+    c_E collects the frozen neighbours outside E (other tiles' values of u, or
+    the boundary data); only T's points are written back.
     """
     u = np.asarray(u, np.float64)
     bA = boundary_rhs(b, r)
@@ -87,8 +88,9 @@ def block_async_launch(u, b, r, tx, ty, D):
     out = np.empty_like(u)
     for y0 in range(0, N, ty):
         for x0 in range(0, N, tx):
-            ys = range(y0, min(y0 + ty, N))
-            xs = range(x0, min(x0 + tx, N))
+            own = [(i, j) for i in range(y0, min(y0 + ty, N)) for j in range(x0, min(x0 + tx, N))]
+            ys = range(max(y0 - o, 0), min(y0 + ty + o, N))
+            xs = range(max(x0 - o, 0), min(x0 + tx + o, N))
             pts = [(i, j) for i in ys for j in xs]
             index = {p: k for k, p in enumerate(pts)}
             n = len(pts)
@@ -105,6 +107,6 @@ def block_async_launch(u, b, r, tx, ty, D):
             x = np.array([u[p] for p in pts])
             for _ in range(D):
                 x = (rhs + r * (adj @ x)) / (1.0 + 4.0 * r)
-            for k, p in enumerate(pts):
-                out[p] = x[k]
+            for p in own:
+                out[p] = x[index[p]]
     return out

@@ -265,6 +265,128 @@ def test_async_launch_matches_block_jacobi(orc, N, tx, ty, D):
     assert np.max(np.abs(got - want)) <= 1e-5 * 100.0
 
 
+@pytest.mark.parametrize("N,tx,ty,D,o", [(9, 4, 3, 3, 1), (10, 4, 4, 4, 2), (7, 3, 5, 2, 1)])
+def test_overlap_launch_matches_block_jacobi(orc, N, tx, ty, D, o):
+    """Islam & Wang, sections 3.5 and 4: each tile iterates on itself widened by
+    o overlap cells (frozen halo outside that) and keeps only its own points."""
+    u = workloads.random_field(N, 53)
+    b = workloads.random_field(N, 54)
+    got = orc.async_launch(u, b, 10.0, tx, ty, D, o).astype(np.float64)
+    want = mf.block_async_launch(u, b, 10.0, tx, ty, D, o)
+    assert np.max(np.abs(got - want)) <= 1e-5 * 100.0
+    # the overlap matters: without it the launch is a different map
+    plain = orc.async_launch(u, b, 10.0, tx, ty, D, 0)
+    assert not np.array_equal(plain, orc.async_launch(u, b, 10.0, tx, ty, D, o))
+
+
+@pytest.mark.parametrize("D,o", [(1, 0), (3, 2), (4, 6), (5, 4)])
+def test_overlap_at_least_depth_is_sync(orc, D, o):
+    """The frozen ring first differs from the synchronous iterate after sweep 1
+    and the difference moves one cell per sweep, so after D sweeps it has
+    reached D - 1 cells into the widened region.  With o >= D - 1 no stale
+    value reaches a tile's own points: the launch equals D synchronous sweeps
+    bit for bit (the limit where overlapping subdomains become exact temporal
+    blocking; o = 0, D = 1 is the page's D = 1 case).  One cell less is not."""
+    N = 29
+    u = workloads.random_field(N, 61)
+    b = workloads.random_field(N, 62)
+    want = u
+    for _ in range(D):
+        want = orc.sweep(want, b, 10.0)
+    assert np.array_equal(orc.async_launch(u, b, 10.0, 8, 4, D, o), want)
+    if o == D - 1 and D > 1:
+        assert not np.array_equal(orc.async_launch(u, b, 10.0, 8, 4, D, o - 1), want)
+
+
+def test_overlap_solve_between_async_and_sync(orc):
+    """More overlap, fewer extra sweeps: sync <= overlap 2 <= overlap 0 (D = 8)."""
+    N, r = 256, 10.0
+    s = workloads.gaussian_source(N, r)
+    sync = orc.solve(N, r, s, steps=3).total_sweeps
+    o0 = orc.solve(N, r, s, steps=3, mode=orc.ASYNC, D=8, tx=32, ty=16)
+    o2 = orc.solve(N, r, s, steps=3, mode=orc.ASYNC, D=8, tx=32, ty=16, o=2)
+    o7 = orc.solve(N, r, s, steps=3, mode=orc.ASYNC, D=8, tx=32, ty=16, o=7)
+    assert o0.status == o2.status == o7.status == orc.OK
+    assert sync <= o2.total_sweeps <= o0.total_sweeps
+    assert o7.total_sweeps == sync
+
+
+# ------------------------------------------------- depth controllers (ASYNC)
+
+def test_static_schedule_equals_static_depth(orc):
+    N, r = 70, 10.0
+    s = workloads.gaussian_source(N, r)
+    a = orc.solve(N, r, s, steps=2, mode=orc.ASYNC, D=4, tx=32, ty=8, log_cap=4096)
+    b = orc.solve(N, r, s, steps=2, mode=orc.ASYNC, D=4, tx=32, ty=8, controller=orc.SCHED,
+                  schedule=[4] * len(a.R_log), log_cap=4096)
+    assert np.array_equal(a.u, b.u) and a.sweeps.tolist() == b.sweeps.tolist()
+    assert a.D_log.tolist() == [4] * len(a.R_log)
+
+
+@pytest.mark.parametrize("ctrl", ["asc", "desc"])
+def test_controllers_latched_and_monotone(orc, ctrl):
+    """Section 02: G-asc and G-desc step D as rho crosses 1e-2, 1e-3, 1e-4 and
+    latch (no oscillation).  Per step the depth starts at 1 (asc) or 8 (desc),
+    moves one way only, takes values in {1, 2, 4, 8}, and reaches the far end
+    once rho is below 1e-4; a replay of the logged depths gives the same solve."""
+    # r = 100: the residual bumps after a depth change cross the thresholds
+    # upwards, which an unlatched controller would follow back
+    N, r = 64, 100.0
+    s = workloads.gaussian_source(N, r)
+    c = orc.G_ASC if ctrl == "asc" else orc.G_DESC
+    res = orc.solve(N, r, s, steps=2, mode=orc.ASYNC, D=8, tx=32, ty=8, controller=c, log_cap=4096)
+    assert res.status == orc.OK
+    per = np.cumsum(res.sweeps // 8)
+    starts = np.concatenate([[0], per[:-1]])
+    for a, e in zip(starts, per):
+        seq = res.D_log[a:e].tolist()
+        assert set(seq) <= {1, 2, 4, 8}
+        assert seq[0] == (1 if ctrl == "asc" else 8)
+        assert seq == sorted(seq, reverse=(ctrl == "desc"))
+        # the checks before the last interval of the step: rho fell below 1e-4
+        # before 1e-5, so the last intervals use the far end
+        assert seq[-1] == (8 if ctrl == "asc" else 1)
+    rep = orc.solve(N, r, s, steps=2, mode=orc.ASYNC, D=8, tx=32, ty=8, controller=orc.SCHED,
+                    schedule=res.D_log, log_cap=4096)
+    assert np.array_equal(rep.u, res.u) and rep.sweeps.tolist() == res.sweeps.tolist()
+
+
+@pytest.mark.parametrize("ctrl", ["asc", "desc"])
+def test_controller_switch_points(orc, ctrl):
+    """The depth changes exactly after the first check whose rho is below each
+    of the page's thresholds 1e-2, 1e-3, 1e-4 (first time step, where
+    bA = ||b_A|| of u^0 = 0 is known in closed form)."""
+    N, r = 64, 10.0
+    s = workloads.gaussian_source(N, r)
+    c = orc.G_ASC if ctrl == "asc" else orc.G_DESC
+    res = orc.solve(N, r, s, steps=1, mode=orc.ASYNC, D=8, tx=32, ty=8, controller=c, log_cap=4096)
+    bA = orc.rhs_norm(orc.rhs(np.zeros((N, N), np.float32), s), r)
+    rho = (res.R_log / bA).astype(np.float32)
+    changes = [i for i in range(1, len(res.D_log)) if res.D_log[i] != res.D_log[i - 1]]
+    firsts = []
+    for th in (1e-2, 1e-3, 1e-4):
+        below = np.nonzero(rho < np.float32(th))[0]
+        if len(below) and below[0] + 1 < len(res.D_log):
+            firsts.append(int(below[0]) + 1)
+    assert changes == sorted(set(firsts)), (changes, firsts)
+
+
+def test_controller_reduces_to_sync(orc):
+    """With a loose tolerance (1e-2) every step stops before rho crosses 1e-2,
+    so G-asc never leaves D = 1 -- the synchronous iterates exactly; and G-desc
+    capped at Dmax = 1 is D = 1 throughout."""
+    N, r = 70, 10.0
+    s = workloads.gaussian_source(N, r)
+    sync = orc.solve(N, r, s, steps=3, tol=1e-2)
+    asc = orc.solve(N, r, s, steps=3, tol=1e-2, mode=orc.ASYNC, D=8, tx=32, ty=8, controller=orc.G_ASC,
+                    log_cap=4096)
+    assert set(asc.D_log.tolist()) == {1}
+    assert np.array_equal(asc.u, sync.u) and asc.sweeps.tolist() == sync.sweeps.tolist()
+    sync5 = orc.solve(N, r, s, steps=3)
+    desc1 = orc.solve(N, r, s, steps=3, mode=orc.ASYNC, D=1, tx=32, ty=8, controller=orc.G_DESC)
+    assert np.array_equal(desc1.u, sync5.u) and desc1.sweeps.tolist() == sync5.sweeps.tolist()
+
+
 def test_async_sweep_ratio_near_page(orc):
     """Section 05: D8 at 32x16 tiles needs about 1.738x the sync sweeps at r = 10;
     section 04: D4 needs 1.35-1.59x."""

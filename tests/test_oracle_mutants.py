@@ -32,6 +32,14 @@ MUTANTS = {
                                    "cur[l] = jacobi_point(cur, l, lp, bl[l], r, d); nxt[l] = cur[l];"),
     "async_halo_from_rhs": ("cur[(size_t)a * lp + c] = U[g];",
                             "cur[(size_t)a * lp + c] = (a == 0 || c == 0 || a == h + 1 || c == w + 1) ? B[g] : U[g];"),
+    "overlap_one_sided": ("int ex0 = x0 - o < 0 ? 0 : x0 - o, ex1 = x1 + o > N ? N : x1 + o;",
+                          "int ex0 = x0, ex1 = x1 + o > N ? N : x1 + o;"),
+    "overlap_writes_widened_region": ("V[at(N, i, j)] = cur[(size_t)(i - ey0 + 1) * lp + (size_t)(j - ex0 + 1)];",
+                                      "{ V[at(N, i, j)] = cur[(size_t)(i - ey0 + 1) * lp + (size_t)(j - ex0 + 1)];"
+                                      " if (i == y0 && y0 > ey0) V[at(N, i - 1, j)] = cur[(size_t)(i - ey0) * lp + "
+                                      "(size_t)(j - ex0 + 1)]; }"),
+    "asc_not_latched": ("if (t > D) D = t;", "D = t;"),
+    "desc_thresholds_shifted": ("if (q >= 1e-2f) return 8;", "if (q >= 1e-1f) return 8;"),
 }
 
 
