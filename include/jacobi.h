@@ -56,7 +56,36 @@ enum jac_status {
 enum jac_kernel {
     JAC_SYNC = 0,    /* (a) one synchronous sweep per launch */
     JAC_TBLOCK = 1,  /* (b) exact temporal blocking: D sweeps per launch, bitwise equal to (a) */
-    JAC_ASYNC = 2    /* (c) block-asynchronous: tile_x x tile_y tiles, frozen halo, D sweeps */
+    JAC_ASYNC = 2,   /* (c) block-asynchronous: tile_x x tile_y tiles, frozen halo, D sweeps */
+    JAC_SYNC_UNFUSED = 3  /* (a) without the fused right-hand side: each sweep reads u_k, u^n and s and
+                             forms b = u^n + s per point (16 bytes per point per sweep instead of 12) --
+                             the unfused baseline of page "stencil-jacobian.vercel.app", section 02 and
+                             section 05 (Table VI); results identical to JAC_SYNC; LAUNCH and GRAPH only */
+};
+
+/* How a check's result reaches the decision (LAUNCH and GRAPH drivers; the
+ * page's section 04, Table V: B = blocking, O = overlapped). */
+enum jac_checks {
+    JAC_CHECKS_OVERLAPPED = 0,  /* the residual of u_{gL} is fused into the first launch of the next
+                                   interval, which is queued before the host reads check g; a launch
+                                   that follows a stopping check returns at once */
+    JAC_CHECKS_BLOCKING = 1     /* after each interval a standalone residual kernel, then the host waits
+                                   for R and decides before anything more is queued */
+};
+
+/* Depth controllers for ASYNC (page "stencil-jacobian.vercel.app", section 02:
+ * D is a launch argument and may change between launches).  They need the
+ * LAUNCH driver; they imply JAC_CHECKS_BLOCKING.  The depths are powers of two
+ * up to opts.D; each time step starts afresh. */
+enum jac_controller {
+    JAC_STATIC = 0,  /* D = opts.D throughout */
+    JAC_G_ASC = 1,   /* start at 1; D steps up through 1, 2, 4, 8 as rho falls below 1e-2, 1e-3, 1e-4;
+                        latched (never steps back within a time step) */
+    JAC_G_DESC = 2,  /* start at 8; D steps down through 8, 4, 2, 1 at the same thresholds; latched */
+    JAC_G_FB = 3     /* hill climbing on the measured convergence rate -ln(rho_g / rho_{g-1}) per ms:
+                        start at 1; after each check (except the one right after a change, the
+                        settling window) double D while the rate holds, halve it when the rate drops
+                        by more than 10% against the previous measurement */
 };
 
 /* How the launches of a step are issued. */
@@ -78,9 +107,17 @@ typedef struct {
     float tol;           /* rho threshold (> 0) */
     int32_t band_rows;   /* TBLOCK: rows per wavefront band (LAUNCH), tile side (PERSISTENT); 0: automatic */
     int64_t max_sweeps;  /* per step; a failed check at or past it ends with JAC_ENOCONV */
+    int32_t checks;      /* jac_checks */
+    int32_t controller;  /* jac_controller (ASYNC only) */
+    int32_t overlap;     /* ASYNC: each tile iterates on itself widened by this many cells per side and
+                            writes back only its own points -- overlapping subdomains (Islam & Wang,
+                            "Hierarchical Jacobi Iteration ...", sections 3.5 and 4); 0..64 with
+                            (tile_x + 2 overlap) * (tile_y + 2 overlap) <= 4096; LAUNCH and GRAPH only */
+    int32_t reserved;    /* 0 */
 } jac_opts;
 
-/* SYNC, LAUNCH, D = 1, 32 x 8 tiles, M = 8, tol = 1e-5, band_rows = 0, max_sweeps = 1e6. */
+/* SYNC, LAUNCH, D = 1, 32 x 8 tiles, M = 8, tol = 1e-5, band_rows = 0, max_sweeps = 1e6,
+ * overlapped checks, static depth, no overlap. */
 void jac_opts_default(jac_opts* opts);
 
 /* Bytes of device workspace a context of size N needs (u twice, b, dt*f,
@@ -143,6 +180,14 @@ int jac_fast_division(jac_t ctx);
 /* Division path the most recent step, sweep or persistent solve took: 1 the
  * fast path, 0 IEEE division (also before any work), < 0 on error. */
 int jac_last_division(jac_t ctx);
+
+/*
+ * Depth of every check interval of the most recent jac_step / jac_solve call
+ * (LAUNCH and GRAPH drivers; for SYNC the depth is 1), in order across its
+ * steps: depths[i] for i < min(*count, cap); *count receives the number of
+ * intervals.  With a depth controller this is the schedule it chose.
+ */
+int jac_depth_log(jac_t ctx, int32_t* depths, int64_t cap, int64_t* count);
 
 /* Release the context (not the workspace).  NULL is accepted. */
 int jac_destroy(jac_t ctx);

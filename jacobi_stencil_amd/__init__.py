@@ -20,23 +20,27 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libjacobi.so")
 
 JAC_OK, JAC_EINVAL, JAC_ENOMEM, JAC_EDEVICE, JAC_ENOCONV, JAC_ENAN = 0, -1, -2, -3, -4, -5
-JAC_SYNC, JAC_TBLOCK, JAC_ASYNC = 0, 1, 2
+JAC_SYNC, JAC_TBLOCK, JAC_ASYNC, JAC_SYNC_UNFUSED = 0, 1, 2, 3
 JAC_LAUNCH, JAC_GRAPH, JAC_PERSISTENT = 0, 1, 2
+JAC_CHECKS_OVERLAPPED, JAC_CHECKS_BLOCKING = 0, 1
+JAC_STATIC, JAC_G_ASC, JAC_G_DESC, JAC_G_FB = 0, 1, 2, 3
 KCLASS = {"rhs": 0, "sync": 1, "sync_check": 2, "tblock": 3, "async": 4, "residual": 5, "persistent": 6,
           "noop": 7, "reduce": 8}
 STATUS_NAMES = {0: "JAC_OK", -1: "JAC_EINVAL", -2: "JAC_ENOMEM", -3: "JAC_EDEVICE", -4: "JAC_ENOCONV",
                 -5: "JAC_ENAN"}
 
 EXPORTS = ("jac_opts_default", "jac_workspace_bytes", "jac_create", "jac_step", "jac_solve", "jac_sweep",
-           "jac_get_field", "jac_set_field", "jac_reset", "jac_fast_division", "jac_last_division", "jac_destroy",
-           "jac_last_error",
+           "jac_get_field", "jac_set_field", "jac_reset", "jac_fast_division", "jac_last_division", "jac_depth_log",
+           "jac_destroy", "jac_last_error",
            "jac_profile", "jac_profile_read", "jac_stream_probe")
 
 
 class jac_opts(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("driver", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("tile_x", ctypes.c_int32), ("tile_y", ctypes.c_int32), ("M", ctypes.c_int32),
-                ("tol", ctypes.c_float), ("band_rows", ctypes.c_int32), ("max_sweeps", ctypes.c_int64)]
+                ("tol", ctypes.c_float), ("band_rows", ctypes.c_int32), ("max_sweeps", ctypes.c_int64),
+                ("checks", ctypes.c_int32), ("controller", ctypes.c_int32), ("overlap", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class JacobiError(RuntimeError):
@@ -74,6 +78,7 @@ def load_library():
         lib.jac_reset.argtypes = [vp]
         lib.jac_fast_division.argtypes = [vp]
         lib.jac_last_division.argtypes = [vp]
+        lib.jac_depth_log.argtypes = [vp, vp, i64, ctypes.POINTER(i64)]
         lib.jac_stream_probe.argtypes = [vp, vp, vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
         lib.jac_destroy.argtypes = [vp]
         lib.jac_last_error.argtypes = []
@@ -165,6 +170,18 @@ def jac_fast_division(ctx) -> int:
 
 def jac_last_division(ctx) -> int:
     return load_library().jac_last_division(ctx)
+
+
+def jac_depth_log(ctx):
+    """Returns (status, int32 array of the depth of each check interval of the last solve)."""
+    lib = load_library()
+    n = ctypes.c_int64(0)
+    st = lib.jac_depth_log(ctx, None, 0, ctypes.byref(n))
+    if st != JAC_OK:
+        return st, np.zeros(0, np.int32)
+    out = np.zeros(max(n.value, 1), np.int32)
+    st = lib.jac_depth_log(ctx, out.ctypes.data, int(n.value), ctypes.byref(n))
+    return st, out[: n.value]
 
 
 def jac_destroy(ctx) -> int:
@@ -271,6 +288,12 @@ class Solver:
         if v < 0:
             _check(v)
         return bool(v)
+
+    def depth_log(self):
+        """Depth of every check interval of the most recent solve or step."""
+        st, d = jac_depth_log(self.ctx)
+        _check(st)
+        return d
 
     @property
     def last_division_fast(self) -> bool:

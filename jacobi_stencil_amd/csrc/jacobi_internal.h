@@ -241,7 +241,8 @@ __device__ __forceinline__ void store_block_max(uint32_t m, Scratch* sc, int64_t
 // Launchers (kernels_*.hip).  All return hipSuccess or the launch error.
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_ghosts(float* u, const Geom& g, hipStream_t s);
-hipError_t launch_rhs(const float* u, const float* src, float* b, const StepArgs& a, hipStream_t s);
+// b = u^n + s and the per-block norm partials; keep_u: the plane gets u^n.
+hipError_t launch_rhs(const float* u, const float* src, float* b, bool keep_u, const StepArgs& a, hipStream_t s);
 // Count the float inputs n (all 2^32 except Inf, NaN and -0) on which
 // div_d<true> differs from n / d into sc->div_bad.
 hipError_t launch_verify_div(float d, float y, Scratch* sc, hipStream_t s);
@@ -266,16 +267,19 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
                           void* out, int nsteps, int cur0, bool async_mode, int D, int L, int tile_x, int tile_y,
                           int side, int64_t max_sweeps, int cus, int* grid_used, hipStream_t stream);
 size_t persist_out_bytes();
-// Block-asynchronous launch: tiles tx x ty (each 1..256, tx*ty <= 4096), a
-// frozen one-cell halo, D in-tile sweeps.
-hipError_t launch_async(const float* uin, const float* b, float* uout, int tx, int ty, int D, bool check,
+// Block-asynchronous launch: tiles tx x ty (each 1..256), each worked on
+// widened by o overlap cells per side ((tx+2o)*(ty+2o) <= 4096, o <= 64), a
+// frozen one-cell halo around that, D in-tile sweeps.
+hipError_t launch_async(const float* uin, const float* b, float* uout, int tx, int ty, int D, int o, bool check,
                         const StepArgs& a, hipStream_t s);
 // Automatic band height for a grid of `resident_waves` wavefront slots.
 int tblock_rows(int N, int D, int resident_waves);
 int tblock_waves_per_cu(int D, bool fast);
-hipError_t launch_sync(const float* uin, const float* b, float* uout, bool check, const StepArgs& a,
-                       hipStream_t s);
-hipError_t launch_residual(const float* u, const float* b, const StepArgs& a, hipStream_t s);
+// One synchronous sweep.  src != NULL: the unfused form, b holds u^n and
+// b = u^n + src is formed per point.
+hipError_t launch_sync(const float* uin, const float* b, const float* src, float* uout, bool check,
+                       const StepArgs& a, hipStream_t s);
+hipError_t launch_residual(const float* u, const float* b, const float* src, const StepArgs& a, hipStream_t s);
 // D sweeps (1..16) in one pass; H = output rows per wavefront band (>= 1).
 hipError_t launch_tblock(const float* uin, const float* b, float* uout, int D, bool check, const StepArgs& a,
                          int H, hipStream_t s);

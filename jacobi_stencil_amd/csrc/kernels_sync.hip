@@ -49,7 +49,9 @@ hipError_t launch_ghosts(float* u, const Geom& g, hipStream_t s) {
 
 // b = u^n + s for every unknown, and per-block maxima of |b + r*g| (g = 100
 // on row 0) for ||b_A||_inf.  One thread per 4 columns of one row; the grid
-// is (column groups) x (rows).
+// is (column groups) x (rows).  KEEP_U (the unfused sweep): the plane gets a
+// copy of u^n instead of b, the norm is the same.
+template <bool KEEP_U>
 __global__ __launch_bounds__(256) void k_rhs(const float* __restrict__ u, const float* __restrict__ src,
                                              float* __restrict__ b, StepArgs a) {
     const Geom g = a.g;
@@ -74,11 +76,13 @@ __global__ __launch_bounds__(256) void k_rhs(const float* __restrict__ u, const 
                 m = m > v ? m : v;
             }
         }
+        const float4 out = KEEP_U ? uu : bb;
         if (col0 + 4 <= g.N) {
-            st4_nt(b + o, bb);
+            st4_nt(b + o, out);
         } else {
+            const float vo[4] = {out.x, out.y, out.z, out.w};
             for (int c = 0; c < 4; ++c)
-                if (col0 + c < g.N) b[o + c] = vb[c];
+                if (col0 + c < g.N) b[o + c] = vo[c];
         }
     }
     store_block_max<4>(m, a.sc, (int64_t)blockIdx.y * gridDim.x + blockIdx.x);
@@ -90,10 +94,13 @@ int64_t rhs_blocks(int N) {
     return gx * gy;
 }
 
-hipError_t launch_rhs(const float* u, const float* src, float* b, const StepArgs& a, hipStream_t s) {
+hipError_t launch_rhs(const float* u, const float* src, float* b, bool keep_u, const StepArgs& a, hipStream_t s) {
     const int gx = (a.g.N + 1023) / 1024;
     int gy = a.g.N < 1024 ? a.g.N : 1024;
-    hipLaunchKernelGGL(k_rhs, dim3(gx, gy), dim3(256), 0, s, u, src, b, a);
+    if (keep_u)
+        hipLaunchKernelGGL(k_rhs<true>, dim3(gx, gy), dim3(256), 0, s, u, src, b, a);
+    else
+        hipLaunchKernelGGL(k_rhs<false>, dim3(gx, gy), dim3(256), 0, s, u, src, b, a);
     return hipGetLastError();
 }
 
@@ -182,12 +189,25 @@ __device__ __forceinline__ void sync_row(const float4& up, const float4& mid, co
     }
 }
 
+// The right-hand side of 4 columns: b itself, or (UNF, the unfused sweep)
+// u^n + s formed on the fly, with the same single addition as the RHS kernel.
+template <bool UNF, bool NT>
+__device__ __forceinline__ float4 rhs4(const float* pb, const float* ps) {
+    const float4 v = NT ? ld4_nt(pb) : ld4(pb);
+    if (!UNF) return v;
+    const float4 w = NT ? ld4_nt(ps) : ld4(ps);
+    return make_float4(v.x + w.x, v.y + w.y, v.z + w.z, v.w + w.w);
+}
+
 // One sweep u_{k+1} = J(u_k).  With CHECK the same pass also measures the
 // residual of u_k (the iterate it reads), which costs no extra memory traffic;
-// RESID_ONLY measures the residual and writes nothing.
-template <bool CHECK, bool RESID_ONLY, bool FAST>
+// RESID_ONLY measures the residual and writes nothing.  UNF: `bin` holds u^n
+// and `sin` the source s, and b = u^n + s is formed per point -- the unfused
+// baseline of page "stencil-jacobian.vercel.app", section 02 (16 bytes per
+// point per sweep instead of 12); the results are identical.
+template <bool CHECK, bool RESID_ONLY, bool FAST, bool UNF>
 __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, const float* __restrict__ bin,
-                                              float* __restrict__ uout, StepArgs a) {
+                                              const float* __restrict__ sin, float* __restrict__ uout, StepArgs a) {
     constexpr bool SWEEP = !RESID_ONLY;
     constexpr bool CHK = CHECK || RESID_ONLY;
     constexpr int H = kSyncRows;
@@ -207,6 +227,7 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
         const int64_t o = g.origin + (int64_t)row0 * P + col0;
         const float* pu = uin + o;
         const float* pb = bin + o;
+        const float* ps = UNF ? sin + o : nullptr;
         float* po = uout + o;
         if (wcol + 256 <= N && row0 + H <= N) {
             // interior wavefront: 256 full columns, H full rows.  West/east
@@ -228,7 +249,7 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
                 for (int k = 0; k < 4; ++k) {
                     const int i = i0 + k;
                     dn[k] = (i == H - 1) ? ld4(pu + (int64_t)(i + 1) * P) : ld4_nt(pu + (int64_t)(i + 1) * P);
-                    bb[k] = ld4_nt(pb + (int64_t)i * P);
+                    bb[k] = rhs4<UNF, true>(pb + (int64_t)i * P, UNF ? ps + (int64_t)i * P : nullptr);
                 }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -254,7 +275,7 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
             float4 mid = ld4(pu);
             for (int i = 0; i < rows; ++i) {
                 const float4 dn = ld4(pu + (int64_t)(i + 1) * P);
-                const float4 bb = ld4(pb + (int64_t)i * P);
+                const float4 bb = rhs4<UNF, false>(pb + (int64_t)i * P, UNF ? ps + (int64_t)i * P : nullptr);
                 const float wl = pu[(int64_t)i * P - 1];
                 const float er = pu[(int64_t)i * P + 4];
                 float4 o4;
@@ -279,28 +300,41 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
 
 int64_t sync_blocks(int N) { return sync_tiles(N).blocks; }
 
-hipError_t launch_sync(const float* uin, const float* b, float* uout, bool check, const StepArgs& a,
-                       hipStream_t s) {
-    SyncTiles t = sync_tiles(a.g.N);
-    const dim3 grid(t.blocks), block(64 * kSyncWaves);
+template <bool UNF>
+static void launch_sync_t(const float* uin, const float* b, const float* src, float* uout, bool check,
+                          const StepArgs& a, dim3 grid, dim3 block, hipStream_t s) {
     if (check) {
         if (a.fastdiv)
-            hipLaunchKernelGGL((k_sync<true, false, true>), grid, block, 0, s, uin, b, uout, a);
+            hipLaunchKernelGGL((k_sync<true, false, true, UNF>), grid, block, 0, s, uin, b, src, uout, a);
         else
-            hipLaunchKernelGGL((k_sync<true, false, false>), grid, block, 0, s, uin, b, uout, a);
+            hipLaunchKernelGGL((k_sync<true, false, false, UNF>), grid, block, 0, s, uin, b, src, uout, a);
     } else {
         if (a.fastdiv)
-            hipLaunchKernelGGL((k_sync<false, false, true>), grid, block, 0, s, uin, b, uout, a);
+            hipLaunchKernelGGL((k_sync<false, false, true, UNF>), grid, block, 0, s, uin, b, src, uout, a);
         else
-            hipLaunchKernelGGL((k_sync<false, false, false>), grid, block, 0, s, uin, b, uout, a);
+            hipLaunchKernelGGL((k_sync<false, false, false, UNF>), grid, block, 0, s, uin, b, src, uout, a);
     }
+}
+
+hipError_t launch_sync(const float* uin, const float* b, const float* src, float* uout, bool check,
+                       const StepArgs& a, hipStream_t s) {
+    SyncTiles t = sync_tiles(a.g.N);
+    const dim3 grid(t.blocks), block(64 * kSyncWaves);
+    if (src)
+        launch_sync_t<true>(uin, b, src, uout, check, a, grid, block, s);
+    else
+        launch_sync_t<false>(uin, b, nullptr, uout, check, a, grid, block, s);
     return hipGetLastError();
 }
 
-hipError_t launch_residual(const float* u, const float* b, const StepArgs& a, hipStream_t s) {
+hipError_t launch_residual(const float* u, const float* b, const float* src, const StepArgs& a, hipStream_t s) {
     SyncTiles t = sync_tiles(a.g.N);
-    hipLaunchKernelGGL((k_sync<false, true, false>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, u, b,
-                       (float*)nullptr, a);
+    if (src)
+        hipLaunchKernelGGL((k_sync<false, true, false, true>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, u, b,
+                           src, (float*)nullptr, a);
+    else
+        hipLaunchKernelGGL((k_sync<false, true, false, false>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, u, b,
+                           (const float*)nullptr, (float*)nullptr, a);
     return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@
 
 #include <algorithm>
 #include <cfloat>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -76,6 +77,7 @@ struct jac_ctx {
     double smax;     // max |s|
     double ubound;   // upper bound on max |u| over u^n and its ghost ring (Inf: none)
     int graph_fast;  // division path the cached graphs were captured with
+    std::vector<int32_t> dlog;  // depth of each check interval of the last jac_solve
     int cus;         // compute units of the device
     void* pout;      // pinned records of the persistent driver
     int pout_cap;
@@ -223,27 +225,40 @@ int timed(jac_ctx* c, int cls, F&& fn) {
     return JAC_OK;
 }
 
+bool is_sync(const jac_opts* o) { return o->kernel == JAC_SYNC || o->kernel == JAC_SYNC_UNFUSED; }
+
 int check_opts(const jac_ctx* c, const jac_opts* o) {
     if (!o) return fail(JAC_EINVAL, "opts is NULL");
-    if (o->kernel != JAC_SYNC && o->kernel != JAC_TBLOCK && o->kernel != JAC_ASYNC)
+    if (o->kernel != JAC_SYNC && o->kernel != JAC_TBLOCK && o->kernel != JAC_ASYNC && o->kernel != JAC_SYNC_UNFUSED)
         return fail(JAC_EINVAL, "unknown kernel");
+    if (o->checks != JAC_CHECKS_OVERLAPPED && o->checks != JAC_CHECKS_BLOCKING)
+        return fail(JAC_EINVAL, "unknown checks mode");
+    if (o->controller < JAC_STATIC || o->controller > JAC_G_FB) return fail(JAC_EINVAL, "unknown controller");
+    if (o->controller != JAC_STATIC && (o->kernel != JAC_ASYNC || o->driver != JAC_LAUNCH))
+        return fail(JAC_EINVAL, "depth controllers need the ASYNC kernel and the LAUNCH driver");
+    if (o->overlap != 0 && o->kernel != JAC_ASYNC) return fail(JAC_EINVAL, "overlap is an ASYNC option");
+    if (o->overlap < 0 || o->overlap > 64) return fail(JAC_EINVAL, "overlap must be in 0..64");
+    if (o->reserved != 0) return fail(JAC_EINVAL, "reserved must be 0");
+    if (o->driver == JAC_PERSISTENT && (o->kernel == JAC_SYNC_UNFUSED || o->overlap != 0))
+        return fail(JAC_EINVAL, "the persistent driver runs SYNC, TBLOCK and ASYNC without overlap");
     if (o->driver != JAC_LAUNCH && o->driver != JAC_GRAPH && o->driver != JAC_PERSISTENT)
         return fail(JAC_EINVAL, "unknown driver");
     if (o->M < 1) return fail(JAC_EINVAL, "M must be >= 1");
     if (!(o->tol > 0.0f) || !std::isfinite(o->tol)) return fail(JAC_EINVAL, "tol must be a positive finite float");
     if (o->max_sweeps < 1) return fail(JAC_EINVAL, "max_sweeps must be >= 1");
     if (o->band_rows < 0 || o->band_rows > 65536) return fail(JAC_EINVAL, "band_rows must be in 0..65536");
-    if (o->kernel != JAC_SYNC && (o->D < 1 || o->D > kMaxD)) return fail(JAC_EINVAL, "D must be in 1..32");
+    if (!is_sync(o) && (o->D < 1 || o->D > kMaxD)) return fail(JAC_EINVAL, "D must be in 1..32");
     if (o->kernel == JAC_ASYNC && (o->tile_x < 1 || o->tile_x > 256 || o->tile_y < 1 || o->tile_y > 256 ||
-                                   o->tile_x * o->tile_y > 4096))
-        return fail(JAC_EINVAL, "tile_x and tile_y must be in 1..256 with tile_x * tile_y <= 4096");
+                                   (int64_t)(o->tile_x + 2 * o->overlap) * (o->tile_y + 2 * o->overlap) > 4096))
+        return fail(JAC_EINVAL,
+                    "tile_x and tile_y must be in 1..256 with (tile_x + 2 overlap) * (tile_y + 2 overlap) <= 4096");
     if (o->kernel == JAC_TBLOCK && o->D > kMaxTBlockD) return fail(JAC_EINVAL, "TBLOCK needs D in 1..16");
     (void)c;
     return JAC_OK;
 }
 
 // Sweeps per launch and the check interval for these options.
-int sweeps_per_launch(const jac_opts* o) { return o->kernel == JAC_SYNC ? 1 : o->D; }
+int sweeps_per_launch(const jac_opts* o) { return is_sync(o) ? 1 : o->D; }
 int64_t check_interval(const jac_opts* o) {
     int spl = sweeps_per_launch(o);
     return spl > o->M ? spl : o->M;
@@ -270,12 +285,15 @@ int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, i
     int64_t npart = 0;
     switch (o->kernel) {
         case JAC_SYNC:
+        case JAC_SYNC_UNFUSED: {
             (void)m;
             npart = sync_blocks(c->N);
             if (check && npart > c->npart_cap) return fail(JAC_EDEVICE, "sync grid exceeds partial slots");
+            const float* src = o->kernel == JAC_SYNC_UNFUSED ? c->s : nullptr;
             st = timed(c, check ? KC_SYNC_CHECK : KC_SYNC,
-                       [&] { return launch_sync(in, c->b, out, check, a, c->stream); });
+                       [&] { return launch_sync(in, c->b, src, out, check, a, c->stream); });
             break;
+        }
         case JAC_TBLOCK: {
             if (o->band_rows == 0 && c->tb_rows[m] == 0)
                 c->tb_rows[m] = tblock_rows(c->N, m, c->cus * std::min(16, tblock_waves_per_cu(m, c->fastdiv != 0)));
@@ -290,7 +308,7 @@ int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, i
             npart = async_blocks(c->N, o->tile_x, o->tile_y);
             if (check && npart > c->npart_cap) return fail(JAC_EINVAL, "tile too small for this N");
             st = timed(c, KC_ASYNC, [&] {
-                return launch_async(in, c->b, out, o->tile_x, o->tile_y, m, check, a, c->stream);
+                return launch_async(in, c->b, out, o->tile_x, o->tile_y, m, o->overlap, check, a, c->stream);
             });
             break;
         default:
@@ -319,24 +337,27 @@ int enqueue_sweeps(jac_ctx* c, const jac_opts* o, int64_t count, bool check_firs
     return JAC_OK;
 }
 
-// b = u^n + s and ||b_A|| (which also clears the stop flag).
-int enqueue_rhs(jac_ctx* c, float tol) {
-    StepArgs a = base_args(c, tol);
+// b = u^n + s and ||b_A|| (which also clears the stop flag).  For the
+// unfused sweep the b plane keeps u^n instead.
+int enqueue_rhs(jac_ctx* c, const jac_opts* o) {
+    StepArgs a = base_args(c, o->tol);
     const int64_t npart = rhs_blocks(c->N);
     if (npart > c->npart_cap) return fail(JAC_EDEVICE, "rhs grid exceeds partial slots");
-    int st = timed(c, KC_RHS, [&] { return launch_rhs(c->u[c->cur], c->s, c->b, a, c->stream); });
+    const bool keep_u = o->kernel == JAC_SYNC_UNFUSED;
+    int st = timed(c, KC_RHS, [&] { return launch_rhs(c->u[c->cur], c->s, c->b, keep_u, a, c->stream); });
     if (st) return st;
     return timed(c, KC_REDUCE, [&] { return launch_reduce(npart, true, a, c->stream); });
 }
 
 // The residual of u[buf] alone (no sweep), reduced into mailbox slot `slot`.
-int enqueue_residual(jac_ctx* c, float tol, int buf, int slot) {
-    StepArgs a = base_args(c, tol);
+int enqueue_residual(jac_ctx* c, const jac_opts* o, int buf, int slot) {
+    StepArgs a = base_args(c, o->tol);
     a.slot = slot;
     const float* in = c->u[buf];
-    int st = timed(c, KC_RESID, [&] { return launch_residual(in, c->b, a, c->stream); });
+    const float* src = o->kernel == JAC_SYNC_UNFUSED ? c->s : nullptr;
+    int st = timed(c, KC_RESID, [&] { return launch_residual(in, c->b, src, a, c->stream); });
     if (st) return st;
-    return enqueue_check_reduce(c, sync_blocks(c->N), tol, slot);
+    return enqueue_check_reduce(c, sync_blocks(c->N), o->tol, slot);
 }
 
 uint32_t read_mail(const volatile uint32_t* p) { return *p; }
@@ -361,7 +382,7 @@ void drop_graphs(jac_ctx* c) {
 
 bool same_graph_key(const jac_opts* a, const jac_opts* b) {
     return a->kernel == b->kernel && a->D == b->D && a->M == b->M && a->tile_x == b->tile_x &&
-           a->tile_y == b->tile_y && a->band_rows == b->band_rows && a->tol == b->tol;
+           a->tile_y == b->tile_y && a->band_rows == b->band_rows && a->tol == b->tol && a->overlap == b->overlap;
 }
 
 // Capture the launches of one interval starting from u[start] on a private
@@ -423,9 +444,120 @@ int graph_for(jac_ctx* c, const jac_opts* o, bool check, int start, hipGraphExec
     return JAC_OK;
 }
 
+// ---- depth controllers (page "stencil-jacobian.vercel.app", section 02)
+
+// G-asc / G-desc levels: the depth steps as rho crosses 1e-2, 1e-3, 1e-4,
+// compared as binary32 values.
+int asc_level(float rho) { return rho >= 1e-2f ? 1 : rho >= 1e-3f ? 2 : rho >= 1e-4f ? 4 : 8; }
+int desc_level(float rho) { return rho >= 1e-2f ? 8 : rho >= 1e-3f ? 4 : rho >= 1e-4f ? 2 : 1; }
+
+struct DepthControl {
+    int kind, Dmax, D;
+    float prev_rho;    // G-fb: rho of the previous check (NaN: none yet)
+    double prev_rate;  // G-fb: the last rate compared against (NaN: none yet)
+    int settle;        // G-fb: checks still to skip after a change
+
+    DepthControl(int k, int dmax) : kind(k), Dmax(dmax), D(dmax), prev_rho(NAN), prev_rate(NAN), settle(0) {
+        if (kind == JAC_G_ASC || kind == JAC_G_FB) D = 1;
+    }
+    // After a check of an interval run at depth D that took `ms` milliseconds.
+    void update(float rho, double ms) {
+        auto clamp = [&](int v) { return v < 1 ? 1 : (v > Dmax ? Dmax : v); };
+        if (kind == JAC_G_ASC) {
+            D = std::max(D, clamp(asc_level(rho)));
+        } else if (kind == JAC_G_DESC) {
+            D = std::min(D, clamp(desc_level(rho) * Dmax / 8));
+        } else if (kind == JAC_G_FB) {
+            const float before = prev_rho;
+            prev_rho = rho;
+            if (std::isnan(before) || !(ms > 0.0)) return;
+            const double rate = -std::log((double)rho / (double)before) / ms;
+            if (settle > 0) {  // the residual bump right after a change
+                --settle;
+                return;
+            }
+            const bool drop = !std::isnan(prev_rate) && rate < 0.9 * prev_rate;
+            prev_rate = rate;
+            const int next = drop ? std::max(1, D / 2) : std::min(Dmax, D * 2);
+            if (next != D) {
+                D = next;
+                settle = 1;
+            }
+        }
+    }
+};
+
+// One step with blocking checks: after each interval a standalone residual
+// kernel, then the host waits for R and decides -- and, under a depth
+// controller, picks the next interval's depth -- before queueing more.
+int run_step_blocking(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out) {
+    const int64_t L = check_interval(o);
+    const bool graph = o->driver == JAC_GRAPH;
+    c->fast_now = division_path(c, 1, (double)o->max_sweeps + (double)L);
+    c->step_serial += 1;
+    c->cur_group = -1;
+    c->cur_first = false;
+    if (c->prof_every > 0) {
+        int s0 = drain_profile(c, c->step_serial - 1);
+        if (s0) return s0;
+    }
+    int st = enqueue_rhs(c, o);
+    if (st) return st;
+    int buf = c->cur;
+    DepthControl ctl(o->controller, is_sync(o) ? 1 : o->D);
+    jac_opts oi = *o;
+    for (int64_t g = 1;; ++g) {
+        oi.D = ctl.D;
+        c->cur_group = g;
+        c->cur_first = true;
+        const auto t0 = std::chrono::steady_clock::now();
+        if (graph) {
+            hipGraphExec_t gx;
+            int flips;
+            st = graph_for(c, &oi, false, buf, &gx, &flips);
+            if (st) return st;
+            JAC_HIP(hipGraphLaunch(gx, c->stream));
+            buf ^= flips;
+        } else {
+            st = enqueue_sweeps(c, &oi, L, false, 0, &buf);
+            if (st) return st;
+        }
+        const int slot = (int)((g - 1) % kRing);
+        c->mail->R[slot] = kEmpty;
+        st = enqueue_residual(c, o, buf, slot);
+        if (st) return st;
+        const int ev = (int)(g % kRing);
+        JAC_HIP(hipEventRecord(c->ev[ev], c->stream));
+        JAC_HIP(hipEventSynchronize(c->ev[ev]));
+        const double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+        const uint32_t Rb = read_mail(&c->mail->R[slot]);
+        if (Rb == kEmpty) return fail(JAC_EDEVICE, "a residual check did not report");
+        const float R = mail_float(&c->mail->R[slot]);
+        const float rho = R / mail_float(&c->mail->bA_bits);
+        c->dlog.push_back(oi.D);
+        const int64_t k = g * L;
+        const bool stop = !(rho >= o->tol);
+        if (stop || k >= o->max_sweeps) {
+            c->cur = buf;
+            if (sweeps_out) *sweeps_out = k;
+            if (rho_out) *rho_out = rho;
+            if (std::isnan(rho)) return fail(JAC_ENAN, "rho is NaN");
+            if (!stop) return fail(JAC_ENOCONV, "max_sweeps reached before rho < tol");
+            return JAC_OK;
+        }
+        ctl.update(rho, ms);
+        if (c->prof_every > 0 && c->recs.size() > 8192) {
+            st = drain_profile(c, c->step_serial);
+            if (st) return st;
+        }
+    }
+}
+
 // One step through the launch or the graph driver.  Check g (g >= 1) examines
 // u_{gL}; its R lands in mailbox slot (g - 1) % kRing.
 int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out) {
+    if (o->checks == JAC_CHECKS_BLOCKING || o->controller != JAC_STATIC)
+        return run_step_blocking(c, o, sweeps_out, rho_out);
     const int64_t L = check_interval(o);
     const bool graph = o->driver == JAC_GRAPH;
     // sweeps this step may run: up to max_sweeps, plus the interval queued beyond a check
@@ -437,7 +569,7 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
         int s0 = drain_profile(c, c->step_serial - 1);  // earlier steps have finished
         if (s0) return s0;
     }
-    int st = enqueue_rhs(c, o->tol);
+    int st = enqueue_rhs(c, o);
     if (st) return st;
     int buf = c->cur;
     c->cur_group = 0;
@@ -466,7 +598,7 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
         int s2;
         if (g_enq * L >= o->max_sweeps) {
             // the last allowed check: measure only, keep u_{gL} in place
-            s2 = enqueue_residual(c, o->tol, buf, slot);
+            s2 = enqueue_residual(c, o, buf, slot);
             if (s2) return s2;
             JAC_HIP(hipEventRecord(c->ev[ev], c->stream));
             final_enqueued = true;
@@ -509,6 +641,7 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
         const bool stop = !(rho >= o->tol);
         if (stop || k >= o->max_sweeps) {
             if (c->prof_every > 0 && stop) mark_noops(c, g);
+            for (int64_t i = 0; i < g; ++i) c->dlog.push_back(sweeps_per_launch(o));
             c->cur = c->start_buf[ev];
             if (sweeps_out) *sweeps_out = k;
             if (rho_out) *rho_out = rho;
@@ -600,6 +733,10 @@ void jac_opts_default(jac_opts* o) {
     o->tol = 1e-5f;
     o->band_rows = 0;
     o->max_sweeps = 1000000;
+    o->checks = JAC_CHECKS_OVERLAPPED;
+    o->controller = JAC_STATIC;
+    o->overlap = 0;
+    o->reserved = 0;
 }
 
 size_t jac_workspace_bytes(int N) {
@@ -748,6 +885,7 @@ int jac_solve(jac_t c, int nsteps, const jac_opts* o, int64_t* sweeps, float* rh
         if (sweeps) sweeps[n] = 0;
         if (rho) rho[n] = NAN;
     }
+    c->dlog.clear();
     if (o->driver == JAC_PERSISTENT) {
         st = run_persistent(c, o, nsteps, sweeps, rho);
     } else {
@@ -776,7 +914,7 @@ int jac_sweep(jac_t c, const jac_opts* o, int64_t nsweeps, float* rho) {
     c->cur_group = -1;
     c->cur_first = false;
     c->fast_now = division_path(c, 1, (double)nsweeps);
-    st = enqueue_rhs(c, o->tol);
+    st = enqueue_rhs(c, o);
     if (st) return st;
     int buf = c->cur;
     st = enqueue_sweeps(c, o, nsweeps, false, 0, &buf);
@@ -788,7 +926,7 @@ int jac_sweep(jac_t c, const jac_opts* o, int64_t nsweeps, float* rho) {
     grow_ubound(c, (double)nsweeps);
     if (rho) {
         c->mail->R[0] = kEmpty;
-        st = enqueue_residual(c, o->tol, c->cur, 0);
+        st = enqueue_residual(c, o, c->cur, 0);
         if (st) return st;
     }
     JAC_HIP(hipStreamSynchronize(c->stream));
@@ -855,6 +993,15 @@ int jac_stream_probe(float* c, const float* a, const float* b, size_t n, int kin
 int jac_fast_division(jac_t c) {
     if (!c) return fail(JAC_EINVAL, "context is NULL");
     return c->fastdiv;
+}
+
+int jac_depth_log(jac_t c, int32_t* depths, int64_t cap, int64_t* count) {
+    if (!c) return fail(JAC_EINVAL, "context is NULL");
+    if (cap < 0 || (cap > 0 && !depths)) return fail(JAC_EINVAL, "depths is NULL or cap < 0");
+    const int64_t n = (int64_t)c->dlog.size();
+    for (int64_t i = 0; i < n && i < cap; ++i) depths[i] = c->dlog[(size_t)i];
+    if (count) *count = n;
+    return JAC_OK;
 }
 
 int jac_last_division(jac_t c) {

@@ -20,9 +20,10 @@ def say(*args):
 
 
 def opts(kernel=jac.JAC_SYNC, driver=jac.JAC_LAUNCH, D=1, tile_x=32, tile_y=8, M=8, tol=1e-5,
-         max_sweeps=10**6, band_rows=0):
+         max_sweeps=10**6, band_rows=0, checks=jac.JAC_CHECKS_OVERLAPPED, controller=jac.JAC_STATIC, overlap=0):
     return jac.jac_opts_default(kernel=kernel, driver=driver, D=D, tile_x=tile_x, tile_y=tile_y, M=M,
-                                tol=tol, max_sweeps=max_sweeps, band_rows=band_rows)
+                                tol=tol, max_sweeps=max_sweeps, band_rows=band_rows, checks=checks,
+                                controller=controller, overlap=overlap)
 
 
 def lib_solve(N, r, s, steps, o, u0=None, allow=(jac.JAC_ENOCONV, jac.JAC_ENAN)):

@@ -33,11 +33,13 @@ def test_library_exports_every_declared_function():
 
 
 def test_opts_layout():
-    assert ctypes.sizeof(jac.jac_opts) == 40
+    assert ctypes.sizeof(jac.jac_opts) == 56
     assert jac.jac_opts.max_sweeps.offset == 32
+    assert (jac.jac_opts.checks.offset, jac.jac_opts.controller.offset, jac.jac_opts.overlap.offset) == (40, 44, 48)
     o = jac.jac_opts_default()
     assert (o.kernel, o.driver, o.D, o.tile_x, o.tile_y, o.M) == (jac.JAC_SYNC, jac.JAC_LAUNCH, 1, 32, 8, 8)
     assert o.tol == pytest.approx(1e-5) and o.max_sweeps == 10**6 and o.band_rows == 0
+    assert (o.checks, o.controller, o.overlap, o.reserved) == (jac.JAC_CHECKS_OVERLAPPED, jac.JAC_STATIC, 0, 0)
 
 
 def test_workspace_bytes():
