@@ -259,7 +259,7 @@ hipError_t launch_probe(float* c, const float* a, const float* b, int64_t n, int
 int64_t rhs_blocks(int N);
 int64_t sync_blocks(int N);
 int64_t tblock_blocks(int N, int D, int H);
-int64_t async_blocks(int N, int tx, int ty);
+int64_t async_blocks(int N, int tx, int ty, int o);
 // The whole solve of nsteps steps in one cooperative kernel (see
 // kernels_persist.hip).  `out` is pinned host memory for nsteps records of
 // persist_out_bytes() each; `partial` needs 2 x grid slots.

@@ -67,34 +67,36 @@ __global__ __launch_bounds__(kAsyncThreads) void k_async(const float* __restrict
             B[k] = v;
         }
         const int npts = w * h;
+        // this thread's points, once: LDS offset, and (region row << 16 | column)
+        // with bit 31 set for a point the tile owns; the sweep loop then does no
+        // index arithmetic
+        const int nq = (npts + kAsyncThreads - 1) / kAsyncThreads;  // uniform
         float bb[kAsyncPerThread];
+        int cl[kAsyncPerThread];
+        uint32_t ij[kAsyncPerThread];
 #pragma unroll
         for (int q = 0; q < kAsyncPerThread; ++q) {
             const int p = threadIdx.x + q * kAsyncThreads;
             bb[q] = 0.0f;
+            cl[q] = lp + 1;
+            ij[q] = 0u;
             if (p < npts) {
                 const int i = p / w, j = p - (p / w) * w;
+                cl[q] = (i + 1) * lp + (j + 1);
+                const bool own = ey0 + i >= y0 && ey0 + i < y1 && ex0 + j >= x0 && ex0 + j < x1;
+                ij[q] = ((uint32_t)i << 16) | (uint32_t)j | (own ? 0x80000000u : 0u);
                 bb[q] = bin[g.origin + (int64_t)(ey0 + i) * P + (ex0 + j)];
             }
         }
         __syncthreads();
-        // a point of the region is one of the tile's own
-        auto owned = [&](int i, int j) {
-            return ey0 + i >= y0 && ey0 + i < y1 && ex0 + j >= x0 && ex0 + j < x1;
-        };
         if (CHK) {
             // residual of u_k on the tile's own points (the halo is u_k too)
 #pragma unroll
             for (int q = 0; q < kAsyncPerThread; ++q) {
-                const int p = threadIdx.x + q * kAsyncThreads;
-                if (p < npts) {
-                    const int i = p / w, j = p - (p / w) * w;
-                    if (owned(i, j)) {
-                        const int c = (i + 1) * lp + (j + 1);
-                        const uint32_t v =
-                            residual_bits(A[c], A[c + 1], A[c - 1], A[c - lp], A[c + lp], bb[q], r);
-                        m = m > v ? m : v;
-                    }
+                if (q < nq && (ij[q] & 0x80000000u)) {
+                    const int c = cl[q];
+                    const uint32_t v = residual_bits(A[c], A[c + 1], A[c - 1], A[c - lp], A[c + lp], bb[q], r);
+                    m = m > v ? m : v;
                 }
             }
         }
@@ -103,10 +105,8 @@ __global__ __launch_bounds__(kAsyncThreads) void k_async(const float* __restrict
         for (int s = 0; s < D; ++s) {
 #pragma unroll
             for (int q = 0; q < kAsyncPerThread; ++q) {
-                const int p = threadIdx.x + q * kAsyncThreads;
-                if (p < npts) {
-                    const int i = p / w, j = p - (p / w) * w;
-                    const int c = (i + 1) * lp + (j + 1);
+                if (q < nq && threadIdx.x + q * kAsyncThreads < npts) {
+                    const int c = cl[q];
                     nxt[c] = jacobi_update<FAST>(cur[c + 1], cur[c - 1], cur[c - lp], cur[c + lp], bb[q], r, d, y);
                 }
             }
@@ -118,19 +118,142 @@ __global__ __launch_bounds__(kAsyncThreads) void k_async(const float* __restrict
         float* dst = uout + g.origin + (int64_t)ey0 * P + ex0;
 #pragma unroll
         for (int q = 0; q < kAsyncPerThread; ++q) {
-            const int p = threadIdx.x + q * kAsyncThreads;
-            if (p < npts) {
-                const int i = p / w, j = p - (p / w) * w;
-                if (owned(i, j)) dst[(int64_t)i * P + j] = cur[(i + 1) * lp + (j + 1)];
+            if (q < nq && (ij[q] & 0x80000000u)) {
+                const int i = (int)((ij[q] >> 16) & 0x7FFFu), j = (int)(ij[q] & 0xFFFFu);
+                dst[(int64_t)i * P + j] = cur[cl[q]];
             }
         }
     }
     if (CHK) store_block_max<kAsyncThreads / 64>(m, a.sc, blockIdx.x);
 }
 
-int64_t async_blocks(int N, int tx, int ty) {
+// ---- register form: tile widths dividing 64, heights 4, 8, 16 or 32, no overlap
+//
+// One wavefront owns a strip of 64 columns x TY rows, one column per lane, and
+// keeps the strip's TY values of u, of b and of the frozen halo in registers;
+// the strip holds 64 / tile_x whole tiles side by side.  North and south
+// neighbours are the lane's own rows (rows Y-1 and Y+TY are the frozen halo
+// rows, read once); west and east neighbours come from the adjacent lanes by
+// DPP shifts, except on a tile's edge columns, which read the frozen halo
+// column instead: the neighbouring tile's (or neighbouring strip's) u_k,
+// captured before the first sweep.  A sweep updates the rows in place from the
+// top, keeping the old value of the row above.  Lanes past column N-1 and rows
+// past N-1 hold the zero ghost column / row and padding and are never updated,
+// which also gives clipped tiles their ghost halo.  No LDS, no barriers.
+constexpr int kWaveStrip = 64;
+
+bool async_wave_form(int tx, int ty, int o) {
+    return o == 0 && (tx == 8 || tx == 16 || tx == 32 || tx == 64) && (ty == 4 || ty == 8 || ty == 16 || ty == 32);
+}
+
+template <int TY, bool EDGE, bool CHK, bool FAST>
+__device__ __forceinline__ uint32_t async_strip(const float* __restrict__ uin, const float* __restrict__ bin,
+                                                float* __restrict__ uout, const StepArgs& a, int tx, int D, int X,
+                                                int Y) {
+    const Geom g = a.g;
+    const int N = g.N, P = g.P;
+    const int lane = threadIdx.x & 63;
+    const int col = X + lane;
+    const bool in_col = !EDGE || col < N;
+    const bool west = (lane & (tx - 1)) == 0, east = (lane & (tx - 1)) == tx - 1;
+    const float r = a.r, d = a.d, y = a.y;
+    const float* pu = uin + g.origin + (int64_t)Y * P + col;
+    const float* pb = bin + g.origin + (int64_t)Y * P + col;
+    float cur[TY], bb[TY], hx[TY];
+    const float top = pu[-(int64_t)P];
+    const float bot = pu[(int64_t)TY * P];
+#pragma unroll
+    for (int i = 0; i < TY; ++i) {
+        cur[i] = pu[(int64_t)i * P];
+        bb[i] = pb[(int64_t)i * P];
+    }
+    // the columns just outside the strip, lane i holding row i
+    const int er = lane < TY ? lane : 0;
+    const float wcol = uin[g.origin + (int64_t)(Y + er) * P + X - 1];
+    const float ecol = uin[g.origin + (int64_t)(Y + er) * P + X + kWaveStrip];
+#pragma unroll
+    for (int i = 0; i < TY; ++i) {
+        const float l = from_left(cur[i]), rr = from_right(cur[i]);
+        const float ws = __shfl(wcol, i, 64), es = __shfl(ecol, i, 64);
+        hx[i] = west ? (lane == 0 ? ws : l) : (east ? (lane == 63 ? es : rr) : 0.0f);
+    }
+    uint32_t m = 0;
+    if (CHK) {
+        // residual of u_k on the strip's points
+#pragma unroll
+        for (int i = 0; i < TY; ++i) {
+            const float l = from_left(cur[i]), rr = from_right(cur[i]);
+            const float W = west ? hx[i] : l;
+            const float E = east ? hx[i] : rr;
+            const float Nn = i > 0 ? cur[i - 1] : top;
+            const float Sn = i + 1 < TY ? cur[i + 1] : bot;
+            const uint32_t v = residual_bits(cur[i], E, W, Nn, Sn, bb[i], r);
+            if ((!EDGE || Y + i < N) && in_col) m = m > v ? m : v;
+        }
+    }
+    for (int s = 0; s < D; ++s) {
+        float prev = top;  // old value of the row above
+#pragma unroll
+        for (int i = 0; i < TY; ++i) {
+            const float c = cur[i];
+            const float l = from_left(c), rr = from_right(c);
+            const float W = west ? hx[i] : l;
+            const float E = east ? hx[i] : rr;
+            const float Sn = i + 1 < TY ? cur[i + 1] : bot;
+            const float v = jacobi_update<FAST>(E, W, prev, Sn, bb[i], r, d, y);
+            prev = c;
+            if (!EDGE || Y + i < N) cur[i] = in_col ? v : c;
+        }
+    }
+    float* po = uout + g.origin + (int64_t)Y * P + col;
+#pragma unroll
+    for (int i = 0; i < TY; ++i)
+        if ((!EDGE || Y + i < N) && in_col) po[(int64_t)i * P] = cur[i];
+    return m;
+}
+
+template <int TY, bool CHK, bool FAST>
+__global__ __launch_bounds__(256) void k_async_wave(const float* __restrict__ uin, const float* __restrict__ bin,
+                                                    float* __restrict__ uout, StepArgs a, int tx, int D) {
+    if (a.sc->stop) return;  // a previous check already stopped the step
+    const int N = a.g.N;
+    const int sx = (N + kWaveStrip - 1) / kWaveStrip, sy = (N + TY - 1) / TY;
+    const int wid = xcd_logical_block(blockIdx.x, gridDim.x) * 4 + (int)(threadIdx.x >> 6);
+    uint32_t m = 0;
+    if (wid < sx * sy) {
+        const int X = (wid % sx) * kWaveStrip, Y = (wid / sx) * TY;
+        if (X + kWaveStrip <= N && Y + TY <= N)
+            m = async_strip<TY, false, CHK, FAST>(uin, bin, uout, a, tx, D, X, Y);
+        else
+            m = async_strip<TY, true, CHK, FAST>(uin, bin, uout, a, tx, D, X, Y);
+    }
+    if (CHK) store_block_max<4>(m, a.sc, blockIdx.x);
+}
+
+int64_t async_blocks(int N, int tx, int ty, int o) {
+    if (async_wave_form(tx, ty, o)) {
+        const int64_t strips = (int64_t)((N + kWaveStrip - 1) / kWaveStrip) * ((N + ty - 1) / ty);
+        return ((strips + 3) / 4 + 7) / 8 * 8;
+    }
     const int64_t tiles = (int64_t)((N + tx - 1) / tx) * ((N + ty - 1) / ty);
     return (tiles + 7) / 8 * 8;
+}
+
+template <int TY>
+static void launch_wave_t(const float* uin, const float* b, float* uout, int tx, int D, bool check,
+                          const StepArgs& a, dim3 grid, hipStream_t s) {
+    const dim3 block(256);
+    if (check) {
+        if (a.fastdiv)
+            hipLaunchKernelGGL((k_async_wave<TY, true, true>), grid, block, 0, s, uin, b, uout, a, tx, D);
+        else
+            hipLaunchKernelGGL((k_async_wave<TY, true, false>), grid, block, 0, s, uin, b, uout, a, tx, D);
+    } else {
+        if (a.fastdiv)
+            hipLaunchKernelGGL((k_async_wave<TY, false, true>), grid, block, 0, s, uin, b, uout, a, tx, D);
+        else
+            hipLaunchKernelGGL((k_async_wave<TY, false, false>), grid, block, 0, s, uin, b, uout, a, tx, D);
+    }
 }
 
 hipError_t launch_async(const float* uin, const float* b, float* uout, int tx, int ty, int D, int o, bool check,
@@ -138,8 +261,18 @@ hipError_t launch_async(const float* uin, const float* b, float* uout, int tx, i
     if (tx < 1 || ty < 1 || tx > 256 || ty > 256 || o < 0 || o > 64 ||
         (int64_t)(tx + 2 * o) * (ty + 2 * o) > kAsyncMaxPts)
         return hipErrorInvalidValue;
-    const int64_t blocks = async_blocks(a.g.N, tx, ty);
+    const int64_t blocks = async_blocks(a.g.N, tx, ty, o);
     if (blocks > (int64_t)0x7fffffff) return hipErrorInvalidValue;
+    if (async_wave_form(tx, ty, o)) {
+        const dim3 grid((unsigned)blocks);
+        switch (ty) {
+            case 4: launch_wave_t<4>(uin, b, uout, tx, D, check, a, grid, s); break;
+            case 8: launch_wave_t<8>(uin, b, uout, tx, D, check, a, grid, s); break;
+            case 16: launch_wave_t<16>(uin, b, uout, tx, D, check, a, grid, s); break;
+            default: launch_wave_t<32>(uin, b, uout, tx, D, check, a, grid, s); break;
+        }
+        return hipGetLastError();
+    }
     const size_t lds = (size_t)2 * (tx + 2 * o + 2) * (ty + 2 * o + 2) * sizeof(float);
     const dim3 grid((unsigned)blocks), block(kAsyncThreads);
     if (check) {

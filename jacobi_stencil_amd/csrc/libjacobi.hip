@@ -305,7 +305,7 @@ int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, i
             break;
         }
         case JAC_ASYNC:
-            npart = async_blocks(c->N, o->tile_x, o->tile_y);
+            npart = async_blocks(c->N, o->tile_x, o->tile_y, o->overlap);
             if (check && npart > c->npart_cap) return fail(JAC_EINVAL, "tile too small for this N");
             st = timed(c, KC_ASYNC, [&] {
                 return launch_async(in, c->b, out, o->tile_x, o->tile_y, m, o->overlap, check, a, c->stream);

@@ -39,6 +39,21 @@ def test_tiles_and_depths_bitwise(tile, D):
     assert_same(lib_solve(N, r, s, 2, opts(kernel=AS, D=D, tile_x=tx, tile_y=ty)), ref, f"{tile} D={D}")
 
 
+@pytest.mark.parametrize("tile", [(8, 4), (16, 8), (64, 4), (8, 32), (32, 32), (16, 16)])
+@pytest.mark.parametrize("N", [64, 150, 200])
+def test_register_form_shapes_bitwise(tile, N):
+    """Tile widths dividing 64 and heights 4..32 run in registers, one 64-column
+    strip per wavefront holding several tiles: edges inside a strip, clipped
+    tiles and strips past the grid must all match the tile model."""
+    r = 10.0
+    say("async register form", tile, N)
+    s = workloads.gaussian_source(N, r)
+    for D in (1, 3, 8):
+        ref = oracle.solve(N, r, s, steps=1, M=8, mode=oracle.ASYNC, D=D, tx=tile[0], ty=tile[1])
+        got = lib_solve(N, r, s, 1, opts(kernel=jac.JAC_ASYNC, D=D, tile_x=tile[0], tile_y=tile[1]))
+        assert_same(got, ref, f"{tile} N={N} D={D}")
+
+
 @pytest.mark.parametrize("D", [3, 12, 16, 32])
 def test_deep_and_odd_depths_bitwise(D):
     N, r = 97, 100.0
