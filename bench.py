@@ -128,7 +128,8 @@ def traffic_from(fetch_csv, write_csv, probe_mib, out_path, key):
     probe = next(k for k in fetch if "k_probe<0" in k)
     f_scale = known / fetch[probe][0]    # the first probe launch is the copy of `probe_mib`
     w_scale = known / write[probe][0]
-    cands = [k for k in fetch if ("k_tblock" in k if ":tblock:" in key else "k_sync<" in k)]
+    pattern = {"tblock": "k_tblock", "async": "k_async", "sync": "k_sync<"}[key.split(":")[1]]
+    cands = [k for k in fetch if pattern in k]
     rows = []
     for k in cands:
         fs = [v for v in fetch[k] if v > 1e6]   # launches that returned at once fetch ~nothing
