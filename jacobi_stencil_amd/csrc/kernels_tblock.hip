@@ -212,12 +212,15 @@ struct TBStream {
         ring[s][lane] = cb;
         float4 out;
         const int depth = j - j0;  // level t is exact from the (2t)-th row of the band on
+        // b of the next level is read one level ahead, so the LDS latency
+        // overlaps the current level's arithmetic
+        auto slot = [&](int t) { return s - t < 0 ? s - t + R : s - t; };
+        float4 bnext = ring[slot(1)][lane];
 #pragma unroll
         for (int t = 1; t <= D; ++t) {
             if (2 * t <= depth) {
-                int st = s - t;
-                if (st < 0) st += R;
-                const float4 bb = ring[st][lane];
+                const float4 bb = bnext;
+                if (t < D) bnext = ring[slot(t + 1)][lane];
                 if (CHK && t == 1) {
                     // residual of u_k on row j-1, from the stencil level 1 reads
                     const int i = j - 1;
