@@ -66,7 +66,13 @@ __device__ __forceinline__ uint32_t level_residual(const float4& up, const float
     return a > b ? a : b;
 }
 
+// Edge kinds of a wavefront band: interior; rows (the band's rows reach the
+// ghost rows -1 or N, its window stays inside the grid); rows and columns (the
+// window reaches past the grid, so the ghost columns -1 and N are re-imposed).
+enum { kEdgeNone = 0, kEdgeRows = 1, kEdgeCols = 2 };
+
 // Re-impose the ghost ring on a computed row i of any level >= 1.
+template <int EK>
 __device__ __forceinline__ void impose_ring(float4& v, int i, int N, const TBLane& L) {
     if (i == -1) {
         v.x = L.in[0] ? kTop : 0.0f;
@@ -75,12 +81,65 @@ __device__ __forceinline__ void impose_ring(float4& v, int i, int N, const TBLan
         v.w = L.in[3] ? kTop : 0.0f;
     } else if (i == N) {
         v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    } else if (i >= 0 && i < N) {
+    } else if (EK == kEdgeCols && i >= 0 && i < N) {
         if (!L.in[0]) v.x = 0.0f;
         if (!L.in[1]) v.y = 0.0f;
         if (!L.in[2]) v.z = 0.0f;
         if (!L.in[3]) v.w = 0.0f;
     }
+}
+
+// Column strips of the wavefront windows (window = 256 columns from X, core =
+// the columns [x0, x1) it stores).  General layout: cores of Wout = 256 - 2Dp
+// columns from column 0, each window Dp wider on both sides, so the first and
+// last windows reach past the grid and re-impose the ghost columns every level.
+// Aligned layout (N a multiple of 4 and N >= 256): the first window starts at
+// column 0 and the last ends at column N - 1, so no window reaches past the
+// grid -- the west neighbour of lane 0 and the east neighbour of lane 63, which
+// the DPP shifts fill with 0, are then exactly the ghost columns.  Cores
+// [0, 256 - Dp), then Wout wide, and the last window's [.., N); at N = 256 one
+// window is the grid.
+struct TBStrip {
+    int X, x0, x1;
+};
+
+__host__ __device__ inline bool tb_aligned(int N) { return N % 4 == 0 && N >= 256; }
+
+__host__ __device__ inline int tb_strip_count(int N, int Dp) {
+    const int Wout = 256 - 2 * Dp;
+    if (!tb_aligned(N)) return (N + Wout - 1) / Wout;
+    if (N == 256) return 1;
+    const int rest = N - 2 * (256 - Dp);
+    return 2 + (rest > 0 ? (rest + Wout - 1) / Wout : 0);
+}
+
+__host__ __device__ inline TBStrip tb_strip(int N, int Dp, int s, int strips) {
+    const int Wout = 256 - 2 * Dp;
+    const int F = 256 - Dp;
+    TBStrip t;
+    if (!tb_aligned(N)) {
+        t.x0 = s * Wout;
+        t.x1 = t.x0 + Wout < N ? t.x0 + Wout : N;
+        t.X = t.x0 - Dp;
+    } else if (N == 256) {
+        t.X = 0;
+        t.x0 = 0;
+        t.x1 = 256;
+    } else if (s == 0) {
+        t.X = 0;
+        t.x0 = 0;
+        t.x1 = F;
+    } else {
+        t.x0 = F + (s - 1) * Wout;
+        if (s == strips - 1) {  // right-aligned; x0 >= N - 256 + Dp by the strip count
+            t.X = N - 256;
+            t.x1 = N;
+        } else {
+            t.X = t.x0 - Dp;
+            t.x1 = t.x0 + Wout;
+        }
+    }
+    return t;
 }
 
 // Row I/O of a wavefront's band, in one of two forms chosen by depth (both
@@ -190,7 +249,7 @@ using TBIO = typename std::conditional<(D >= 5), TBBufferIO, TBGlobalIO>::type;
 // The streaming state of one wavefront: for every level t < D three row
 // registers whose roles rotate (up = row i-1, mid = row i, new = row i+1 of
 // that level, as seen by level t+1), the prefetched next row, the ring slot.
-template <int D, bool CHK, bool EDGE, bool FAST>
+template <int D, bool CHK, int EK, bool FAST>
 struct TBStream {
     TBIO<D> io;
     float r, d, y;
@@ -214,13 +273,15 @@ struct TBStream {
         const int depth = j - j0;  // level t is exact from the (2t)-th row of the band on
         // b of the next level is read one level ahead, so the LDS latency
         // overlaps the current level's arithmetic
+        // (two buffers by level parity, so no copies between them)
         auto slot = [&](int t) { return s - t < 0 ? s - t + R : s - t; };
-        float4 bnext = ring[slot(1)][lane];
+        float4 bq[2];
+        bq[1] = ring[slot(1)][lane];
 #pragma unroll
         for (int t = 1; t <= D; ++t) {
             if (2 * t <= depth) {
-                const float4 bb = bnext;
-                if (t < D) bnext = ring[slot(t + 1)][lane];
+                const float4 bb = bq[t & 1];
+                if (t < D) bq[(t + 1) & 1] = ring[slot(t + 1)][lane];
                 if (CHK && t == 1) {
                     // residual of u_k on row j-1, from the stencil level 1 reads
                     const int i = j - 1;
@@ -230,22 +291,22 @@ struct TBStream {
                     }
                 }
                 float4 v = level_update<FAST>(UP[t - 1], MID[t - 1], NEW[t - 1], bb, r, d, y);
-                if (EDGE) impose_ring(v, j - t, N, L);
+                if (EK != kEdgeNone) impose_ring<EK>(v, j - t, N, L);
                 if (t < D) NEW[t] = v;
                 else out = v;
             }
         }
         const int i = j - D;
-        io.template store<EDGE>(out, i, i >= y0 && i <= last, y0, L);
+        io.template store<EK == kEdgeCols>(out, i, i >= y0 && i <= last, y0, L);
         s = (s + 1 == R) ? 0 : s + 1;
     }
 };
 
-template <int D, bool CHK, bool EDGE, bool FAST>
+template <int D, bool CHK, int EK, bool FAST>
 __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const float* __restrict__ bin,
                                             float* __restrict__ uout, const StepArgs& a, const TBLane& L, int X,
                                             bool lane_loads, int y0, int last, float4 (*ring)[64]) {
-    TBStream<D, CHK, EDGE, FAST> st;
+    TBStream<D, CHK, EK, FAST> st;
     st.N = a.g.N;
     st.r = a.r;
     st.d = a.d;
@@ -289,36 +350,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(tb_waves_per
 void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
                                                float* __restrict__ uout, StepArgs a, int H) {
     constexpr int Dp = (D + 3) & ~3;
-    constexpr int Wout = 256 - 2 * Dp;
     __shared__ float4 ring[D + 1][64];
     if (a.sc->stop) return;  // a previous check already stopped the step
     const int N = a.g.N;
     const int lane = threadIdx.x;
-    const int strips = (N + Wout - 1) / Wout;
+    const int strips = tb_strip_count(N, Dp);
     const int bands = (N + H - 1) / H;
     const int t = xcd_logical_block(blockIdx.x, gridDim.x);
     uint32_t m = 0;
     if (t < strips * bands) {
-        const int x0 = (t % strips) * Wout;  // first output column
-        const int X = x0 - Dp;               // first column of the window
+        const TBStrip sp = tb_strip(N, Dp, t % strips, strips);
+        const int X = sp.X;                  // first column of the window
         const int y0 = (t / strips) * H;
         const int last = (y0 + H < N ? y0 + H : N) - 1;
         TBLane L;
         L.c0 = X + 4 * lane;
-        const bool core_lane = lane >= Dp / 4 && lane < 64 - Dp / 4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             L.in[c] = L.c0 + c >= 0 && L.c0 + c < N;
-            L.core[c] = core_lane && L.in[c];
+            L.core[c] = L.c0 + c >= sp.x0 && L.c0 + c < sp.x1;
         }
         // lanes wholly outside [0, N) would load only zero padding and the zero
         // ghost columns: they skip the loads and keep zeros
         const bool lane_loads = L.c0 < N && L.c0 + 4 > 0;
-        const bool edge = X < 0 || X + 256 > N || y0 - D < 0 || last + D >= N;
-        if (edge)
-            m = tb_band<D, CHK, true, FAST>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
+        const bool cols = X < 0 || X + 256 > N;
+        const bool rows = y0 - D < 0 || last + D >= N;
+        if (cols)
+            m = tb_band<D, CHK, kEdgeCols, FAST>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
+        else if (rows)
+            m = tb_band<D, CHK, kEdgeRows, FAST>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
         else
-            m = tb_band<D, CHK, false, FAST>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
+            m = tb_band<D, CHK, kEdgeNone, FAST>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
     }
     if (CHK) store_block_max<1>(m, a.sc, blockIdx.x);
 }
@@ -366,8 +428,7 @@ int tblock_waves_per_cu(int D, bool fast) {
 // 15% faster at 8192^2 than the one-round height.
 int tblock_rows(int N, int D, int resident_waves) {
     const int Dp = (D + 3) & ~3;
-    const int Wout = 256 - 2 * Dp;
-    const int strips = (N + Wout - 1) / Wout;
+    const int strips = tb_strip_count(N, Dp);
     int bands = resident_waves / strips;
     if (bands < 1) bands = 1;
     int H = (N + bands - 1) / bands;
@@ -377,19 +438,14 @@ int tblock_rows(int N, int D, int resident_waves) {
 
 int64_t tblock_blocks(int N, int D, int H) {
     const int Dp = (D + 3) & ~3;
-    const int Wout = 256 - 2 * Dp;
-    const int64_t tiles = (int64_t)((N + Wout - 1) / Wout) * ((N + H - 1) / H);
+    const int64_t tiles = (int64_t)tb_strip_count(N, Dp) * ((N + H - 1) / H);
     return (tiles + 7) / 8 * 8;
 }
 
 template <int D>
 static hipError_t launch_tb_d(const float* uin, const float* b, float* uout, bool check, const StepArgs& a,
                               int H, hipStream_t s) {
-    constexpr int Dp = (D + 3) & ~3;
-    constexpr int Wout = 256 - 2 * Dp;
-    const int N = a.g.N;
-    const int tiles = ((N + Wout - 1) / Wout) * ((N + H - 1) / H);
-    const int blocks = (tiles + 7) / 8 * 8;
+    const int blocks = (int)tblock_blocks(a.g.N, D, H);
     if (check) {
         if (a.fastdiv)
             hipLaunchKernelGGL((k_tblock<D, true, true>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H);

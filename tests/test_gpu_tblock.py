@@ -31,10 +31,12 @@ def test_every_depth_bitwise(D, N):
 
 
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 9, 15, 63, 64, 65, 127, 129, 224, 240, 248, 249, 255, 256,
-                               257, 481, 513])
+                               257, 260, 264, 481, 496, 500, 504, 508, 512, 513, 740, 744, 1000])
 @pytest.mark.parametrize("D", [2, 4, 8])
 def test_small_and_ragged_grids_bitwise(N, D):
-    """Window widths 248/240 (D 2-4 / 8) and band heights meet N at every offset."""
+    """Window widths 248/240 (D 2-4 / 8) and band heights meet N at every offset;
+    N a multiple of 4 from 256 on takes the aligned strip layout (first window
+    at column 0, last window ending at column N-1), the others the general one."""
     r = 1.0
     say("tblock small", N, D)
     s = workloads.point_source(N, r)
