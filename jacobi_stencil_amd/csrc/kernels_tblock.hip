@@ -422,13 +422,17 @@ int tblock_waves_per_cu(int D, bool fast) {
 // leave most SIMDs idle at the end -- but at least 16 rows, so the D rows the
 // band re-reads above and below stay a moderate fraction.  Resident waves are
 // counted at most four per SIMD: more only shortens the bands (more re-read
-// rows) without adding issue slots the arithmetic needs.  Depths up to 4 are
-// bound by memory bandwidth rather than by the arithmetic: there bands of at
-// most 64 rows (more wavefronts than one round, each shorter) measured up to
-// 15% faster at 8192^2 than the one-round height.
+// rows) without adding issue slots the arithmetic needs.  For D = 5..8 (bound
+// by the arithmetic, four wavefronts per SIMD) the round is sized for three:
+// the longer bands recompute fewer rows, which at 8192^2 outweighed the fourth
+// wavefront (D = 8: 202 vs 212 us per launch, D = 6: 195 vs 207 us); deeper
+// pipelines fit only two per SIMD and need both.  Depths up to 4 are bound by
+// memory bandwidth: there bands of at most 64 rows (more wavefronts than one
+// round, each shorter) measured up to 15% faster than the one-round height.
 int tblock_rows(int N, int D, int resident_waves) {
     const int Dp = (D + 3) & ~3;
     const int strips = tb_strip_count(N, Dp);
+    if (D >= 5 && D <= 8) resident_waves = resident_waves * 3 / 4;
     int bands = resident_waves / strips;
     if (bands < 1) bands = 1;
     int H = (N + bands - 1) / bands;
