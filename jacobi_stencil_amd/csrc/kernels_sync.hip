@@ -148,16 +148,25 @@ hipError_t launch_reduce(int64_t npart, bool norm, const StepArgs& a, hipStream_
 // ------------------------------------------------------------ sync sweep
 
 constexpr int kSyncWaves = 4;
-constexpr int kSyncRows = 16;  // rows per wavefront
+
+// Rows per wavefront: 16 (each row of u read about once, the two rows shared
+// with the neighbouring bands excepted), or 4 on grids too small to give the
+// GPU a few thousand 16-row wavefronts -- there a sweep is bound by the
+// latency of a wavefront's row stream, not by bandwidth.
+static int sync_rows(int N) {
+    const int64_t waves16 = (int64_t)((N + 255) / 256) * ((N + 15) / 16);
+    return waves16 >= 1024 ? 16 : 4;
+}
 
 struct SyncTiles {
-    int tiles_x, tiles_y, blocks;
+    int rows, tiles_x, tiles_y, blocks;
 };
 
 static SyncTiles sync_tiles(int N) {
     SyncTiles t;
+    t.rows = sync_rows(N);
     t.tiles_x = (N + 255) / 256;
-    t.tiles_y = (N + kSyncWaves * kSyncRows - 1) / (kSyncWaves * kSyncRows);
+    t.tiles_y = (N + kSyncWaves * t.rows - 1) / (kSyncWaves * t.rows);
     t.blocks = (t.tiles_x * t.tiles_y + 7) / 8 * 8;
     return t;
 }
@@ -205,12 +214,11 @@ __device__ __forceinline__ float4 rhs4(const float* pb, const float* ps) {
 // and `sin` the source s, and b = u^n + s is formed per point -- the unfused
 // baseline of page "stencil-jacobian.vercel.app", section 02 (16 bytes per
 // point per sweep instead of 12); the results are identical.
-template <bool CHECK, bool RESID_ONLY, bool FAST, bool UNF>
+template <bool CHECK, bool RESID_ONLY, bool FAST, bool UNF, int H>
 __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, const float* __restrict__ bin,
                                               const float* __restrict__ sin, float* __restrict__ uout, StepArgs a) {
     constexpr bool SWEEP = !RESID_ONLY;
     constexpr bool CHK = CHECK || RESID_ONLY;
-    constexpr int H = kSyncRows;
     if (a.sc->stop) return;  // a previous check already stopped the step
     const Geom g = a.g;
     const int N = g.N, P = g.P;
@@ -300,19 +308,19 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
 
 int64_t sync_blocks(int N) { return sync_tiles(N).blocks; }
 
-template <bool UNF>
+template <bool UNF, int H>
 static void launch_sync_t(const float* uin, const float* b, const float* src, float* uout, bool check,
                           const StepArgs& a, dim3 grid, dim3 block, hipStream_t s) {
     if (check) {
         if (a.fastdiv)
-            hipLaunchKernelGGL((k_sync<true, false, true, UNF>), grid, block, 0, s, uin, b, src, uout, a);
+            hipLaunchKernelGGL((k_sync<true, false, true, UNF, H>), grid, block, 0, s, uin, b, src, uout, a);
         else
-            hipLaunchKernelGGL((k_sync<true, false, false, UNF>), grid, block, 0, s, uin, b, src, uout, a);
+            hipLaunchKernelGGL((k_sync<true, false, false, UNF, H>), grid, block, 0, s, uin, b, src, uout, a);
     } else {
         if (a.fastdiv)
-            hipLaunchKernelGGL((k_sync<false, false, true, UNF>), grid, block, 0, s, uin, b, src, uout, a);
+            hipLaunchKernelGGL((k_sync<false, false, true, UNF, H>), grid, block, 0, s, uin, b, src, uout, a);
         else
-            hipLaunchKernelGGL((k_sync<false, false, false, UNF>), grid, block, 0, s, uin, b, src, uout, a);
+            hipLaunchKernelGGL((k_sync<false, false, false, UNF, H>), grid, block, 0, s, uin, b, src, uout, a);
     }
 }
 
@@ -320,21 +328,37 @@ hipError_t launch_sync(const float* uin, const float* b, const float* src, float
                        const StepArgs& a, hipStream_t s) {
     SyncTiles t = sync_tiles(a.g.N);
     const dim3 grid(t.blocks), block(64 * kSyncWaves);
-    if (src)
-        launch_sync_t<true>(uin, b, src, uout, check, a, grid, block, s);
-    else
-        launch_sync_t<false>(uin, b, nullptr, uout, check, a, grid, block, s);
+    if (t.rows == 16) {
+        if (src)
+            launch_sync_t<true, 16>(uin, b, src, uout, check, a, grid, block, s);
+        else
+            launch_sync_t<false, 16>(uin, b, nullptr, uout, check, a, grid, block, s);
+    } else {
+        if (src)
+            launch_sync_t<true, 4>(uin, b, src, uout, check, a, grid, block, s);
+        else
+            launch_sync_t<false, 4>(uin, b, nullptr, uout, check, a, grid, block, s);
+    }
     return hipGetLastError();
+}
+
+template <int H>
+static void launch_residual_t(const float* u, const float* b, const float* src, const StepArgs& a, dim3 grid,
+                              hipStream_t s) {
+    const dim3 block(64 * kSyncWaves);
+    if (src)
+        hipLaunchKernelGGL((k_sync<false, true, false, true, H>), grid, block, 0, s, u, b, src, (float*)nullptr, a);
+    else
+        hipLaunchKernelGGL((k_sync<false, true, false, false, H>), grid, block, 0, s, u, b, (const float*)nullptr,
+                           (float*)nullptr, a);
 }
 
 hipError_t launch_residual(const float* u, const float* b, const float* src, const StepArgs& a, hipStream_t s) {
     SyncTiles t = sync_tiles(a.g.N);
-    if (src)
-        hipLaunchKernelGGL((k_sync<false, true, false, true>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, u, b,
-                           src, (float*)nullptr, a);
+    if (t.rows == 16)
+        launch_residual_t<16>(u, b, src, a, dim3(t.blocks), s);
     else
-        hipLaunchKernelGGL((k_sync<false, true, false, false>), dim3(t.blocks), dim3(64 * kSyncWaves), 0, s, u, b,
-                           (const float*)nullptr, (float*)nullptr, a);
+        launch_residual_t<4>(u, b, src, a, dim3(t.blocks), s);
     return hipGetLastError();
 }
 

@@ -419,8 +419,10 @@ int tblock_waves_per_cu(int D, bool fast) {
 
 // Band height: the shortest bands (most parallelism) such that the whole grid
 // is one round of resident wavefronts -- a second, partly filled round would
-// leave most SIMDs idle at the end -- but at least 16 rows, so the D rows the
-// band re-reads above and below stay a moderate fraction.  Resident waves are
+// leave most SIMDs idle at the end -- but at least 4 rows.  Small grids (N up to
+// ~2048) hit the floor: there a launch is bound by the latency of a band's
+// row pipeline, and short bands (many wavefronts, more recomputed rows) beat
+// long ones (N = 256, D = 8: 6.2 ms per ten steps at 4 rows, 10.0 at 16).  Resident waves are
 // counted at most four per SIMD: more only shortens the bands (more re-read
 // rows) without adding issue slots the arithmetic needs.  For D = 5..8 (bound
 // by the arithmetic, four wavefronts per SIMD) the round is sized for three:
@@ -437,7 +439,7 @@ int tblock_rows(int N, int D, int resident_waves) {
     if (bands < 1) bands = 1;
     int H = (N + bands - 1) / bands;
     if (D <= 4 && H > 64) H = 64;
-    return H < 16 ? 16 : H;
+    return H < 4 ? 4 : H;
 }
 
 int64_t tblock_blocks(int N, int D, int H) {
