@@ -191,19 +191,32 @@ __device__ __forceinline__ uint32_t async_strip(const float* __restrict__ uin, c
             if ((!EDGE || Y + i < N) && in_col) m = m > v ? m : v;
         }
     }
-    for (int s = 0; s < D; ++s) {
-        float prev = top;  // old value of the row above
+    // One sweep from `src` into `dst` (rows past the grid and lanes past
+    // column N-1 keep their values).  Two sweeps per trip with the roles
+    // swapped, so no register is copied back between sweeps.
+    auto sweep = [&](const float (&src)[TY], float (&dst)[TY]) {
 #pragma unroll
         for (int i = 0; i < TY; ++i) {
-            const float c = cur[i];
+            const float c = src[i];
             const float l = from_left(c), rr = from_right(c);
             const float W = west ? hx[i] : l;
             const float E = east ? hx[i] : rr;
-            const float Sn = i + 1 < TY ? cur[i + 1] : bot;
-            const float v = jacobi_update<FAST>(E, W, prev, Sn, bb[i], r, d, y);
-            prev = c;
-            if (!EDGE || Y + i < N) cur[i] = in_col ? v : c;
+            const float Nn = i > 0 ? src[i - 1] : top;
+            const float Sn = i + 1 < TY ? src[i + 1] : bot;
+            const float v = jacobi_update<FAST>(E, W, Nn, Sn, bb[i], r, d, y);
+            dst[i] = ((!EDGE || Y + i < N) && in_col) ? v : c;
         }
+    };
+    float alt[TY];
+    int s = 0;
+    for (; s + 2 <= D; s += 2) {
+        sweep(cur, alt);
+        sweep(alt, cur);
+    }
+    if (s < D) {
+        sweep(cur, alt);
+#pragma unroll
+        for (int i = 0; i < TY; ++i) cur[i] = alt[i];
     }
     float* po = uout + g.origin + (int64_t)Y * P + col;
 #pragma unroll
