@@ -155,6 +155,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // Lane i receives lane i-1's value (lane 0 receives 0): DPP wave_shr:1.
+// A shift reads the source lane only if that lane is active (else 0): call it
+// with every lane active -- `c ? x : from_left(v)` evaluates the shift only in
+// the lanes without c; compute the shift first, then select.
 __device__ __forceinline__ float from_left(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xF, 0xF, true));
 }

@@ -14,7 +14,12 @@
 // points; points near a tile edge then see fresher neighbours.  o = 0 is the
 // plain block-async launch; o >= D - 1 reproduces D synchronous sweeps.
 //
-// Here: tiles of tile_x columns by tile_y rows start at unknown (0, 0), the
+// Three forms, chosen by tile shape (results identical): four columns per lane
+// in 256-column strips (widths dividing 256, heights 4 and 8), one column per
+// lane in 64-column strips (widths dividing 64, heights up to 32), and the LDS
+// form below for every other shape and for overlap.
+//
+// LDS form: tiles of tile_x columns by tile_y rows start at unknown (0, 0), the
 // last ones in each direction clipped to the grid.  The halo comes from the
 // iterate the launch reads (u_k, ping-pong between launches), so a launch is a
 // deterministic function of u_k and the result does not depend on scheduling.
@@ -243,7 +248,179 @@ __global__ __launch_bounds__(256) void k_async_wave(const float* __restrict__ ui
     if (CHK) store_block_max<4>(m, a.sc, blockIdx.x);
 }
 
+// ---- four-column register form: tile widths 4..256 dividing 256, heights 4 and 8, no overlap
+//
+// As above, but each lane holds 4 adjacent columns (one 16-byte load per row)
+// and a wavefront owns a strip of 256 columns.  The west and east neighbours of
+// a lane's inner columns are in its own registers; only column 0 of the lane
+// takes a DPP shift from the lane to its left and column 3 one from the lane to
+// its right, and since tile widths are multiples of 4, a tile edge can only fall
+// on those two columns -- so the frozen halo is kept, and selected, for them
+// alone.  Per point-sweep: the 8 instructions of the update plus half a shift
+// and half a select, against 2 and 2 in the one-column form.
+constexpr int kWideStrip = 256;
+
+bool async_wide_form(int tx, int ty, int o) {
+    return o == 0 && tx % 4 == 0 && kWideStrip % tx == 0 && (ty == 4 || ty == 8);
+}
+
+template <int TY, bool EDGE, bool CHK, bool FAST>
+__device__ __forceinline__ uint32_t async_wide_strip(const float* __restrict__ uin, const float* __restrict__ bin,
+                                                     float* __restrict__ uout, const StepArgs& a, int tx, int D,
+                                                     int X, int Y) {
+    const Geom g = a.g;
+    const int N = g.N, P = g.P;
+    const int lane = threadIdx.x & 63;
+    const int c0 = X + 4 * lane;
+    // columns of this lane that are unknowns (EDGE strips only reach past N)
+    const bool in0 = !EDGE || c0 < N, in1 = !EDGE || c0 + 1 < N, in2 = !EDGE || c0 + 2 < N,
+               in3 = !EDGE || c0 + 3 < N;
+    const bool west = (c0 % tx) == 0, east = ((c0 + 4) % tx) == 0;
+    const float r = a.r, d = a.d, y = a.y;
+    const float* pu = uin + g.origin + (int64_t)Y * P + c0;
+    const float* pb = bin + g.origin + (int64_t)Y * P + c0;
+    float4 cur[TY], alt[TY], bb[TY];
+    float hw[TY], he[TY];  // frozen halo of column 0 (west) and column 3 (east) on tile edges
+    const float4 top = ld4(pu - P);
+    const float4 bot = ld4(pu + (int64_t)TY * P);
+#pragma unroll
+    for (int i = 0; i < TY; ++i) {
+        cur[i] = ld4(pu + (int64_t)i * P);
+        bb[i] = ld4(pb + (int64_t)i * P);
+    }
+    // the columns just outside the strip, lane i holding row i
+    const int er = lane < TY ? lane : 0;
+    const float wcol = uin[g.origin + (int64_t)(Y + er) * P + X - 1];
+    const float ecol = uin[g.origin + (int64_t)(Y + er) * P + X + kWideStrip];
+#pragma unroll
+    for (int i = 0; i < TY; ++i) {
+        const float l = from_left(cur[i].w), rr = from_right(cur[i].x);
+        const float ws = __shfl(wcol, i, 64), es = __shfl(ecol, i, 64);
+        hw[i] = lane == 0 ? ws : l;
+        he[i] = lane == 63 ? es : rr;
+    }
+    uint32_t m = 0;
+    if (CHK) {
+        // residual of u_k on the strip's points
+#pragma unroll
+        for (int i = 0; i < TY; ++i) {
+            const float4 c = cur[i];
+            const float4 n = i > 0 ? cur[i - 1] : top;
+            const float4 sth = i + 1 < TY ? cur[i + 1] : bot;
+            const float l = from_left(c.w), rr = from_right(c.x);  // in every lane, then select
+            const float W = west ? hw[i] : l;
+            const float E = east ? he[i] : rr;
+            uint32_t v0 = residual_bits(c.x, c.y, W, n.x, sth.x, bb[i].x, r);
+            uint32_t v1 = residual_bits(c.y, c.z, c.x, n.y, sth.y, bb[i].y, r);
+            uint32_t v2 = residual_bits(c.z, c.w, c.y, n.z, sth.z, bb[i].z, r);
+            uint32_t v3 = residual_bits(c.w, E, c.z, n.w, sth.w, bb[i].w, r);
+            if (EDGE) {
+                const bool row = Y + i < N;
+                v0 = (row && in0) ? v0 : 0u;
+                v1 = (row && in1) ? v1 : 0u;
+                v2 = (row && in2) ? v2 : 0u;
+                v3 = (row && in3) ? v3 : 0u;
+            }
+            const uint32_t va = v0 > v1 ? v0 : v1, vb = v2 > v3 ? v2 : v3;
+            const uint32_t v = va > vb ? va : vb;
+            m = m > v ? m : v;
+        }
+    }
+    // One sweep from `src` into `dst`; rows past the grid and columns past N-1
+    // keep their values.  Two sweeps per trip with the roles swapped.
+    auto sweep = [&](const float4 (&src)[TY], float4 (&dst)[TY]) {
+#pragma unroll
+        for (int i = 0; i < TY; ++i) {
+            const float4 c = src[i];
+            const float4 n = i > 0 ? src[i - 1] : top;
+            const float4 sth = i + 1 < TY ? src[i + 1] : bot;
+            const float l = from_left(c.w), rr = from_right(c.x);  // in every lane, then select
+            const float W = west ? hw[i] : l;
+            const float E = east ? he[i] : rr;
+            float4 v;
+            v.x = jacobi_update<FAST>(c.y, W, n.x, sth.x, bb[i].x, r, d, y);
+            v.y = jacobi_update<FAST>(c.z, c.x, n.y, sth.y, bb[i].y, r, d, y);
+            v.z = jacobi_update<FAST>(c.w, c.y, n.z, sth.z, bb[i].z, r, d, y);
+            v.w = jacobi_update<FAST>(E, c.z, n.w, sth.w, bb[i].w, r, d, y);
+            if (EDGE) {
+                const bool row = Y + i < N;
+                v.x = (row && in0) ? v.x : c.x;
+                v.y = (row && in1) ? v.y : c.y;
+                v.z = (row && in2) ? v.z : c.z;
+                v.w = (row && in3) ? v.w : c.w;
+            }
+            dst[i] = v;
+        }
+    };
+    int s = 0;
+    for (; s + 2 <= D; s += 2) {
+        sweep(cur, alt);
+        sweep(alt, cur);
+    }
+    if (s < D) {
+        sweep(cur, alt);
+#pragma unroll
+        for (int i = 0; i < TY; ++i) cur[i] = alt[i];
+    }
+    float* po = uout + g.origin + (int64_t)Y * P + c0;
+#pragma unroll
+    for (int i = 0; i < TY; ++i) {
+        if (!EDGE) {
+            st4_nt(po + (int64_t)i * P, cur[i]);
+        } else if (Y + i < N) {
+            float* q = po + (int64_t)i * P;
+            if (in3) {
+                st4_nt(q, cur[i]);
+            } else {
+                if (in0) q[0] = cur[i].x;
+                if (in1) q[1] = cur[i].y;
+                if (in2) q[2] = cur[i].z;
+            }
+        }
+    }
+    return m;
+}
+
+template <int TY, bool CHK, bool FAST>
+__global__ __launch_bounds__(256) void k_async_wide(const float* __restrict__ uin, const float* __restrict__ bin,
+                                                    float* __restrict__ uout, StepArgs a, int tx, int D) {
+    if (a.sc->stop) return;  // a previous check already stopped the step
+    const int N = a.g.N;
+    const int sx = (N + kWideStrip - 1) / kWideStrip, sy = (N + TY - 1) / TY;
+    const int wid = xcd_logical_block(blockIdx.x, gridDim.x) * 4 + (int)(threadIdx.x >> 6);
+    uint32_t m = 0;
+    if (wid < sx * sy) {
+        const int X = (wid % sx) * kWideStrip, Y = (wid / sx) * TY;
+        if (X + kWideStrip <= N && Y + TY <= N)
+            m = async_wide_strip<TY, false, CHK, FAST>(uin, bin, uout, a, tx, D, X, Y);
+        else
+            m = async_wide_strip<TY, true, CHK, FAST>(uin, bin, uout, a, tx, D, X, Y);
+    }
+    if (CHK) store_block_max<4>(m, a.sc, blockIdx.x);
+}
+
+template <int TY>
+static void launch_wide_t(const float* uin, const float* b, float* uout, int tx, int D, bool check,
+                          const StepArgs& a, dim3 grid, hipStream_t s) {
+    const dim3 block(256);
+    if (check) {
+        if (a.fastdiv)
+            hipLaunchKernelGGL((k_async_wide<TY, true, true>), grid, block, 0, s, uin, b, uout, a, tx, D);
+        else
+            hipLaunchKernelGGL((k_async_wide<TY, true, false>), grid, block, 0, s, uin, b, uout, a, tx, D);
+    } else {
+        if (a.fastdiv)
+            hipLaunchKernelGGL((k_async_wide<TY, false, true>), grid, block, 0, s, uin, b, uout, a, tx, D);
+        else
+            hipLaunchKernelGGL((k_async_wide<TY, false, false>), grid, block, 0, s, uin, b, uout, a, tx, D);
+    }
+}
+
 int64_t async_blocks(int N, int tx, int ty, int o) {
+    if (async_wide_form(tx, ty, o)) {
+        const int64_t strips = (int64_t)((N + kWideStrip - 1) / kWideStrip) * ((N + ty - 1) / ty);
+        return ((strips + 3) / 4 + 7) / 8 * 8;
+    }
     if (async_wave_form(tx, ty, o)) {
         const int64_t strips = (int64_t)((N + kWaveStrip - 1) / kWaveStrip) * ((N + ty - 1) / ty);
         return ((strips + 3) / 4 + 7) / 8 * 8;
@@ -276,6 +453,14 @@ hipError_t launch_async(const float* uin, const float* b, float* uout, int tx, i
         return hipErrorInvalidValue;
     const int64_t blocks = async_blocks(a.g.N, tx, ty, o);
     if (blocks > (int64_t)0x7fffffff) return hipErrorInvalidValue;
+    if (async_wide_form(tx, ty, o)) {
+        const dim3 grid((unsigned)blocks);
+        switch (ty) {
+            case 4: launch_wide_t<4>(uin, b, uout, tx, D, check, a, grid, s); break;
+            default: launch_wide_t<8>(uin, b, uout, tx, D, check, a, grid, s); break;
+        }
+        return hipGetLastError();
+    }
     if (async_wave_form(tx, ty, o)) {
         const dim3 grid((unsigned)blocks);
         switch (ty) {

@@ -39,12 +39,15 @@ def test_tiles_and_depths_bitwise(tile, D):
     assert_same(lib_solve(N, r, s, 2, opts(kernel=AS, D=D, tile_x=tx, tile_y=ty)), ref, f"{tile} D={D}")
 
 
-@pytest.mark.parametrize("tile", [(8, 4), (16, 8), (64, 4), (8, 32), (32, 32), (16, 16)])
-@pytest.mark.parametrize("N", [64, 150, 200])
+@pytest.mark.parametrize("tile", [(8, 4), (16, 8), (64, 4), (8, 32), (32, 32), (16, 16), (4, 8), (4, 4), (128, 4),
+                                  (256, 8), (12, 8)])
+@pytest.mark.parametrize("N", [64, 150, 200, 300])
 def test_register_form_shapes_bitwise(tile, N):
-    """Tile widths dividing 64 and heights 4..32 run in registers, one 64-column
-    strip per wavefront holding several tiles: edges inside a strip, clipped
-    tiles and strips past the grid must all match the tile model."""
+    """Register forms: widths dividing 256 (multiples of 4) with heights 4 and 8
+    run four columns per lane in 256-column strips; other widths dividing 64
+    with heights up to 32 one column per lane in 64-column strips.  Tile edges
+    inside a strip, clipped tiles and strips past the grid must all match the
+    tile model; (12, 8) takes the LDS form."""
     r = 10.0
     say("async register form", tile, N)
     s = workloads.gaussian_source(N, r)
