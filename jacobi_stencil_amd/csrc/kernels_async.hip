@@ -183,23 +183,11 @@ __device__ __forceinline__ uint32_t async_strip(const float* __restrict__ uin, c
         hx[i] = west ? (lane == 0 ? ws : l) : (east ? (lane == 63 ? es : rr) : 0.0f);
     }
     uint32_t m = 0;
-    if (CHK) {
-        // residual of u_k on the strip's points
-#pragma unroll
-        for (int i = 0; i < TY; ++i) {
-            const float l = from_left(cur[i]), rr = from_right(cur[i]);
-            const float W = west ? hx[i] : l;
-            const float E = east ? hx[i] : rr;
-            const float Nn = i > 0 ? cur[i - 1] : top;
-            const float Sn = i + 1 < TY ? cur[i + 1] : bot;
-            const uint32_t v = residual_bits(cur[i], E, W, Nn, Sn, bb[i], r);
-            if ((!EDGE || Y + i < N) && in_col) m = m > v ? m : v;
-        }
-    }
     // One sweep from `src` into `dst` (rows past the grid and lanes past
-    // column N-1 keep their values).  Two sweeps per trip with the roles
+    // column N-1 keep their values); with `check` the residual of u_k is taken
+    // from the same stencil on the way.  Two sweeps per trip with the roles
     // swapped, so no register is copied back between sweeps.
-    auto sweep = [&](const float (&src)[TY], float (&dst)[TY]) {
+    auto sweep = [&](const float (&src)[TY], float (&dst)[TY], bool check) {
 #pragma unroll
         for (int i = 0; i < TY; ++i) {
             const float c = src[i];
@@ -208,18 +196,23 @@ __device__ __forceinline__ uint32_t async_strip(const float* __restrict__ uin, c
             const float E = east ? hx[i] : rr;
             const float Nn = i > 0 ? src[i - 1] : top;
             const float Sn = i + 1 < TY ? src[i + 1] : bot;
+            const bool live = (!EDGE || Y + i < N) && in_col;
+            if (CHK && check) {
+                const uint32_t e = residual_bits(c, E, W, Nn, Sn, bb[i], r);
+                if (live) m = m > e ? m : e;
+            }
             const float v = jacobi_update<FAST>(E, W, Nn, Sn, bb[i], r, d, y);
-            dst[i] = ((!EDGE || Y + i < N) && in_col) ? v : c;
+            dst[i] = live ? v : c;
         }
     };
     float alt[TY];
     int s = 0;
     for (; s + 2 <= D; s += 2) {
-        sweep(cur, alt);
-        sweep(alt, cur);
+        sweep(cur, alt, s == 0);
+        sweep(alt, cur, false);
     }
     if (s < D) {
-        sweep(cur, alt);
+        sweep(cur, alt, s == 0);
 #pragma unroll
         for (int i = 0; i < TY; ++i) cur[i] = alt[i];
     }
@@ -300,65 +293,58 @@ __device__ __forceinline__ uint32_t async_wide_strip(const float* __restrict__ u
         he[i] = lane == 63 ? es : rr;
     }
     uint32_t m = 0;
-    if (CHK) {
-        // residual of u_k on the strip's points
-#pragma unroll
-        for (int i = 0; i < TY; ++i) {
-            const float4 c = cur[i];
-            const float4 n = i > 0 ? cur[i - 1] : top;
-            const float4 sth = i + 1 < TY ? cur[i + 1] : bot;
-            const float l = from_left(c.w), rr = from_right(c.x);  // in every lane, then select
-            const float W = west ? hw[i] : l;
-            const float E = east ? he[i] : rr;
-            uint32_t v0 = residual_bits(c.x, c.y, W, n.x, sth.x, bb[i].x, r);
-            uint32_t v1 = residual_bits(c.y, c.z, c.x, n.y, sth.y, bb[i].y, r);
-            uint32_t v2 = residual_bits(c.z, c.w, c.y, n.z, sth.z, bb[i].z, r);
-            uint32_t v3 = residual_bits(c.w, E, c.z, n.w, sth.w, bb[i].w, r);
-            if (EDGE) {
-                const bool row = Y + i < N;
-                v0 = (row && in0) ? v0 : 0u;
-                v1 = (row && in1) ? v1 : 0u;
-                v2 = (row && in2) ? v2 : 0u;
-                v3 = (row && in3) ? v3 : 0u;
-            }
-            const uint32_t va = v0 > v1 ? v0 : v1, vb = v2 > v3 ? v2 : v3;
-            const uint32_t v = va > vb ? va : vb;
-            m = m > v ? m : v;
+    // Residual of u_k on row i, from the stencil the first sweep reads anyway.
+    auto residual_row = [&](int i, const float4& c, const float4& n, const float4& sth, float W, float E) {
+        uint32_t v0 = residual_bits(c.x, c.y, W, n.x, sth.x, bb[i].x, r);
+        uint32_t v1 = residual_bits(c.y, c.z, c.x, n.y, sth.y, bb[i].y, r);
+        uint32_t v2 = residual_bits(c.z, c.w, c.y, n.z, sth.z, bb[i].z, r);
+        uint32_t v3 = residual_bits(c.w, E, c.z, n.w, sth.w, bb[i].w, r);
+        if (EDGE) {
+            const bool row = Y + i < N;
+            v0 = (row && in0) ? v0 : 0u;
+            v1 = (row && in1) ? v1 : 0u;
+            v2 = (row && in2) ? v2 : 0u;
+            v3 = (row && in3) ? v3 : 0u;
         }
-    }
-    // One sweep from `src` into `dst`; rows past the grid and columns past N-1
-    // keep their values.  Two sweeps per trip with the roles swapped.
-    auto sweep = [&](const float4 (&src)[TY], float4 (&dst)[TY]) {
-#pragma unroll
-        for (int i = 0; i < TY; ++i) {
-            const float4 c = src[i];
-            const float4 n = i > 0 ? src[i - 1] : top;
-            const float4 sth = i + 1 < TY ? src[i + 1] : bot;
-            const float l = from_left(c.w), rr = from_right(c.x);  // in every lane, then select
-            const float W = west ? hw[i] : l;
-            const float E = east ? he[i] : rr;
-            float4 v;
-            v.x = jacobi_update<FAST>(c.y, W, n.x, sth.x, bb[i].x, r, d, y);
-            v.y = jacobi_update<FAST>(c.z, c.x, n.y, sth.y, bb[i].y, r, d, y);
-            v.z = jacobi_update<FAST>(c.w, c.y, n.z, sth.z, bb[i].z, r, d, y);
-            v.w = jacobi_update<FAST>(E, c.z, n.w, sth.w, bb[i].w, r, d, y);
-            if (EDGE) {
-                const bool row = Y + i < N;
-                v.x = (row && in0) ? v.x : c.x;
-                v.y = (row && in1) ? v.y : c.y;
-                v.z = (row && in2) ? v.z : c.z;
-                v.w = (row && in3) ? v.w : c.w;
-            }
-            dst[i] = v;
+        const uint32_t va = v0 > v1 ? v0 : v1, vb = v2 > v3 ? v2 : v3;
+        const uint32_t v = va > vb ? va : vb;
+        m = m > v ? m : v;
+    };
+    // One row i of a sweep: the new values from the old rows n (above), c
+    // and sth (below); rows past the grid and columns past N-1 keep theirs.
+    // With `check` the row's residual of u_k is taken on the way.
+    auto update_row = [&](int i, const float4& c, const float4& n, const float4& sth, bool check) {
+        const float l = from_left(c.w), rr = from_right(c.x);  // in every lane, then select
+        const float W = west ? hw[i] : l;
+        const float E = east ? he[i] : rr;
+        if (CHK && check) residual_row(i, c, n, sth, W, E);
+        float4 v;
+        v.x = jacobi_update<FAST>(c.y, W, n.x, sth.x, bb[i].x, r, d, y);
+        v.y = jacobi_update<FAST>(c.z, c.x, n.y, sth.y, bb[i].y, r, d, y);
+        v.z = jacobi_update<FAST>(c.w, c.y, n.z, sth.z, bb[i].z, r, d, y);
+        v.w = jacobi_update<FAST>(E, c.z, n.w, sth.w, bb[i].w, r, d, y);
+        if (EDGE) {
+            const bool row = Y + i < N;
+            v.x = (row && in0) ? v.x : c.x;
+            v.y = (row && in1) ? v.y : c.y;
+            v.z = (row && in2) ? v.z : c.z;
+            v.w = (row && in3) ? v.w : c.w;
         }
+        return v;
+    };
+    // two sweeps per trip with the register sets swapped
+    auto sweep = [&](const float4 (&src)[TY], float4 (&dst)[TY], bool check) {
+#pragma unroll
+        for (int i = 0; i < TY; ++i)
+            dst[i] = update_row(i, src[i], i > 0 ? src[i - 1] : top, i + 1 < TY ? src[i + 1] : bot, check);
     };
     int s = 0;
     for (; s + 2 <= D; s += 2) {
-        sweep(cur, alt);
-        sweep(alt, cur);
+        sweep(cur, alt, s == 0);
+        sweep(alt, cur, false);
     }
     if (s < D) {
-        sweep(cur, alt);
+        sweep(cur, alt, s == 0);
 #pragma unroll
         for (int i = 0; i < TY; ++i) cur[i] = alt[i];
     }
