@@ -253,8 +253,17 @@ __global__ __launch_bounds__(256) void k_async_wave(const float* __restrict__ ui
 // and half a select, against 2 and 2 in the one-column form.
 constexpr int kWideStrip = 256;
 
-bool async_wide_form(int tx, int ty, int o) {
-    return o == 0 && tx % 4 == 0 && kWideStrip % tx == 0 && (ty == 4 || ty == 8);
+// A four-column grid has a quarter of the one-column form's wavefronts; it is
+// used only where that still leaves two per SIMD (MI355X has 1024): on smaller
+// grids the idle SIMDs cost more than the instructions it saves (N = 1024,
+// D4 at 32 x 8 tiles: 7.2 ms per ten steps against 6.4 in the one-column form;
+// N = 2048: 10.3 against 12.4).
+constexpr int64_t kWideMinWaves = 2048;
+
+bool async_wide_form(int N, int tx, int ty, int o) {
+    if (!(o == 0 && tx % 4 == 0 && kWideStrip % tx == 0 && (ty == 4 || ty == 8))) return false;
+    const int64_t waves = (int64_t)((N + kWideStrip - 1) / kWideStrip) * ((N + ty - 1) / ty);
+    return waves >= kWideMinWaves;
 }
 
 template <int TY, bool EDGE, bool CHK, bool FAST>
@@ -403,7 +412,7 @@ static void launch_wide_t(const float* uin, const float* b, float* uout, int tx,
 }
 
 int64_t async_blocks(int N, int tx, int ty, int o) {
-    if (async_wide_form(tx, ty, o)) {
+    if (async_wide_form(N, tx, ty, o)) {
         const int64_t strips = (int64_t)((N + kWideStrip - 1) / kWideStrip) * ((N + ty - 1) / ty);
         return ((strips + 3) / 4 + 7) / 8 * 8;
     }
@@ -439,7 +448,7 @@ hipError_t launch_async(const float* uin, const float* b, float* uout, int tx, i
         return hipErrorInvalidValue;
     const int64_t blocks = async_blocks(a.g.N, tx, ty, o);
     if (blocks > (int64_t)0x7fffffff) return hipErrorInvalidValue;
-    if (async_wide_form(tx, ty, o)) {
+    if (async_wide_form(a.g.N, tx, ty, o)) {
         const dim3 grid((unsigned)blocks);
         switch (ty) {
             case 4: launch_wide_t<4>(uin, b, uout, tx, D, check, a, grid, s); break;

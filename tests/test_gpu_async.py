@@ -43,17 +43,35 @@ def test_tiles_and_depths_bitwise(tile, D):
                                   (256, 8), (12, 8)])
 @pytest.mark.parametrize("N", [64, 150, 200, 300])
 def test_register_form_shapes_bitwise(tile, N):
-    """Register forms: widths dividing 256 (multiples of 4) with heights 4 and 8
-    run four columns per lane in 256-column strips; other widths dividing 64
-    with heights up to 32 one column per lane in 64-column strips.  Tile edges
-    inside a strip, clipped tiles and strips past the grid must all match the
-    tile model; (12, 8) takes the LDS form."""
+    """Register forms on small grids: widths dividing 64 with heights up to 32
+    run one column per lane in 64-column strips, other shapes the LDS form (the
+    four-column form needs a larger grid, tested below).  Tile edges inside a
+    strip, clipped tiles and strips past the grid must all match the tile
+    model."""
     r = 10.0
     say("async register form", tile, N)
     s = workloads.gaussian_source(N, r)
     for D in (1, 3, 8):
         ref = oracle.solve(N, r, s, steps=1, M=8, mode=oracle.ASYNC, D=D, tx=tile[0], ty=tile[1])
         got = lib_solve(N, r, s, 1, opts(kernel=jac.JAC_ASYNC, D=D, tile_x=tile[0], tile_y=tile[1]))
+        assert_same(got, ref, f"{tile} N={N} D={D}")
+
+
+@pytest.mark.parametrize("tile,N", [((32, 8), 2048), ((8, 8), 2100), ((4, 4), 1540), ((256, 4), 1540),
+                                    ((128, 8), 2050)])
+def test_four_column_form_bitwise(tile, N):
+    """Widths dividing 256 (multiples of 4) with heights 4 and 8 run four
+    columns per lane in 256-column strips once the grid gives that form two
+    wavefronts per SIMD (N >= 2048 at height 8, >= 1449 at height 4): the same
+    tile model, bit for bit, on whole and ragged grids.  Two checked intervals
+    (the sweep cap ends the step at its check, on both sides)."""
+    r = 10.0
+    say("async four-column form", tile, N)
+    s = workloads.gaussian_source(N, r)
+    for D in (3, 8):
+        cap = 2 * interval(D)
+        ref = oracle.solve(N, r, s, steps=1, M=8, mode=oracle.ASYNC, D=D, tx=tile[0], ty=tile[1], max_sweeps=cap)
+        got = lib_solve(N, r, s, 1, opts(kernel=AS, D=D, tile_x=tile[0], tile_y=tile[1], max_sweeps=cap))
         assert_same(got, ref, f"{tile} N={N} D={D}")
 
 
