@@ -60,6 +60,9 @@ def parse():
                     help="turn two rocprofv3 --pmc counter files into HBM bytes per launch, then exit")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
+    ap.add_argument("--counters-from", nargs="+", metavar="CSV",
+                    help="summarise rocprofv3 --pmc counter files for the --kernel class "
+                         "(median per real launch of its most-called kernel), then exit")
     return ap.parse_args()
 
 
@@ -140,12 +143,41 @@ def traffic_from(fetch_csv, write_csv, probe_mib, out_path, key):
     n, fb, wb, kname = rows[0]
     res = {"kernel": kname, "dispatches": n, "fetch_bytes": fb, "write_bytes": wb,
            "bytes_per_launch": fb + wb, "fetch_scale": f_scale, "write_scale": w_scale,
-           "source_sha256": _kernel_source_hash()}
+           "source_sha256": _kernel_source_hash(key.split(":")[1])}
     table = json.load(open(out_path)) if os.path.exists(out_path) else {}
     table[key] = res
     with open(out_path, "w") as f:
         json.dump(table, f, indent=1)
     print(json.dumps({key: res}, indent=1))
+
+
+def counters_from(paths, kclass):
+    """Median per launch of every counter or derived metric in rocprofv3 --pmc
+    files, for the most-called kernel of a class.  Launches queued after a
+    stopping check return at once; only launches that ran at least half as
+    long as the longest one are counted."""
+    import csv
+    import statistics
+
+    pattern = {"tblock": "k_tblock", "async": "k_async", "sync": "k_sync<"}[kclass]
+    per = {}  # kernel -> dispatch -> (duration ns, {counter: value})
+    for path in paths:
+        for row in csv.DictReader(open(path)):
+            k = row["Kernel_Name"]
+            if pattern not in k:
+                continue
+            key = (path, row["Dispatch_Id"])
+            dur = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+            d = per.setdefault(k, {}).setdefault(key, [dur, {}])
+            d[1][row["Counter_Name"]] = d[1].get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    kname = max(per, key=lambda k: len(per[k]))
+    ds = list(per[kname].values())
+    longest = max(dur for dur, _ in ds)
+    real = [c for dur, c in ds if dur >= longest / 2]
+    names = sorted({n for c in real for n in c})
+    res = {"kernel": kname, "launches": len(real),
+           "median": {n: statistics.median(c[n] for c in real if n in c) for n in names}}
+    print(json.dumps(res, indent=1))
 
 
 def main():
@@ -155,15 +187,19 @@ def main():
               "(multi-GPU sharding is not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-
-    import jacobi_stencil_amd as jac
-    import workloads
-
+    # counter-file summaries need no device
+    if args.counters_from:
+        counters_from(args.counters_from, args.kernel)
+        return
     if args.traffic_from:
         traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_mib, args.traffic,
                      f"{args.config}:{args.kernel}:D{1 if args.kernel == 'sync' else args.D}")
         return
+
+    import torch
+
+    import jacobi_stencil_amd as jac
+    import workloads
     cfg = dict(workloads.CONFIGS[args.config], name=args.config)
     N, r = cfg["N"], cfg["r"]
     if isinstance(r, tuple):
@@ -201,7 +237,14 @@ def main():
 
     ms_per_step = elapsed / args.steps * 1e3
     total_sweeps = int(sweeps.sum())
-    value = N * N * total_sweeps / (ms_per_step / 1e3) / 1e9
+    exact_sweeps = total_sweeps
+    if args.kernel == "async":
+        # the value counts the exact method's sweeps: take them from an untimed
+        # temporally blocked solve of the same workload (bitwise the synchronous one)
+        sol.reset()
+        _, ex, _ = sol.solve(nsteps, jac.jac_opts_default(kernel=KERNELS["tblock"], D=8))
+        exact_sweeps = int(ex.sum())
+    value = N * N * exact_sweeps / (ms_per_step / 1e3) / 1e9
     D = 1 if args.kernel == "sync" else args.D
     bytes_per_launch = BYTES_PER_POINT_PASS * N * N
     achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
@@ -209,7 +252,7 @@ def main():
     if os.path.exists(args.traffic):
         t = json.load(open(args.traffic))
         key = f"{args.config}:{args.kernel}:D{D}"
-        if key in t and t[key].get("source_sha256") == _kernel_source_hash():
+        if key in t and t[key].get("source_sha256") == _kernel_source_hash(args.kernel):
             traffic = t[key]["bytes_per_launch"]
 
     common = {"traffic": traffic, "kernel_class": cls, "launches": k_n, "timed_launches": k_timed,
@@ -245,6 +288,8 @@ def main():
         "time_to_solution_ms": round(ms_per_step, 3),
         "sweeps_per_solve": total_sweeps,
         "sweeps_per_step": sweeps.tolist(),
+        "exact_sweeps_per_solve": exact_sweeps,
+        "extra_sweep_ratio": round(total_sweeps / exact_sweeps, 4),
         "pct_hbm_roofline_model": round(100.0 * value * BYTES_PER_POINT_PASS / D / HBM_PEAK_GBS, 2),
         "stream_probe_gbs": probe,
         "roofline": roofline,
@@ -255,14 +300,15 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def _kernel_source_hash():
+def _kernel_source_hash(kclass):
+    """Hash of the sources a kernel class is built from: its own file and the
+    shared device header.  Counter figures taken under another hash are stale."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "jacobi_stencil_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in (f"kernels_{kclass.split('_')[0]}.hip", "jacobi_internal.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
 
