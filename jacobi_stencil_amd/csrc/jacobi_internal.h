@@ -276,7 +276,7 @@ size_t persist_out_bytes();
 hipError_t launch_async(const float* uin, const float* b, float* uout, int tx, int ty, int D, int o, bool check,
                         const StepArgs& a, hipStream_t s);
 // Automatic band height for a grid of `resident_waves` wavefront slots.
-int tblock_rows(int N, int D, int resident_waves);
+int tblock_rows(int N, int D, int cus, int waves_per_cu);
 int tblock_waves_per_cu(int D, bool fast);
 // One synchronous sweep.  src != NULL: the unfused form, b holds u^n and
 // b = u^n + src is formed per point.

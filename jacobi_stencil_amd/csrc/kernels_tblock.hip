@@ -12,13 +12,14 @@
 // MI355X design (differs from the page's 2-D tile): one wavefront owns a
 // 256-column window (64 lanes x 4 columns, one 16-byte load per row) whose
 // central 256 - 2*Dp columns are its output (Dp = D rounded up to a multiple
-// of 4, so every load stays 16-byte aligned), and streams down a band of H
-// output rows plus D rows above and below.  Time is pipelined along the rows:
-// when row j of u_k arrives, level 1 (u_{k+1}) is computed for row j-1,
-// level 2 for row j-2, ..., level D for row j-D, which is stored.  Each level
+// of 4, so every load stays 16-byte aligned), and streams along a band of H
+// output rows plus D rows above and below (downwards, or for every other band
+// from D = 5 on upwards).  Time is pipelined along the rows: when row j of u_k
+// arrives, level 1 (u_{k+1}) is computed for the row before it, level 2 for
+// the one before that, ..., level D for the row D back, which is stored.  Each level
 // keeps only its last two rows in registers; the west/east neighbours of a
 // lane's 4 columns come from the adjacent lanes by DPP lane shifts; b rows go
-// through a per-wavefront ring in LDS (level t reads b of row j-t).  Only the
+// through a per-wavefront ring in LDS (level t reads b of the row t back).  Only the
 // columns are recomputed redundantly (256 / (256 - 2*Dp)) and the band's D
 // extra rows on each side ((H + 2D) / H); the 2-D tile of the page pays both
 // factors squared.  Values that leave the exact cone (the window's outer
@@ -175,10 +176,9 @@ struct TBGlobalIO {
         lane_loads = loads;
         store_lane = L.core[0];
     }
-    // row j of u_k and b into (nu, nb); rows past j1 are not needed
+    // row j of u_k and b into (nu, nb); rows outside [j0, j1] are not needed
     __device__ __forceinline__ void load(float4& nu, float4& nb, int j, int j0, int j1) {
-        (void)j0;
-        if (lane_loads && j <= j1) {
+        if (lane_loads && j >= j0 && j <= j1) {
             nu = ld4_nt(pu + (int64_t)j * P);
             nb = ld4_nt(pb + (int64_t)j * P);
         }
@@ -200,7 +200,7 @@ struct TBGlobalIO {
 };
 
 struct TBBufferIO {
-    __amdgpu_buffer_rsrc_t ru, rb;  // u_k and b, from row j0 and window column X
+    __amdgpu_buffer_rsrc_t ru, rb;  // u_k and b, from row j0 - 1 and window column X
     __amdgpu_buffer_rsrc_t ro;      // output, from row y0 and window column X
     uint32_t vload;                 // the lane's byte offset in a row; kOOB: lane wholly outside [0, N)
     uint32_t vst4;                  // 16-byte store offset of a lane whose 4 columns are all stored
@@ -211,8 +211,8 @@ struct TBBufferIO {
                                          const TBLane& L, int X, bool loads, int j0, int y0) {
         const int P = a.g.P;
         rowb = (uint32_t)P * 4u;
-        ru = make_rsrc(uin + a.g.origin + (int64_t)j0 * P + X);
-        rb = make_rsrc(bin + a.g.origin + (int64_t)j0 * P + X);
+        ru = make_rsrc(uin + a.g.origin + (int64_t)(j0 - 1) * P + X);
+        rb = make_rsrc(bin + a.g.origin + (int64_t)(j0 - 1) * P + X);
         ro = make_rsrc(uout + a.g.origin + (int64_t)y0 * P + X);
         const uint32_t lb = (uint32_t)(threadIdx.x & 63) * 16u;
         vload = loads ? lb : kOOB;
@@ -221,11 +221,12 @@ struct TBBufferIO {
 #pragma unroll
         for (int c = 0; c < 4; ++c) vst1[c] = (!full && L.core[c]) ? lb + 4u * c : kOOB;
     }
-    // row j of u_k and b into (nu, nb); row j1 + 1 lies inside the padded
+    // row j of u_k and b into (nu, nb); the row one past the band's end
+    // (j0 - 1 or j1 + 1, in the direction of travel) lies inside the padded
     // plane and is loaded and left unused
     __device__ __forceinline__ void load(float4& nu, float4& nb, int j, int j0, int j1) {
         (void)j1;
-        const uint32_t so = (uint32_t)(j - j0) * rowb;
+        const uint32_t so = (uint32_t)(j - j0 + 1) * rowb;
         nu = bld4(ru, vload, so);
         nb = bld4(rb, vload, so);
     }
@@ -247,9 +248,13 @@ template <int D>
 using TBIO = typename std::conditional<(D >= 5), TBBufferIO, TBGlobalIO>::type;
 
 // The streaming state of one wavefront: for every level t < D three row
-// registers whose roles rotate (up = row i-1, mid = row i, new = row i+1 of
-// that level, as seen by level t+1), the prefetched next row, the ring slot.
-template <int D, bool CHK, int EK, bool FAST>
+// registers whose roles rotate (old = the row before, mid, new = the row after,
+// in the direction of travel, as seen by level t+1), the prefetched next row,
+// the ring slot.  DIR = +1 streams the band downwards, -1 upwards; going up,
+// the "before" rows lie below, so the update and the residual are handed the
+// old and new rows as south and north instead of north and south -- every
+// point sees the same neighbours in the same order either way.
+template <int D, bool CHK, int EK, bool FAST, int DIR>
 struct TBStream {
     TBIO<D> io;
     float r, d, y;
@@ -267,10 +272,10 @@ struct TBStream {
         const int lane = threadIdx.x & 63;
         NEW[0] = nu;
         const float4 cb = nb;
-        io.load(nu, nb, j + 1, j0, j1);  // fetch the next row while this one is worked on
+        io.load(nu, nb, j + DIR, j0, j1);  // fetch the next row while this one is worked on
         ring[s][lane] = cb;
         float4 out;
-        const int depth = j - j0;  // level t is exact from the (2t)-th row of the band on
+        const int depth = DIR > 0 ? j - j0 : j1 - j;  // level t is exact from the (2t)-th row streamed on
         // b of the next level is read one level ahead, so the LDS latency
         // overlaps the current level's arithmetic
         // (two buffers by level parity, so no copies between them)
@@ -283,30 +288,32 @@ struct TBStream {
                 const float4 bb = bq[t & 1];
                 if (t < D) bq[(t + 1) & 1] = ring[slot(t + 1)][lane];
                 if (CHK && t == 1) {
-                    // residual of u_k on row j-1, from the stencil level 1 reads
-                    const int i = j - 1;
+                    // residual of u_k on the row level 1 computes, from the stencil it reads
+                    const int i = j - DIR;
                     if (i >= y0 && i <= last) {
-                        const uint32_t v = level_residual(UP[0], MID[0], NEW[0], bb, r, L);
+                        const uint32_t v = DIR > 0 ? level_residual(UP[0], MID[0], NEW[0], bb, r, L)
+                                                   : level_residual(NEW[0], MID[0], UP[0], bb, r, L);
                         m = m > v ? m : v;
                     }
                 }
-                float4 v = level_update<FAST>(UP[t - 1], MID[t - 1], NEW[t - 1], bb, r, d, y);
-                if (EK != kEdgeNone) impose_ring<EK>(v, j - t, N, L);
+                float4 v = DIR > 0 ? level_update<FAST>(UP[t - 1], MID[t - 1], NEW[t - 1], bb, r, d, y)
+                                   : level_update<FAST>(NEW[t - 1], MID[t - 1], UP[t - 1], bb, r, d, y);
+                if (EK != kEdgeNone) impose_ring<EK>(v, j - DIR * t, N, L);
                 if (t < D) NEW[t] = v;
                 else out = v;
             }
         }
-        const int i = j - D;
+        const int i = j - DIR * D;
         io.template store<EK == kEdgeCols>(out, i, i >= y0 && i <= last, y0, L);
         s = (s + 1 == R) ? 0 : s + 1;
     }
 };
 
-template <int D, bool CHK, int EK, bool FAST>
+template <int D, bool CHK, int EK, bool FAST, int DIR>
 __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const float* __restrict__ bin,
                                             float* __restrict__ uout, const StepArgs& a, const TBLane& L, int X,
                                             bool lane_loads, int y0, int last, float4 (*ring)[64]) {
-    TBStream<D, CHK, EK, FAST> st;
+    TBStream<D, CHK, EK, FAST, DIR> st;
     st.N = a.g.N;
     st.r = a.r;
     st.d = a.d;
@@ -323,27 +330,49 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     st.nu = zero;
     st.nb = zero;
-    st.io.load(st.nu, st.nb, st.j0, st.j0, st.j1);
+    const int first = DIR > 0 ? st.j0 : st.j1;
+    st.io.load(st.nu, st.nb, first, st.j0, st.j1);
     float4 A[D], B[D], C[D];
 #pragma unroll
     for (int t = 0; t < D; ++t) { A[t] = zero; B[t] = zero; C[t] = zero; }
     // Three rows per trip, the level registers rotating A -> B -> C.  While
     // the pipeline fills (the first 2D rows of the band) a row computes only
     // the levels that are already exact.
-    for (int j = st.j0; j <= st.j1; j += 3) {
-        st.row(j, A, B, C);
-        if (j + 1 > st.j1) break;
-        st.row(j + 1, B, C, A);
-        if (j + 2 > st.j1) break;
-        st.row(j + 2, C, A, B);
+    if constexpr (DIR > 0) {
+        for (int j = st.j0; j <= st.j1; j += 3) {
+            st.row(j, A, B, C);
+            if (j + 1 > st.j1) break;
+            st.row(j + 1, B, C, A);
+            if (j + 2 > st.j1) break;
+            st.row(j + 2, C, A, B);
+        }
+    } else {
+        for (int j = st.j1; j >= st.j0; j -= 3) {
+            st.row(j, A, B, C);
+            if (j - 1 < st.j0) break;
+            st.row(j - 1, B, C, A);
+            if (j - 2 < st.j0) break;
+            st.row(j - 2, C, A, B);
+        }
     }
     return st.m;
 }
 
-// Register budget: D <= 8 fits 128 VGPRs, four wavefronts per SIMD; deeper
-// pipelines get two.
+template <int D, bool CHK, bool FAST, int DIR>
+__device__ __forceinline__ uint32_t tb_band_kind(const float* __restrict__ uin, const float* __restrict__ bin,
+                                                 float* __restrict__ uout, const StepArgs& a, const TBLane& L, int X,
+                                                 bool lane_loads, int y0, int last, float4 (*ring)[64], bool cols,
+                                                 bool rows) {
+    if (cols) return tb_band<D, CHK, kEdgeCols, FAST, DIR>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
+    if (rows) return tb_band<D, CHK, kEdgeRows, FAST, DIR>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
+    return tb_band<D, CHK, kEdgeNone, FAST, DIR>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
+}
+
+// Register budget per depth: up to 4, four wavefronts per SIMD (128 VGPRs);
+// 5..8 three (168 VGPRs: the launch sizes its bands for three wavefronts per
+// SIMD anyway); deeper pipelines two.
 template <int D>
-constexpr int tb_waves_per_simd() { return D <= 8 ? 4 : 2; }
+constexpr int tb_waves_per_simd() { return D <= 4 ? 4 : (D <= 8 ? 3 : 2); }
 
 template <int D, bool CHK, bool FAST>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(tb_waves_per_simd<D>())))
@@ -375,12 +404,22 @@ void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
         const bool lane_loads = L.c0 < N && L.c0 + 4 > 0;
         const bool cols = X < 0 || X + 256 > N;
         const bool rows = y0 - D < 0 || last + D >= N;
-        if (cols)
-            m = tb_band<D, CHK, kEdgeCols, FAST>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
-        else if (rows)
-            m = tb_band<D, CHK, kEdgeRows, FAST>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
-        else
-            m = tb_band<D, CHK, kEdgeNone, FAST>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
+        // From D = 5 odd bands stream upwards: two vertically adjacent bands
+        // (behind the same L2) then read the rows they share -- each one's
+        // halo is the other's edge -- at the same time, both at their start
+        // or both at their end, instead of a whole band apart (D = 8 at
+        // 8192^2: 635 -> 584 MB fetched per launch, 202 -> 197 us; D = 6: 200
+        // -> 189 us).  The shallow depths keep one direction: their loads are
+        // nontemporal, not kept in L2 for the neighbour, and alternating ran
+        // slower (D = 4: 169 -> 182 us, D = 2: 169 -> 177 us).
+        if constexpr (D >= 5) {
+            if ((t / strips) & 1)
+                m = tb_band_kind<D, CHK, FAST, -1>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring, cols, rows);
+            else
+                m = tb_band_kind<D, CHK, FAST, 1>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring, cols, rows);
+        } else {
+            m = tb_band_kind<D, CHK, FAST, 1>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring, cols, rows);
+        }
     }
     if (CHK) store_block_max<1>(m, a.sc, blockIdx.x);
 }
@@ -425,16 +464,18 @@ int tblock_waves_per_cu(int D, bool fast) {
 // long ones (N = 256, D = 8: 6.2 ms per ten steps at 4 rows, 10.0 at 16).  Resident waves are
 // counted at most four per SIMD: more only shortens the bands (more re-read
 // rows) without adding issue slots the arithmetic needs.  For D = 5..8 (bound
-// by the arithmetic, four wavefronts per SIMD) the round is sized for three:
-// the longer bands recompute fewer rows, which at 8192^2 outweighed the fourth
-// wavefront (D = 8: 202 vs 212 us per launch, D = 6: 195 vs 207 us); deeper
-// pipelines fit only two per SIMD and need both.  Depths up to 4 are bound by
+// by the arithmetic) the round is sized for three per SIMD: the longer bands
+// recompute fewer rows, which at 8192^2 outweighed a fourth wavefront (D = 8:
+// 202 vs 212 us per launch, D = 6: 195 vs 207 us); deeper pipelines fit only
+// two per SIMD and need both.  Depths up to 4 are bound by
 // memory bandwidth: there bands of at most 64 rows (more wavefronts than one
 // round, each shorter) measured up to 15% faster than the one-round height.
-int tblock_rows(int N, int D, int resident_waves) {
+int tblock_rows(int N, int D, int cus, int waves_per_cu) {
     const int Dp = (D + 3) & ~3;
     const int strips = tb_strip_count(N, Dp);
-    if (D >= 5 && D <= 8) resident_waves = resident_waves * 3 / 4;
+    int w = waves_per_cu < 16 ? waves_per_cu : 16;
+    if (D >= 5 && D <= 8 && w > 12) w = 12;
+    const int resident_waves = cus * w;
     int bands = resident_waves / strips;
     if (bands < 1) bands = 1;
     int H = (N + bands - 1) / bands;

@@ -296,7 +296,7 @@ int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, i
         }
         case JAC_TBLOCK: {
             if (o->band_rows == 0 && c->tb_rows[m] == 0)
-                c->tb_rows[m] = tblock_rows(c->N, m, c->cus * std::min(16, tblock_waves_per_cu(m, c->fastdiv != 0)));
+                c->tb_rows[m] = tblock_rows(c->N, m, c->cus, tblock_waves_per_cu(m, c->fastdiv != 0));
             const int H = o->band_rows > 0 ? o->band_rows : c->tb_rows[m];
             npart = tblock_blocks(c->N, m, H);
             if (check && npart > c->npart_cap)
