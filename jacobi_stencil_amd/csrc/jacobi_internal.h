@@ -260,7 +260,9 @@ hipError_t launch_probe(float* c, const float* a, const float* b, int64_t n, int
                         int blocks, hipStream_t s);
 // Blocks each launch will use (for the host's partial-slot check).
 int64_t rhs_blocks(int N);
-int64_t sync_blocks(int N);
+int64_t sync_blocks(int N, int rows);
+// Rows per wavefront of the synchronous sweep on a device with `cus` CUs.
+int sync_rows_for(int N, int cus);
 int64_t tblock_blocks(int N, int D, int H);
 int64_t async_blocks(int N, int tx, int ty, int o);
 // The whole solve of nsteps steps in one cooperative kernel (see
@@ -275,14 +277,16 @@ size_t persist_out_bytes();
 // frozen one-cell halo around that, D in-tile sweeps.
 hipError_t launch_async(const float* uin, const float* b, float* uout, int tx, int ty, int D, int o, bool check,
                         const StepArgs& a, hipStream_t s);
-// Automatic band height for a grid of `resident_waves` wavefront slots.
+// Automatic band height on `cus` CUs that each hold `waves_per_cu` wavefronts
+// of this depth.
 int tblock_rows(int N, int D, int cus, int waves_per_cu);
 int tblock_waves_per_cu(int D, bool fast);
 // One synchronous sweep.  src != NULL: the unfused form, b holds u^n and
 // b = u^n + src is formed per point.
-hipError_t launch_sync(const float* uin, const float* b, const float* src, float* uout, bool check,
+hipError_t launch_sync(const float* uin, const float* b, const float* src, float* uout, bool check, int rows,
                        const StepArgs& a, hipStream_t s);
-hipError_t launch_residual(const float* u, const float* b, const float* src, const StepArgs& a, hipStream_t s);
+hipError_t launch_residual(const float* u, const float* b, const float* src, int rows, const StepArgs& a,
+                           hipStream_t s);
 // D sweeps (1..16) in one pass; H = output rows per wavefront band (>= 1).
 hipError_t launch_tblock(const float* uin, const float* b, float* uout, int D, bool check, const StepArgs& a,
                          int H, hipStream_t s);

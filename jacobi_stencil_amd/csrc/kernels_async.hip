@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kAsyncThreads) void k_async(const float* __restrict
         for (int s = 0; s < D; ++s) {
 #pragma unroll
             for (int q = 0; q < kAsyncPerThread; ++q) {
-                if (q < nq && threadIdx.x + q * kAsyncThreads < npts) {
+                if (q < nq && (int)threadIdx.x + q * kAsyncThreads < npts) {
                     const int c = cl[q];
                     nxt[c] = jacobi_update<FAST>(cur[c + 1], cur[c - 1], cur[c - lp], cur[c + lp], bb[q], r, d, y);
                 }

@@ -149,22 +149,13 @@ hipError_t launch_reduce(int64_t npart, bool norm, const StepArgs& a, hipStream_
 
 constexpr int kSyncWaves = 4;
 
-// Rows per wavefront: 16 (each row of u read about once, the two rows shared
-// with the neighbouring bands excepted), or 4 on grids too small to give the
-// GPU a few thousand 16-row wavefronts -- there a sweep is bound by the
-// latency of a wavefront's row stream, not by bandwidth.
-static int sync_rows(int N) {
-    const int64_t waves16 = (int64_t)((N + 255) / 256) * ((N + 15) / 16);
-    return waves16 >= 1024 ? 16 : 4;
-}
-
 struct SyncTiles {
     int rows, tiles_x, tiles_y, blocks;
 };
 
-static SyncTiles sync_tiles(int N) {
+static SyncTiles sync_tiles(int N, int rows) {
     SyncTiles t;
-    t.rows = sync_rows(N);
+    t.rows = rows;
     t.tiles_x = (N + 255) / 256;
     t.tiles_y = (N + kSyncWaves * t.rows - 1) / (kSyncWaves * t.rows);
     t.blocks = (t.tiles_x * t.tiles_y + 7) / 8 * 8;
@@ -248,19 +239,20 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
             const float eedge = uin[g.origin + (int64_t)(row0 + erow) * P + wcol + 256];
             float4 up = ld4(pu - P);
             float4 mid = ld4_nt(pu);
-            // rows in groups of four: the loads of a group are all in flight
-            // before its first row is computed
+            // rows in groups of G (up to 8): the loads of a group are all in
+            // flight before its first row is computed
+            constexpr int G = H < 8 ? H : 8;
 #pragma unroll
-            for (int i0 = 0; i0 < H; i0 += 4) {
-                float4 dn[4], bb[4];
+            for (int i0 = 0; i0 < H; i0 += G) {
+                float4 dn[G], bb[G];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
+                for (int k = 0; k < G; ++k) {
                     const int i = i0 + k;
                     dn[k] = (i == H - 1) ? ld4(pu + (int64_t)(i + 1) * P) : ld4_nt(pu + (int64_t)(i + 1) * P);
                     bb[k] = rhs4<UNF, true>(pb + (int64_t)i * P, UNF ? ps + (int64_t)i * P : nullptr);
                 }
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
+                for (int k = 0; k < G; ++k) {
                     const int i = i0 + k;
                     float wl = from_left(mid.w);
                     float er = from_right(mid.x);
@@ -306,7 +298,29 @@ __global__ __launch_bounds__(256) void k_sync(const float* __restrict__ uin, con
     if (CHK) store_block_max<kSyncWaves>(m, a.sc, blockIdx.x);
 }
 
-int64_t sync_blocks(int N) { return sync_tiles(N).blocks; }
+int64_t sync_blocks(int N, int rows) { return sync_tiles(N, rows).blocks; }
+
+// Rows per wavefront.  16 by default (each row of u read about once, the two
+// rows shared with the neighbouring bands excepted), or 4 on grids too small to
+// give the GPU a thousand 16-row wavefronts -- there a sweep is bound by the
+// latency of a wavefront's row stream, not by bandwidth.  64 when those longer
+// bands make one balanced round: the same number of workgroups on every CU, at
+// least four (one wavefront per SIMD each) and no more than fit at once.  Then
+// fewer shared rows are re-read and more loads are in flight per wavefront
+// (N = 8192: 140 us per sweep against 148 at 16 rows); otherwise the longer
+// bands lose to their uneven last round (N = 6144 to 16384: 2-13 % slower).
+// At most 64: a wavefront preloads its two edge columns one row per lane.
+int sync_rows_for(int N, int cus) {
+    const int64_t strips = (N + 255) / 256;
+    const int64_t blocks64 = sync_blocks(N, 64);
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_sync<true, false, true, false, 64>, 64 * kSyncWaves,
+                                                     0) != hipSuccess)
+        per_cu = 0;
+    if (cus > 0 && blocks64 % cus == 0 && blocks64 / cus >= 4 && blocks64 / cus <= per_cu) return 64;
+    if (strips * ((N + 15) / 16) >= 1024) return 16;
+    return 4;
+}
 
 template <bool UNF, int H>
 static void launch_sync_t(const float* uin, const float* b, const float* src, float* uout, bool check,
@@ -324,11 +338,16 @@ static void launch_sync_t(const float* uin, const float* b, const float* src, fl
     }
 }
 
-hipError_t launch_sync(const float* uin, const float* b, const float* src, float* uout, bool check,
+hipError_t launch_sync(const float* uin, const float* b, const float* src, float* uout, bool check, int rows,
                        const StepArgs& a, hipStream_t s) {
-    SyncTiles t = sync_tiles(a.g.N);
+    SyncTiles t = sync_tiles(a.g.N, rows);
     const dim3 grid(t.blocks), block(64 * kSyncWaves);
-    if (t.rows == 16) {
+    if (t.rows == 64) {
+        if (src)
+            launch_sync_t<true, 64>(uin, b, src, uout, check, a, grid, block, s);
+        else
+            launch_sync_t<false, 64>(uin, b, nullptr, uout, check, a, grid, block, s);
+    } else if (t.rows == 16) {
         if (src)
             launch_sync_t<true, 16>(uin, b, src, uout, check, a, grid, block, s);
         else
@@ -353,9 +372,12 @@ static void launch_residual_t(const float* u, const float* b, const float* src, 
                            (float*)nullptr, a);
 }
 
-hipError_t launch_residual(const float* u, const float* b, const float* src, const StepArgs& a, hipStream_t s) {
-    SyncTiles t = sync_tiles(a.g.N);
-    if (t.rows == 16)
+hipError_t launch_residual(const float* u, const float* b, const float* src, int rows, const StepArgs& a,
+                           hipStream_t s) {
+    SyncTiles t = sync_tiles(a.g.N, rows);
+    if (t.rows == 64)
+        launch_residual_t<64>(u, b, src, a, dim3(t.blocks), s);
+    else if (t.rows == 16)
         launch_residual_t<16>(u, b, src, a, dim3(t.blocks), s);
     else
         launch_residual_t<4>(u, b, src, a, dim3(t.blocks), s);

@@ -90,6 +90,7 @@ struct jac_ctx {
     hipGraphExec_t g_group[2];  // one checking interval, by start buffer
     int g_flips_first, g_flips_group;  // buffer parity change across each graph
     int tb_rows[kMaxTBlockD + 1];  // automatic band height per depth (0: not yet computed)
+    int sync_rows;                 // rows per wavefront of the synchronous sweep
     Geom g;
     hipStream_t stream;
     float* u[2];
@@ -287,11 +288,11 @@ int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, i
         case JAC_SYNC:
         case JAC_SYNC_UNFUSED: {
             (void)m;
-            npart = sync_blocks(c->N);
+            npart = sync_blocks(c->N, c->sync_rows);
             if (check && npart > c->npart_cap) return fail(JAC_EDEVICE, "sync grid exceeds partial slots");
             const float* src = o->kernel == JAC_SYNC_UNFUSED ? c->s : nullptr;
             st = timed(c, check ? KC_SYNC_CHECK : KC_SYNC,
-                       [&] { return launch_sync(in, c->b, src, out, check, a, c->stream); });
+                       [&] { return launch_sync(in, c->b, src, out, check, c->sync_rows, a, c->stream); });
             break;
         }
         case JAC_TBLOCK: {
@@ -355,9 +356,9 @@ int enqueue_residual(jac_ctx* c, const jac_opts* o, int buf, int slot) {
     a.slot = slot;
     const float* in = c->u[buf];
     const float* src = o->kernel == JAC_SYNC_UNFUSED ? c->s : nullptr;
-    int st = timed(c, KC_RESID, [&] { return launch_residual(in, c->b, src, a, c->stream); });
+    int st = timed(c, KC_RESID, [&] { return launch_residual(in, c->b, src, c->sync_rows, a, c->stream); });
     if (st) return st;
-    return enqueue_check_reduce(c, sync_blocks(c->N), o->tol, slot);
+    return enqueue_check_reduce(c, sync_blocks(c->N, c->sync_rows), o->tol, slot);
 }
 
 uint32_t read_mail(const volatile uint32_t* p) { return *p; }
@@ -793,6 +794,7 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
         }
     }
     c->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+    c->sync_rows = sync_rows_for(N, c->cus);
     c->pout = nullptr;
     c->pout_cap = 0;
     c->cap_stream = nullptr;

@@ -92,6 +92,19 @@ def test_large_config_against_stored_oracle_hashes(name):
         sol.close()
 
 
+@pytest.mark.parametrize("checks", [jac.JAC_CHECKS_OVERLAPPED, jac.JAC_CHECKS_BLOCKING])
+def test_long_band_form_on_ragged_grid_bitwise(checks):
+    """N = 8190 gives 64-row wavefront bands on a 256-CU GPU (32 x 32
+    workgroups: one balanced round), with a ragged last band and strip; two
+    checked intervals, overlapped checks fused into the sweep or blocking ones
+    by the residual-only kernel."""
+    N, r = 8190, 10.0
+    say("sync long bands", N, checks)
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=1, M=8, max_sweeps=16)
+    assert_same(lib_solve(N, r, s, 1, opts(max_sweeps=16, checks=checks)), ref, f"N={N} checks={checks}")
+
+
 # ------------------------------------------------------------ driver edges
 
 def test_max_sweeps_gives_noconv_and_keeps_checked_iterate():
