@@ -83,7 +83,9 @@ __host__ __device__ inline uint32_t* scratch_partials(Scratch* sc) {
 // partials is launched with at most this many blocks (checked on the host).
 inline int64_t partial_cap(int N) { return (int64_t)N * N / 64 + 65536; }
 
-// Host-visible results, in pinned host memory the device writes directly.
+// Host-visible results, in coherent pinned host memory that the device writes
+// directly with system-scope stores (not held in its caches), so the host sees
+// them without a system-wide cache flush behind every check.
 constexpr int kRing = 64;   // check results kept in flight
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;  // never a |res| bit pattern (sign bit set)
 struct Mailbox {

@@ -128,14 +128,14 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(int64_t npart, int no
             sc->bA_bits = bm;
             sc->stop = 0u;
             sc->check_seq = 0u;
-            a.mail->bA_bits = bm;
+            __hip_atomic_store(&a.mail->bA_bits, bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         } else {
             const float rho = __uint_as_float(bm) / __uint_as_float(sc->bA_bits);
             sc->stop = (rho >= a.tol) ? 0u : 1u;
             const uint32_t seq = sc->check_seq;
             const int slot = a.slot >= 0 ? a.slot : (int)(seq % (uint32_t)kRing);
             sc->check_seq = seq + 1u;
-            a.mail->R[slot] = bm;
+            __hip_atomic_store(&a.mail->R[slot], bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
 }
