@@ -72,24 +72,28 @@ constexpr uint32_t kBarrierSpins = 10000000u;
 // that outlasts the spin budget sets the error word; every waiter polls it, so
 // all blocks leave.  Returns false when the kernel must stop.  `gen` counts
 // this block's barriers (the host zeroed the flags and the release word).
+// Memory order: one device-scope release per store (each one writes back the
+// XCD's L2, so there is no extra fence beside it), relaxed polls, and one
+// acquire after a wait -- an acquiring poll would invalidate the cache on
+// every spin (N = 256, ten steps: 18.1 -> 15.9 ms for the synchronous sweep,
+// 4.47 -> 4.01 ms for temporal blocking at D = 8).
 __device__ bool grid_barrier(Scratch* sc, uint32_t& gen) {
     __shared__ uint32_t ok;
     const uint32_t next = gen + 1;
     uint32_t* flags = scratch_flags(sc);
-    __syncthreads();
+    __syncthreads();  // the block's writes before thread 0's release below
     if (threadIdx.x == 0) {
-        __threadfence();  // this block's writes before its arrival
         __hip_atomic_store(&flags[(size_t)blockIdx.x * kFlagStride], next, __ATOMIC_RELEASE,
                            __HIP_MEMORY_SCOPE_AGENT);
         ok = 1;
     }
     __syncthreads();
     if (blockIdx.x == 0) {
-        // each thread watches some of the flags
+        // each thread watches some of the flags (relaxed polls, one acquire after)
         uint32_t good = 1;
         for (int i = threadIdx.x; i < (int)gridDim.x && good; i += blockDim.x) {
             uint32_t spins = 0;
-            while (__hip_atomic_load(&flags[(size_t)i * kFlagStride], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
+            while (__hip_atomic_load(&flags[(size_t)i * kFlagStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                    next) {
                 if (__hip_atomic_load(&sc->bar_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
                     ++spins > kBarrierSpins) {
@@ -100,15 +104,14 @@ __device__ bool grid_barrier(Scratch* sc, uint32_t& gen) {
                 __builtin_amdgcn_s_sleep(1);
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (!good) ok = 0;  // any thread that gave up
         __syncthreads();
-        if (threadIdx.x == 0) {
-            __threadfence();
+        if (threadIdx.x == 0)
             __hip_atomic_store(&sc->bar_release, next, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
     } else if (threadIdx.x == 0) {
         uint32_t spins = 0;
-        while (__hip_atomic_load(&sc->bar_release, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < next) {
+        while (__hip_atomic_load(&sc->bar_release, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < next) {
             if (__hip_atomic_load(&sc->bar_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
                 ++spins > kBarrierSpins) {
                 __hip_atomic_store(&sc->bar_error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -117,11 +120,9 @@ __device__ bool grid_barrier(Scratch* sc, uint32_t& gen) {
             }
             __builtin_amdgcn_s_sleep(1);
         }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other blocks' writes after the barrier
     }
-    if (threadIdx.x == 0) {
-        if (__hip_atomic_load(&sc->bar_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) ok = 0;
-        __threadfence();  // the other blocks' writes after the barrier
-    }
+    if (threadIdx.x == 0 && __hip_atomic_load(&sc->bar_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) ok = 0;
     __syncthreads();
     gen = next;
     return ok != 0;
