@@ -209,8 +209,9 @@ int jac_stream_probe(float* c, const float* a, const float* b, size_t n, int kin
 /*
  * Launch timing.  jac_profile(ctx, k) with k > 0 counts every kernel launch of
  * the library by class and brackets every k-th launch of each class with a
- * pair of HIP events on the context's stream (a pair costs about 10 us of
- * dispatch gap, so k = 1 slows small kernels noticeably); k = 0 turns it off.
+ * pair of HIP events on the context's stream (each event holds the next
+ * kernel back by a few microseconds, so k = 1 slows small kernels noticeably);
+ * k = 0 turns it off.
  * Enabling resets the counters.  jac_profile_read returns, for one class, the
  * summed device time of the bracketed launches, the number of launches and
  * the number bracketed.  Classes: 0 right-hand side, 1 sync sweep, 2 sync

@@ -8,9 +8,9 @@
 // How the host keeps the GPU busy across checks: the launches covering sweeps
 // gL+1 .. (g+1)L form "group g".  The first launch of group g >= 1 also
 // measures the residual of u_{gL} (the iterate it reads), so a check costs no
-// extra pass over memory; the last block of that launch writes R to pinned
-// host memory and, if the step must stop, sets a device flag that turns every
-// later launch of the step into an immediate return.  The host enqueues group
+// extra pass over memory; a one-block reduction that follows it writes R to
+// the coherent host mailbox and, if the step must stop, sets a device flag
+// that turns every later launch of the step into an immediate return.  The host enqueues group
 // g+1 before it waits for check g, so the device never idles during the round
 // trip, and a stop at check g leaves u_{gL} untouched in the buffer group g
 // read from (its first launch wrote only the other buffer).
