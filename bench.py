@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--profile-every", type=int, default=16,
                     help="bracket every k-th launch of a class with HIP events (0: none)")
     ap.add_argument("--cpu-steps", type=int, default=10, help="time steps in the CPU sample")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all host cores)")
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="time only the CPU oracle on the workload and print its cpu_baseline object")
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="array size of the bandwidth probe, MiB (0: skip)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -66,10 +69,24 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(cfg, nsteps):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, nsteps, threads=0):
+    """The oracle on the host cores (all of them, or `threads`), timed on the
+    first `nsteps` time steps of the workload."""
     import oracle
     import workloads
 
+    if threads > 0:
+        oracle.set_threads(threads)
     N, r = cfg["N"], cfg["r"]
     s = workloads.source(cfg["source"], N, r)
     t0 = time.perf_counter()
@@ -79,7 +96,8 @@ def cpu_baseline(cfg, nsteps):
     return {"value": N * N * sw / dt / 1e9, "unit": "Gpoint-updates/s", "cores": oracle.get_threads(),
             "kind": "oracle",
             "sample": f"{cfg['name']} time steps 1-{nsteps} of 10 ({sw} sweeps, {dt:.1f} s), "
-                      f"OpenMP over rows, float32"}
+                      f"OpenMP over rows, float32",
+            "host": {"nproc": os.cpu_count(), "cpu": cpu_model()}}
 
 
 def copy_probe(torch, jac, mib):
@@ -187,6 +205,15 @@ def main():
               "(multi-GPU sharding is not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.cpu_only:
+        import workloads
+
+        cfg = dict(workloads.CONFIGS[args.config], name=args.config)
+        if isinstance(cfg["r"], tuple):
+            cfg["r"] = cfg["r"][-1]
+        print(json.dumps({"config": args.config, "cpu_baseline": cpu_baseline(cfg, args.cpu_steps, args.cpu_threads)}),
+              flush=True)
+        return
     # counter-file summaries need no device
     if args.counters_from:
         counters_from(args.counters_from, args.kernel)
@@ -295,7 +322,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_steps)
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_steps, args.cpu_threads)
     sol.close()
     print(json.dumps(line), flush=True)
 

@@ -43,3 +43,17 @@ def test_counters_summary_takes_the_most_called_kernel_and_skips_no_op_launches(
     res = json.loads(capsys.readouterr().out)
     assert res["kernel"] == main_k and res["launches"] == 2
     assert res["median"] == {"A": 15.0, "B": 2.0}
+
+
+def test_cpu_only_times_the_oracle_without_a_device():
+    import json
+
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "C5", "--cpu-only",
+                           "--cpu-threads", "1", "--cpu-steps", "2"], capture_output=True, text=True, timeout=300,
+                          cwd=ROOT)
+    assert proc.returncode == 0, proc.stderr
+    res = json.loads(proc.stdout.strip().splitlines()[-1])
+    cb = res["cpu_baseline"]
+    assert res["config"] == "C5" and cb["kind"] == "oracle" and cb["cores"] == 1
+    assert cb["value"] > 0 and "(488 sweeps" in cb["sample"]  # two steps of C5 at r = 10: 248 + 240
+    assert cb["host"]["nproc"] >= 1
