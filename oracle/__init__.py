@@ -25,6 +25,8 @@ _LIB = os.path.join(_HERE, "libjacobi_oracle.so")
 
 SYNC = 0
 ASYNC = 2
+# negative control: b re-formed from the current iterate before every sweep
+WRONG_B = 3
 # depth controllers for ASYNC (page "stencil-jacobian.vercel.app", section 02)
 STATIC, G_ASC, G_DESC, SCHED = 0, 1, 2, 3
 OK, EINVAL, ENOMEM, ENOCONV, ENAN = 0, -1, -2, -4, -5

@@ -312,7 +312,13 @@ static int clamp_depth(int v, int Dmax) { return v < 1 ? 1 : (v > Dmax ? Dmax : 
  *   mode:    ORC_SYNC  - point Jacobi, a check after every M sweeps;
  *            ORC_ASYNC - block-async launches of min(D, left) sweeps, tiles
  *                        tx x ty widened by o overlap cells; the check
- *                        interval is M, or Dmax when Dmax > M.
+ *                        interval is M, or Dmax when Dmax > M;
+ *            ORC_WRONG_B - the mistake page "stencil-jacobian.vercel.app"
+ *                        section 01 recounts: point Jacobi with b formed
+ *                        from the current iterate before every sweep (and
+ *                        the check on that b) instead of from u^n, which
+ *                        solves the steady-state problem instead (a negative
+ *                        control: its sweep count grows as N^2).
  *   ctrl:    (ORC_ASYNC) how the depth D of each check interval is chosen:
  *            ORC_STATIC D = Dmax throughout; ORC_G_ASC / ORC_G_DESC from the
  *            rho of the previous check (see asc_level / desc_level); ORC_SCHED
@@ -332,9 +338,9 @@ int orc_solve_ex(int N, float r, const float* s, float* u_io, int steps, float t
                  float* R_log, int* d_log, int64_t log_cap, int64_t* log_n) {
     if (N < 1 || steps < 0 || M < 1 || Dmax < 1 || tx < 1 || ty < 1 || o < 0 || max_sweeps < 1)
         return ORC_EINVAL;
-    if (mode != ORC_SYNC && mode != ORC_ASYNC) return ORC_EINVAL;
+    if (mode != ORC_SYNC && mode != ORC_ASYNC && mode != ORC_WRONG_B) return ORC_EINVAL;
     if (ctrl < ORC_STATIC || ctrl > ORC_SCHED || (ctrl == ORC_SCHED && !sched)) return ORC_EINVAL;
-    if (mode == ORC_SYNC && ctrl != ORC_STATIC) return ORC_EINVAL;
+    if (mode != ORC_ASYNC && ctrl != ORC_STATIC) return ORC_EINVAL;
     float d = diag_of(r);
     float* U0 = alloc_padded(N);
     float* U1 = alloc_padded(N);
@@ -366,6 +372,10 @@ int orc_solve_ex(int N, float r, const float* s, float* u_io, int steps, float t
                 if (mode == ORC_SYNC) {
                     sweep_padded(N, r, d, cur, B, nxt);
                     left -= 1;
+                } else if (mode == ORC_WRONG_B) {
+                    rhs_padded(N, cur, s, B);
+                    sweep_padded(N, r, d, cur, B, nxt);
+                    left -= 1;
                 } else {
                     int m = D < left ? D : left;
                     async_launch_padded(N, r, d, cur, B, nxt, tx, ty, m, o);
@@ -374,6 +384,10 @@ int orc_solve_ex(int N, float r, const float* s, float* u_io, int steps, float t
                 float* tmp = cur; cur = nxt; nxt = tmp;
             }
             k += interval;
+            if (mode == ORC_WRONG_B) {
+                rhs_padded(N, cur, s, B);
+                bA = rhs_norm_padded(N, r, B);
+            }
             float R = residual_padded(N, r, cur, B);
             float q = R / bA;
             if (R_log && nlog < log_cap) R_log[nlog] = R;

@@ -13,7 +13,7 @@ extern "C" {
 #endif
 
 enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_ENOMEM = -2, ORC_ENOCONV = -4, ORC_ENAN = -5 };
-enum { ORC_SYNC = 0, ORC_ASYNC = 2 };
+enum { ORC_SYNC = 0, ORC_ASYNC = 2, ORC_WRONG_B = 3 };
 enum { ORC_STATIC = 0, ORC_G_ASC = 1, ORC_G_DESC = 2, ORC_SCHED = 3 };
 
 void  orc_set_threads(int n);

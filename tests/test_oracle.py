@@ -11,6 +11,7 @@ import os
 
 import numpy as np
 import pytest
+from scipy import fft
 
 import workloads
 from tests import matrix_forms as mf
@@ -401,3 +402,63 @@ def test_async_sweep_ratio_near_page(orc):
     d4 = orc.solve(N, r, s, mode=orc.ASYNC, D=4, tx=32, ty=8)
     lo, hi = g["D4_range"]
     assert 0.97 * lo <= d4.total_sweeps / sync <= 1.03 * hi
+
+
+# ------------------------------------------------- the "wrong b" negative control
+
+def _steady_solve(rhs, r):
+    """Float64 solve of r*(4u - sum of neighbours) = rhs (zero outside the grid):
+    the steady-state operator A - I, which the 2-D sine transform diagonalises
+    with eigenvalues 2r(2 - cos(p pi/(N+1)) - cos(q pi/(N+1)))."""
+    N = np.asarray(rhs).shape[0]
+    c = np.cos(np.arange(1, N + 1) * np.pi / (N + 1))
+    lam = 2.0 * float(r) * (2.0 - c[:, None] - c[None, :])
+    return fft.idstn(fft.dstn(np.asarray(rhs, np.float64), type=1, norm="ortho") / lam, type=1, norm="ortho")
+
+
+@pytest.mark.parametrize("N,r", [(24, 10.0), (31, 1.0)])
+def test_wrong_b_converges_to_steady_state(orc, N, r):
+    """Section 01's recounted mistake: b taken from the current iterate instead of
+    u^n makes the iteration converge to the steady-state problem.  The fixed
+    point is the float64 steady state within ||(A - I)^-1|| * residual, and it is
+    far from the backward-Euler solution."""
+    s = workloads.gaussian_source(N, r)
+    w = orc.solve(N, r, s, steps=1, mode=orc.WRONG_B, max_sweeps=10**6)
+    assert w.status == orc.OK and w.rho[0] < 1e-5
+    ss = _steady_solve(mf.boundary_rhs(s, r), r)
+    res = np.abs(mf.boundary_rhs(s, r) - (mf.apply_A(w.u, r) - w.u.astype(np.float64))).max()
+    # (A - I)^-1 is non-negative (an M-matrix inverse), so its inf-norm is max((A - I)^-1 1)
+    inv_norm = float(_steady_solve(np.ones((N, N)), r).max())
+    err = np.abs(w.u - ss).max()
+    assert err <= inv_norm * res * (1 + 1e-6) + 1e-3
+    assert np.abs(w.u - mf.dst_solve(s, r)).max() > 100 * (inv_norm * res + 1e-3)
+
+
+@pytest.mark.parametrize("N", [16, 32, 64])
+def test_wrong_b_contraction_is_quadratic_in_N(orc, N):
+    """Section 01: with the wrong b, the slowest mode contracts per sweep by
+    (1 + 4r cos(pi/(N+1)))/(1+4r), so the sweeps needed grow as N^2; with the
+    right b it is at most 4r cos(pi/(N+1))/(1+4r), independent of N to first
+    order.  The rate is read off the logged residuals (least squares over the
+    later checks) and compared with these closed forms.  The page's own count at
+    N = 512 depends on a check its first solver used that the page does not give
+    (parity unpinned for that figure)."""
+    r, M = 10.0, 8
+    s = workloads.gaussian_source(N, r)
+    h = np.pi / (N + 1)
+
+    def rate(res):
+        R = res.R_log.astype(np.float64)
+        lo, hi = int(0.4 * len(R)), int(0.9 * len(R))
+        assert hi - lo >= 4
+        return np.exp(np.polyfit(np.arange(lo, hi), np.log(R[lo:hi]), 1)[0] / M)
+
+    wrong = orc.solve(N, r, s, steps=1, mode=orc.WRONG_B, M=M, log_cap=100000, max_sweeps=10**7)
+    right = orc.solve(N, r, s, steps=1, M=M, log_cap=100000)
+    assert wrong.status == orc.OK and right.status == orc.OK
+    lam_w = (1 + 4 * r * np.cos(h)) / (1 + 4 * r)
+    lam_r = 4 * r * np.cos(h) / (1 + 4 * r)
+    assert abs((1 - rate(wrong)) / (1 - lam_w) - 1) < 0.03
+    # the right solve stops before its slowest mode dominates: lam_r is a bound
+    assert rate(right) <= lam_r + 1e-3
+    assert wrong.sweeps[0] > 1.5 * right.sweeps[0]
