@@ -218,7 +218,8 @@ int jac_stream_probe(float* c, const float* a, const float* b, size_t n, int kin
  * sweep with check, 3 temporal-blocking launch, 4 block-async launch,
  * 5 residual only, 6 persistent solve, 7 launches issued ahead of a check that
  * stopped the step (they return at once and do no sweep), 8 one-block
- * reductions of a check or of ||b_A||.
+ * reductions of a check or of ||b_A||, 9 the first temporal-blocking launch of
+ * a step when it also forms b (launch driver, overlapped checks).
  */
 int jac_profile(jac_t ctx, int every);
 int jac_profile_read(jac_t ctx, int kclass, double* ms_timed, int64_t* launches, int64_t* timed_launches);

@@ -290,6 +290,11 @@ hipError_t launch_sync(const float* uin, const float* b, const float* src, float
 hipError_t launch_residual(const float* u, const float* b, const float* src, int rows, const StepArgs& a,
                            hipStream_t s);
 // D sweeps (1..16) in one pass; H = output rows per wavefront band (>= 1).
+// The first launch of a step that also forms b = u^n + s from u and src (the
+// constant-divisor quotient only), stores b and leaves per-block maxima of
+// |b_A| in the partial slots.
+hipError_t launch_tblock_rhs(const float* u, const float* src, float* b, float* uout, int D, const StepArgs& a,
+                             int H, hipStream_t s);
 hipError_t launch_tblock(const float* uin, const float* b, float* uout, int D, bool check, const StepArgs& a,
                          int H, hipStream_t s);
 

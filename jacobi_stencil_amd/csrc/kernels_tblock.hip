@@ -26,6 +26,11 @@
 // columns, the first rows of each level) are computed but never stored and
 // never feed a stored value.
 //
+// The first launch of a time step may also form the right-hand side (RHS): it
+// reads s where the others read b, takes b = u^n + s for every row it streams
+// (one addition, as the separate right-hand-side pass does), stores b for its
+// own rows and columns, and leaves per-block maxima of |b_A| for the norm.
+//
 // Boundary: at every level the ghost ring keeps its fixed values -- row -1 is
 // 100 on columns 0..N-1, row N and columns -1 and N are 0.  Wavefronts whose
 // window or row range touches the ring re-impose them after each level; the
@@ -161,11 +166,12 @@ struct TBGlobalIO {
     const float* pu;
     const float* pb;
     float* po;
+    float* pbo;
     int P;
     bool lane_loads, store_lane;
 
-    __device__ __forceinline__ void init(const float* uin, const float* bin, float* uout, const StepArgs& a,
-                                         const TBLane& L, int X, bool loads, int j0, int y0) {
+    __device__ __forceinline__ void init(const float* uin, const float* bin, float* uout, float* bout,
+                                         const StepArgs& a, const TBLane& L, int X, bool loads, int j0, int y0) {
         (void)X;
         (void)j0;
         (void)y0;
@@ -173,6 +179,7 @@ struct TBGlobalIO {
         pu = uin + a.g.origin + L.c0;
         pb = bin + a.g.origin + L.c0;
         po = uout + a.g.origin + L.c0;
+        pbo = bout ? bout + a.g.origin + L.c0 : nullptr;
         lane_loads = loads;
         store_lane = L.core[0];
     }
@@ -184,10 +191,9 @@ struct TBGlobalIO {
         }
     }
     template <bool EDGE>
-    __device__ __forceinline__ void store(const float4& out, int i, bool row_out, int y0, const TBLane& L) {
-        (void)y0;
+    __device__ __forceinline__ void store_to(float* base, const float4& out, int i, bool row_out, const TBLane& L) {
         if (row_out && store_lane) {
-            float* q = po + (int64_t)i * P;
+            float* q = base + (int64_t)i * P;
             if (L.core[3]) {
                 st4_nt(q, out);
             } else {
@@ -197,23 +203,36 @@ struct TBGlobalIO {
             }
         }
     }
+    template <bool EDGE>
+    __device__ __forceinline__ void store(const float4& out, int i, bool row_out, int y0, const TBLane& L) {
+        (void)y0;
+        store_to<EDGE>(po, out, i, row_out, L);
+    }
+    // row j of b (RHS launches)
+    template <bool EDGE>
+    __device__ __forceinline__ void store_b(const float4& v, int j, bool row_out, int y0, const TBLane& L) {
+        (void)y0;
+        store_to<EDGE>(pbo, v, j, row_out, L);
+    }
 };
 
 struct TBBufferIO {
     __amdgpu_buffer_rsrc_t ru, rb;  // u_k and b, from row j0 - 1 and window column X
     __amdgpu_buffer_rsrc_t ro;      // output, from row y0 and window column X
+    __amdgpu_buffer_rsrc_t rbo;     // b output of an RHS launch, from row y0 and window column X
     uint32_t vload;                 // the lane's byte offset in a row; kOOB: lane wholly outside [0, N)
     uint32_t vst4;                  // 16-byte store offset of a lane whose 4 columns are all stored
     uint32_t vst1[4];               // dword store offsets of a partly stored lane's columns (EDGE)
     uint32_t rowb;                  // row pitch in bytes
 
-    __device__ __forceinline__ void init(const float* uin, const float* bin, float* uout, const StepArgs& a,
-                                         const TBLane& L, int X, bool loads, int j0, int y0) {
+    __device__ __forceinline__ void init(const float* uin, const float* bin, float* uout, float* bout,
+                                         const StepArgs& a, const TBLane& L, int X, bool loads, int j0, int y0) {
         const int P = a.g.P;
         rowb = (uint32_t)P * 4u;
         ru = make_rsrc(uin + a.g.origin + (int64_t)(j0 - 1) * P + X);
         rb = make_rsrc(bin + a.g.origin + (int64_t)(j0 - 1) * P + X);
         ro = make_rsrc(uout + a.g.origin + (int64_t)y0 * P + X);
+        if (bout) rbo = make_rsrc(bout + a.g.origin + (int64_t)y0 * P + X);
         const uint32_t lb = (uint32_t)(threadIdx.x & 63) * 16u;
         vload = loads ? lb : kOOB;
         const bool full = L.core[0] && L.core[1] && L.core[2] && L.core[3];
@@ -231,16 +250,27 @@ struct TBBufferIO {
         nb = bld4(rb, vload, so);
     }
     template <bool EDGE>
+    __device__ __forceinline__ void store_to(__amdgpu_buffer_rsrc_t r, const float4& out, int i, bool row_out,
+                                             int y0) {
+        const uint32_t so = row_out ? (uint32_t)(i - y0) * rowb : 0u;
+        bst4_nt(r, row_out ? vst4 : kOOB, so, out);
+        if (EDGE) {
+            bst1(r, row_out ? vst1[0] : kOOB, so, out.x);
+            bst1(r, row_out ? vst1[1] : kOOB, so, out.y);
+            bst1(r, row_out ? vst1[2] : kOOB, so, out.z);
+            bst1(r, row_out ? vst1[3] : kOOB, so, out.w);
+        }
+    }
+    template <bool EDGE>
     __device__ __forceinline__ void store(const float4& out, int i, bool row_out, int y0, const TBLane& L) {
         (void)L;
-        const uint32_t so = row_out ? (uint32_t)(i - y0) * rowb : 0u;
-        bst4_nt(ro, row_out ? vst4 : kOOB, so, out);
-        if (EDGE) {
-            bst1(ro, row_out ? vst1[0] : kOOB, so, out.x);
-            bst1(ro, row_out ? vst1[1] : kOOB, so, out.y);
-            bst1(ro, row_out ? vst1[2] : kOOB, so, out.z);
-            bst1(ro, row_out ? vst1[3] : kOOB, so, out.w);
-        }
+        store_to<EDGE>(ro, out, i, row_out, y0);
+    }
+    // row j of b (RHS launches)
+    template <bool EDGE>
+    __device__ __forceinline__ void store_b(const float4& v, int j, bool row_out, int y0, const TBLane& L) {
+        (void)L;
+        store_to<EDGE>(rbo, v, j, row_out, y0);
     }
 };
 
@@ -250,11 +280,12 @@ using TBIO = typename std::conditional<(D >= 5), TBBufferIO, TBGlobalIO>::type;
 // The streaming state of one wavefront: for every level t < D three row
 // registers whose roles rotate (old = the row before, mid, new = the row after,
 // in the direction of travel, as seen by level t+1), the prefetched next row,
-// the ring slot.  DIR = +1 streams the band downwards, -1 upwards; going up,
+// the ring slot.  RHS: the b operand holds s and b = u^n + s is formed per row
+// (CHK and RHS never go together).  DIR = +1 streams the band downwards, -1 upwards; going up,
 // the "before" rows lie below, so the update and the residual are handed the
 // old and new rows as south and north instead of north and south -- every
 // point sees the same neighbours in the same order either way.
-template <int D, bool CHK, int EK, bool FAST, int DIR>
+template <int D, bool CHK, int EK, bool FAST, int DIR, bool RHS>
 struct TBStream {
     TBIO<D> io;
     float r, d, y;
@@ -263,7 +294,7 @@ struct TBStream {
     float4 (*ring)[64];
     float4 nu, nb;  // row j+1 of u_k and b, loaded one row ahead
     int s;          // ring slot of the current row
-    uint32_t m;     // running max |res| (CHK)
+    uint32_t m;     // running max |res| (CHK) or |b_A| (RHS), as bits
 
     // One row j: read it, push every level one row further, store level D.
     // UP/MID/NEW are the level registers in this row's rotation.
@@ -271,9 +302,25 @@ struct TBStream {
         constexpr int R = D + 1;
         const int lane = threadIdx.x & 63;
         NEW[0] = nu;
-        const float4 cb = nb;
+        const float4 cb = RHS ? make_float4(nu.x + nb.x, nu.y + nb.y, nu.z + nb.z, nu.w + nb.w) : nb;
         io.load(nu, nb, j + DIR, j0, j1);  // fetch the next row while this one is worked on
         ring[s][lane] = cb;
+        if (RHS) {
+            // b of an own row is stored once, by the wavefront whose core holds it;
+            // ||b_A|| = max |b + r*g| with g = 100 on row 0
+            const bool own = j >= y0 && j <= last;
+            io.template store_b<EK == kEdgeCols>(cb, j, own, y0, L);
+            if (own) {
+                const float rg = r * (j == 0 ? kTop : 0.0f);
+                const uint32_t v0 = L.core[0] ? __float_as_uint(fabsf(cb.x + rg)) : 0u;
+                const uint32_t v1 = L.core[1] ? __float_as_uint(fabsf(cb.y + rg)) : 0u;
+                const uint32_t v2 = L.core[2] ? __float_as_uint(fabsf(cb.z + rg)) : 0u;
+                const uint32_t v3 = L.core[3] ? __float_as_uint(fabsf(cb.w + rg)) : 0u;
+                const uint32_t x = v0 > v1 ? v0 : v1, z = v2 > v3 ? v2 : v3;
+                const uint32_t w = x > z ? x : z;
+                m = m > w ? m : w;
+            }
+        }
         float4 out;
         const int depth = DIR > 0 ? j - j0 : j1 - j;  // level t is exact from the (2t)-th row streamed on
         // b of the next level is read one level ahead, so the LDS latency
@@ -309,11 +356,12 @@ struct TBStream {
     }
 };
 
-template <int D, bool CHK, int EK, bool FAST, int DIR>
+template <int D, bool CHK, int EK, bool FAST, int DIR, bool RHS>
 __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const float* __restrict__ bin,
-                                            float* __restrict__ uout, const StepArgs& a, const TBLane& L, int X,
-                                            bool lane_loads, int y0, int last, float4 (*ring)[64]) {
-    TBStream<D, CHK, EK, FAST, DIR> st;
+                                            float* __restrict__ uout, float* __restrict__ bout, const StepArgs& a,
+                                            const TBLane& L, int X, bool lane_loads, int y0, int last,
+                                            float4 (*ring)[64]) {
+    TBStream<D, CHK, EK, FAST, DIR, RHS> st;
     st.N = a.g.N;
     st.r = a.r;
     st.d = a.d;
@@ -322,7 +370,7 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     st.j1 = last + D;
     st.y0 = y0;
     st.last = last;
-    st.io.init(uin, bin, uout, a, L, X, lane_loads, st.j0, y0);
+    st.io.init(uin, bin, uout, bout, a, L, X, lane_loads, st.j0, y0);
     st.L = L;
     st.ring = ring;
     st.s = 0;
@@ -358,14 +406,16 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     return st.m;
 }
 
-template <int D, bool CHK, bool FAST, int DIR>
+template <int D, bool CHK, bool FAST, int DIR, bool RHS>
 __device__ __forceinline__ uint32_t tb_band_kind(const float* __restrict__ uin, const float* __restrict__ bin,
-                                                 float* __restrict__ uout, const StepArgs& a, const TBLane& L, int X,
-                                                 bool lane_loads, int y0, int last, float4 (*ring)[64], bool cols,
-                                                 bool rows) {
-    if (cols) return tb_band<D, CHK, kEdgeCols, FAST, DIR>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
-    if (rows) return tb_band<D, CHK, kEdgeRows, FAST, DIR>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
-    return tb_band<D, CHK, kEdgeNone, FAST, DIR>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring);
+                                                 float* __restrict__ uout, float* __restrict__ bout,
+                                                 const StepArgs& a, const TBLane& L, int X, bool lane_loads, int y0,
+                                                 int last, float4 (*ring)[64], bool cols, bool rows) {
+    if (cols)
+        return tb_band<D, CHK, kEdgeCols, FAST, DIR, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring);
+    if (rows)
+        return tb_band<D, CHK, kEdgeRows, FAST, DIR, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring);
+    return tb_band<D, CHK, kEdgeNone, FAST, DIR, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring);
 }
 
 // Register budget per depth: up to 4, four wavefronts per SIMD (128 VGPRs);
@@ -374,13 +424,18 @@ __device__ __forceinline__ uint32_t tb_band_kind(const float* __restrict__ uin, 
 template <int D>
 constexpr int tb_waves_per_simd() { return D <= 4 ? 4 : (D <= 8 ? 3 : 2); }
 
-template <int D, bool CHK, bool FAST>
+// RHS (the first launch of a step): bin is s, bout receives b; it runs
+// whatever the stop flag says, since the norm reduction after it clears the
+// flag the previous step left set.
+template <int D, bool CHK, bool FAST, bool RHS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(tb_waves_per_simd<D>())))
 void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
-                                               float* __restrict__ uout, StepArgs a, int H) {
+                                               float* __restrict__ uout, StepArgs a, int H,
+                                               float* __restrict__ bout) {
+    static_assert(!(CHK && RHS), "a launch either checks or forms b");
     constexpr int Dp = (D + 3) & ~3;
     __shared__ float4 ring[D + 1][64];
-    if (a.sc->stop) return;  // a previous check already stopped the step
+    if (!RHS && a.sc->stop) return;  // a previous check already stopped the step
     const int N = a.g.N;
     const int lane = threadIdx.x;
     const int strips = tb_strip_count(N, Dp);
@@ -414,14 +469,17 @@ void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
         // slower (D = 4: 169 -> 182 us, D = 2: 169 -> 177 us).
         if constexpr (D >= 5) {
             if ((t / strips) & 1)
-                m = tb_band_kind<D, CHK, FAST, -1>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring, cols, rows);
+                m = tb_band_kind<D, CHK, FAST, -1, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring,
+                                                        cols, rows);
             else
-                m = tb_band_kind<D, CHK, FAST, 1>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring, cols, rows);
+                m = tb_band_kind<D, CHK, FAST, 1, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring,
+                                                       cols, rows);
         } else {
-            m = tb_band_kind<D, CHK, FAST, 1>(uin, bin, uout, a, L, X, lane_loads, y0, last, ring, cols, rows);
+            m = tb_band_kind<D, CHK, FAST, 1, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring, cols,
+                                                   rows);
         }
     }
-    if (CHK) store_block_max<1>(m, a.sc, blockIdx.x);
+    if (CHK || RHS) store_block_max<1>(m, a.sc, blockIdx.x);
 }
 
 // Resident wavefronts per CU for the checking variant of depth D (the one with
@@ -429,8 +487,8 @@ void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
 template <int D>
 static int tb_waves_per_cu(bool fast) {
     int n = 0;
-    hipError_t e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tblock<D, true, true>, 64, 0)
-                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tblock<D, true, false>, 64, 0);
+    hipError_t e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tblock<D, true, true, false>, 64, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tblock<D, true, false, false>, 64, 0);
     return (e == hipSuccess && n > 0) ? n : 4;
 }
 
@@ -493,18 +551,57 @@ template <int D>
 static hipError_t launch_tb_d(const float* uin, const float* b, float* uout, bool check, const StepArgs& a,
                               int H, hipStream_t s) {
     const int blocks = (int)tblock_blocks(a.g.N, D, H);
+    float* none = nullptr;
     if (check) {
         if (a.fastdiv)
-            hipLaunchKernelGGL((k_tblock<D, true, true>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H);
+            hipLaunchKernelGGL((k_tblock<D, true, true, false>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H,
+                               none);
         else
-            hipLaunchKernelGGL((k_tblock<D, true, false>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H);
+            hipLaunchKernelGGL((k_tblock<D, true, false, false>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H,
+                               none);
     } else {
         if (a.fastdiv)
-            hipLaunchKernelGGL((k_tblock<D, false, true>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H);
+            hipLaunchKernelGGL((k_tblock<D, false, true, false>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H,
+                               none);
         else
-            hipLaunchKernelGGL((k_tblock<D, false, false>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H);
+            hipLaunchKernelGGL((k_tblock<D, false, false, false>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H,
+                               none);
     }
     return hipGetLastError();
+}
+
+// The right-hand-side variant exists for the constant-divisor quotient only;
+// with the IEEE quotient the step keeps the separate right-hand-side pass.
+template <int D>
+static hipError_t launch_tb_rhs_d(const float* u, const float* src, float* b, float* uout, const StepArgs& a, int H,
+                                  hipStream_t s) {
+    if (!a.fastdiv) return hipErrorInvalidValue;
+    const int blocks = (int)tblock_blocks(a.g.N, D, H);
+    hipLaunchKernelGGL((k_tblock<D, false, true, true>), dim3(blocks), dim3(64), 0, s, u, src, uout, a, H, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_tblock_rhs(const float* u, const float* src, float* b, float* uout, int D, const StepArgs& a,
+                             int H, hipStream_t s) {
+    switch (D) {
+        case 1: return launch_tb_rhs_d<1>(u, src, b, uout, a, H, s);
+        case 2: return launch_tb_rhs_d<2>(u, src, b, uout, a, H, s);
+        case 3: return launch_tb_rhs_d<3>(u, src, b, uout, a, H, s);
+        case 4: return launch_tb_rhs_d<4>(u, src, b, uout, a, H, s);
+        case 5: return launch_tb_rhs_d<5>(u, src, b, uout, a, H, s);
+        case 6: return launch_tb_rhs_d<6>(u, src, b, uout, a, H, s);
+        case 7: return launch_tb_rhs_d<7>(u, src, b, uout, a, H, s);
+        case 8: return launch_tb_rhs_d<8>(u, src, b, uout, a, H, s);
+        case 9: return launch_tb_rhs_d<9>(u, src, b, uout, a, H, s);
+        case 10: return launch_tb_rhs_d<10>(u, src, b, uout, a, H, s);
+        case 11: return launch_tb_rhs_d<11>(u, src, b, uout, a, H, s);
+        case 12: return launch_tb_rhs_d<12>(u, src, b, uout, a, H, s);
+        case 13: return launch_tb_rhs_d<13>(u, src, b, uout, a, H, s);
+        case 14: return launch_tb_rhs_d<14>(u, src, b, uout, a, H, s);
+        case 15: return launch_tb_rhs_d<15>(u, src, b, uout, a, H, s);
+        case 16: return launch_tb_rhs_d<16>(u, src, b, uout, a, H, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_tblock(const float* uin, const float* b, float* uout, int D, bool check, const StepArgs& a,

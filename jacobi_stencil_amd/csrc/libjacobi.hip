@@ -50,12 +50,13 @@ int fail(int code, const std::string& msg) {
 constexpr int kMaxN = 65536;
 constexpr int kMaxD = 32;
 constexpr int kMaxTBlockD = 16;
-constexpr int kClasses = 9;
+constexpr int kClasses = 10;
 
 enum KClass {
     KC_RHS = 0, KC_SYNC = 1, KC_SYNC_CHECK = 2, KC_TBLOCK = 3, KC_ASYNC = 4, KC_RESID = 5, KC_PERSIST = 6,
     KC_NOOP = 7,   // launches issued ahead of a check that then stopped the step: they return at once
-    KC_REDUCE = 8  // one-block reductions of a check's or a norm's partial maxima
+    KC_REDUCE = 8,  // one-block reductions of a check's or a norm's partial maxima
+    KC_TBLOCK_RHS = 9  // a step's first temporal-blocking launch, which also forms b
 };
 
 // One launch as seen by the launch timer.
@@ -73,6 +74,7 @@ struct jac_ctx {
     int N;
     float r, d, y;
     int fastdiv;     // 1: the constant-divisor quotient was verified for this d
+    bool rhs_pending;  // the next temporal-blocking launch forms b itself (first of a step)
     int fast_now;    // division path of the work being enqueued (see division_path)
     bool src_plain;  // the source is finite and holds no -0
     double smax;     // max |s|
@@ -302,6 +304,19 @@ int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, i
                 c->tb_rows[m] = tblock_rows(c->N, m, c->cus, tblock_waves_per_cu(m, c->fastdiv != 0));
             const int H = o->band_rows > 0 ? o->band_rows : c->tb_rows[m];
             npart = tblock_blocks(c->N, m, H);
+            if (c->rhs_pending && !check) {
+                // b = u^n + s formed in this launch, then ||b_A|| from its partial maxima
+                c->rhs_pending = false;
+                if (npart > c->npart_cap)
+                    return fail(JAC_EINVAL, "band_rows too small for this N: too many wavefront bands");
+                st = timed(c, KC_TBLOCK_RHS,
+                           [&] { return launch_tblock_rhs(in, c->s, c->b, out, m, a, H, c->stream); });
+                if (st) return st;
+                st = timed(c, KC_REDUCE, [&] { return launch_reduce(npart, true, a, c->stream); });
+                if (st) return st;
+                *buf ^= 1;
+                return JAC_OK;
+            }
             if (check && npart > c->npart_cap)
                 return fail(JAC_EINVAL, "band_rows too small for this N: too many wavefront bands");
             st = timed(c, KC_TBLOCK, [&] { return launch_tblock(in, c->b, out, m, check, a, H, c->stream); });
@@ -586,7 +601,10 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
         int s0 = drain_profile(c, c->step_serial - 1);  // earlier steps have finished
         if (s0) return s0;
     }
-    int st = enqueue_rhs(c, o);
+    // temporal blocking through the launch driver forms b in the step's first
+    // launch; the other paths run the separate right-hand-side pass
+    const bool fuse_rhs = !graph && o->kernel == JAC_TBLOCK && c->fast_now;
+    int st = fuse_rhs ? JAC_OK : enqueue_rhs(c, o);
     if (st) return st;
     int buf = c->cur;
     c->cur_group = 0;
@@ -599,7 +617,9 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
         JAC_HIP(hipGraphLaunch(gx, c->stream));
         buf ^= flips;
     } else {
+        c->rhs_pending = fuse_rhs;
         st = enqueue_sweeps(c, o, L, false, 0, &buf);
+        c->rhs_pending = false;
         if (st) return st;
     }
 
@@ -828,6 +848,7 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
     c->sc = (Scratch*)(base + 4 * c->g.plane);
     c->npart_cap = partial_cap(N);
     c->cur = 0;
+    c->rhs_pending = false;
     c->prof_every = 0;
     c->step_serial = 0;
     c->cur_group = -1;

@@ -91,7 +91,8 @@ def test_config_c2_against_stored_oracle(D):
 
 @pytest.mark.parametrize("D", [4, 8])
 def test_config_c3_against_stored_oracle(D):
-    """N = 8192, r = 10, the benchmark workload."""
+    """N = 8192, r = 10, the benchmark workload: step by step, then all ten steps
+    in one solve call with the default options, as the benchmark times it."""
     exp = load_expected("C3")
     assert exp is not None
     say("tblock C3", D)
@@ -103,6 +104,11 @@ def test_config_c3_against_stored_oracle(D):
             assert k == exp["sweeps"][n]
             assert f"{np.float32(rho).view(np.uint32):08x}" == exp["rho_bits"][n]
             assert field_hash(sol.field()) == exp["field_sha256"][n], f"step {n}"
+        sol.reset()
+        st, k, rho = sol.solve(exp["steps"], jac.jac_opts_default(kernel=TB, D=D))
+        assert st == jac.JAC_OK and k.tolist() == exp["sweeps"]
+        assert [f"{np.float32(x).view(np.uint32):08x}" for x in rho] == exp["rho_bits"]
+        assert field_hash(sol.field()) == exp["field_sha256"][-1]
     finally:
         sol.close()
 
@@ -156,6 +162,37 @@ def test_band_heights_bitwise(H):
     s = workloads.gaussian_source(N, r)
     ref = oracle.solve(N, r, s, steps=2)
     assert_same(lib_solve(N, r, s, 2, opts(kernel=TB, D=D, band_rows=H)), ref, f"H={H}")
+
+
+@pytest.mark.parametrize("N,D,r", [(70, 8, 10.0), (300, 4, 0.05), (513, 3, 1.0), (1040, 8, 10.0)])
+def test_first_launch_forms_rhs_bitwise(N, D, r):
+    """Overlapped checks through the launch driver: each step's first launch
+    forms b = u^n + s itself and leaves the partial maxima of |b_A|, and no
+    separate right-hand-side pass runs; blocking checks and the graph driver
+    keep the separate pass.  Every path gives the oracle's bits (random u^0, so
+    b differs from s; at r = 0.05 the interior, not row 0, sets ||b_A||)."""
+    say("tblock rhs in first launch", N, D, r)
+    s = workloads.random_source(N, r, 11)
+    u0 = workloads.random_field(N, 11)
+    ref = oracle.solve(N, r, s, u0=u0, steps=3)
+    for checks, driver, fused in ((jac.JAC_CHECKS_OVERLAPPED, jac.JAC_LAUNCH, True),
+                                  (jac.JAC_CHECKS_BLOCKING, jac.JAC_LAUNCH, False),
+                                  (jac.JAC_CHECKS_OVERLAPPED, jac.JAC_GRAPH, False)):
+        sol = jac.Solver(N, r, s)
+        try:
+            sol.set_field(u0)
+            sol.profile(1)
+            st, k, rho = sol.solve(3, opts(kernel=TB, D=D, checks=checks, driver=driver))
+            u = sol.field()
+            _, n_rhs, _ = sol.profile_read("rhs")
+            _, n_first, _ = sol.profile_read("tblock_rhs")
+            fast = sol.last_division_fast
+        finally:
+            sol.close()
+        assert_same((st, u, k, rho), ref, f"N={N} D={D} checks={checks} driver={driver}")
+        # the forming launch exists for the constant-divisor quotient only
+        assert fast or r < 1.0
+        assert (n_rhs, n_first) == ((0, 3) if fused and fast else (3, 0)), (checks, driver, fast)
 
 
 @pytest.mark.parametrize("kernel,D", [(TB, 8), (jac.JAC_SYNC, 1)])
