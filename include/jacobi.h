@@ -105,7 +105,9 @@ typedef struct {
     int32_t tile_y;      /* ASYNC tile height in rows (1..256) */
     int32_t M;           /* check interval in sweeps (>= 1); the interval is max(M, D) */
     float tol;           /* rho threshold (> 0) */
-    int32_t band_rows;   /* TBLOCK: rows per wavefront band (LAUNCH), tile side (PERSISTENT); 0: automatic */
+    int32_t band_rows;   /* TBLOCK: rows per wavefront band (LAUNCH; for D >= 5 lowered where a band's rows
+                            would span 2 GiB or more, which changes no result), tile side (PERSISTENT);
+                            0: automatic */
     int64_t max_sweeps;  /* per step; a failed check at or past it ends with JAC_ENOCONV */
     int32_t checks;      /* jac_checks */
     int32_t controller;  /* jac_controller (ASYNC only) */

@@ -266,6 +266,7 @@ int64_t sync_blocks(int N, int rows);
 // Rows per wavefront of the synchronous sweep on a device with `cus` CUs.
 int sync_rows_for(int N, int cus);
 int64_t tblock_blocks(int N, int D, int H);
+int tblock_max_rows(int N, int D);
 int64_t async_blocks(int N, int tx, int ty, int o);
 // The whole solve of nsteps steps in one cooperative kernel (see
 // kernels_persist.hip).  `out` is pinned host memory for nsteps records of

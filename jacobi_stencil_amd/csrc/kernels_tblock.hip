@@ -541,6 +541,17 @@ int tblock_rows(int N, int D, int cus, int waves_per_cu) {
     return H < 4 ? 4 : H;
 }
 
+// Buffer row I/O (D >= 5) addresses a band's rows by 32-bit byte offsets from
+// the row before it, and offsets from kOOB (2 GiB) on read as zeros: a band's
+// rows plus two on each side must span less than that.  Flat I/O (D <= 4) has
+// no limit.
+int tblock_max_rows(int N, int D) {
+    if (D < 5) return INT32_MAX;
+    const int64_t rowb = (int64_t)make_geom(N).P * 4;
+    const int64_t h = ((int64_t)kOOB - 1024) / rowb - 2 * D - 4;
+    return h < 1 ? 1 : (h > INT32_MAX ? INT32_MAX : (int)h);
+}
+
 int64_t tblock_blocks(int N, int D, int H) {
     const int Dp = (D + 3) & ~3;
     const int64_t tiles = (int64_t)tb_strip_count(N, Dp) * ((N + H - 1) / H);

@@ -302,7 +302,8 @@ int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, i
         case JAC_TBLOCK: {
             if (o->band_rows == 0 && c->tb_rows[m] == 0)
                 c->tb_rows[m] = tblock_rows(c->N, m, c->cus, tblock_waves_per_cu(m, c->fastdiv != 0));
-            const int H = o->band_rows > 0 ? o->band_rows : c->tb_rows[m];
+            const int Hmax = tblock_max_rows(c->N, m);  // any height gives the same bits
+            const int H = std::min(o->band_rows > 0 ? o->band_rows : c->tb_rows[m], Hmax);
             npart = tblock_blocks(c->N, m, H);
             if (c->rhs_pending && !check) {
                 // b = u^n + s formed in this launch, then ||b_A|| from its partial maxima

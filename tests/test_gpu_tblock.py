@@ -195,6 +195,35 @@ def test_first_launch_forms_rhs_bitwise(N, D, r):
         assert (n_rhs, n_first) == ((0, 3) if fused and fast else (3, 0)), (checks, driver, fast)
 
 
+def test_band_spanning_more_than_2gib_bitwise():
+    """N = 24576 asked for as one band of rows at D = 8: its rows span 2.4 GB,
+    past the 32-bit offsets of the buffer row I/O, so the library lowers the
+    band height.  After the step's first launch (which also forms b), every
+    point must equal the oracle's value for a point at the same distance from
+    the ghost ring on a 40 x 40 grid with the same constant source: from u = 0,
+    8 sweeps see only 8 cells around a point, and the rest is translation
+    invariant."""
+    N, r, D, c, n = 24576, 1.0, 8, np.float32(0.25), 40
+    say("tblock band over 2 GiB", N, D)
+    ref = oracle.solve(n, r, np.full((n, n), c, np.float32), steps=1, max_sweeps=8)
+    assert ref.status == oracle.ENOCONV and ref.sweeps[0] == 8
+    sol = jac.Solver(N, r, np.full((N, N), c, np.float32))
+    try:
+        st, k, rho = sol.step(opts(kernel=TB, D=D, band_rows=N, max_sweeps=8), allow=(jac.JAC_ENOCONV,))
+        u = sol.field()
+    finally:
+        sol.close()
+    assert st == jac.JAC_ENOCONV and k == 8
+    assert np.float32(rho).view(np.uint32) == ref.rho[0].view(np.uint32)
+    idx = np.full(N, n // 2)
+    idx[: n // 2] = np.arange(n // 2)
+    idx[N - n // 2:] = np.arange(n // 2, n)
+    for r0 in range(0, N, 4096):  # row blocks keep the expected array small
+        want = ref.u[idx[r0:r0 + 4096, None], idx[None, :]]
+        got = u[r0:r0 + 4096]
+        assert np.array_equal(bits(got), bits(want)), f"rows {r0}..{r0 + 4095}"
+
+
 @pytest.mark.parametrize("kernel,D", [(TB, 8), (jac.JAC_SYNC, 1)])
 def test_config_c4_against_stored_oracle(kernel, D):
     """N = 18432, r = 100, point source, ten steps (14160 sweeps), every step
