@@ -68,7 +68,12 @@ enum jac_kernel {
 enum jac_checks {
     JAC_CHECKS_OVERLAPPED = 0,  /* the residual of u_{gL} is fused into the first launch of the next
                                    interval, which is queued before the host reads check g; a launch
-                                   that follows a stopping check returns at once */
+                                   that follows a stopping check returns at once.  A check that the
+                                   step's last three checks extrapolate below 0.97 * tol runs as a
+                                   residual pass alone; if it does not converge, the interval it
+                                   skipped follows.  Results never depend on this.  Environment
+                                   variable JACOBI_PREDICT_MARGIN=m at create time replaces 0.97
+                                   (0 turns the prediction off) */
     JAC_CHECKS_BLOCKING = 1     /* after each interval a standalone residual kernel, then the host waits
                                    for R and decides before anything more is queued */
 };

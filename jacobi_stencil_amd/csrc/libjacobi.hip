@@ -75,6 +75,7 @@ struct jac_ctx {
     float r, d, y;
     int fastdiv;     // 1: the constant-divisor quotient was verified for this d
     bool rhs_pending;  // the next temporal-blocking launch forms b itself (first of a step)
+    float predict_margin;  // overlapped checks: a check predicted below margin * tol runs alone (0: never)
     int fast_now;    // division path of the work being enqueued (see division_path)
     bool src_plain;  // the source is finite and holds no -0
     double smax;     // max |s|
@@ -586,6 +587,39 @@ int run_step_blocking(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float*
     }
 }
 
+// Final-check prediction (overlapped checks).  The check that ends a step is
+// normally fused into a launch whose sweeps are then thrown away (a whole
+// interval: eight launches of the synchronous sweep).  Once the last three
+// checks of the step fall at a steady rate, rho of a later check is
+// extrapolated geometrically; if it falls below margin * tol, that check is
+// queued as a residual pass alone (8 bytes per point) with nothing behind it.
+// If it does not converge after all, the interval it skipped is queued next
+// from the same iterate.  The iterates, counts and rho are those of the
+// unpredicted order; only which launches run changes.
+constexpr float kPredictMargin = 0.97f;
+
+struct CheckHistory {
+    float rho[3] = {0.0f, 0.0f, 0.0f};  // rho of the last three checks of the step, newest first
+    int64_t last = 0;                   // the check rho[0] belongs to (0: none yet)
+    int n = 0;
+    void push(int64_t g, float r) {
+        rho[2] = rho[1];
+        rho[1] = rho[0];
+        rho[0] = r;
+        last = g;
+        n = n < 3 ? n + 1 : 3;
+    }
+    // is check g (> last) predicted to converge?
+    bool predicts_stop(int64_t g, float tol, float margin) const {
+        if (margin <= 0.0f || n < 3 || g <= last) return false;
+        if (!(rho[0] > 0.0f && rho[1] > 0.0f && rho[2] > 0.0f)) return false;  // also excludes NaN
+        const double q1 = (double)rho[0] / rho[1], q0 = (double)rho[1] / rho[2];
+        if (!(q1 < 1.0 && q0 < 1.0) || std::fabs(q1 / q0 - 1.0) > 0.02) return false;
+        const double pred = (double)rho[0] * std::pow(q1, (double)(g - last));
+        return pred < (double)margin * (double)tol;
+    }
+};
+
 // One step through the launch or the graph driver.  Check g (g >= 1) examines
 // u_{gL}; its R lands in mailbox slot (g - 1) % kRing.
 int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out) {
@@ -626,6 +660,23 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
 
     int64_t g_enq = 1;  // next group to enqueue
     bool final_enqueued = false;
+    int64_t predicted = 0;  // the check queued alone on a prediction (0: none)
+    CheckHistory hist;
+    // the interval after check g, from u_{gL}, without a check (group 0's form)
+    auto enqueue_plain_interval = [&](int64_t g) -> int {
+        c->cur_group = g;
+        c->cur_first = false;
+        if (graph) {
+            hipGraphExec_t gx;
+            int flips;
+            int s2 = graph_for(c, o, false, buf, &gx, &flips);
+            if (s2) return s2;
+            JAC_HIP(hipGraphLaunch(gx, c->stream));
+            buf ^= flips;
+            return JAC_OK;
+        }
+        return enqueue_sweeps(c, o, L, false, 0, &buf);
+    };
     auto enqueue_group = [&]() -> int {
         const int ev = (int)(g_enq % kRing);
         const int slot = (int)((g_enq - 1) % kRing);
@@ -640,6 +691,13 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
             if (s2) return s2;
             JAC_HIP(hipEventRecord(c->ev[ev], c->stream));
             final_enqueued = true;
+        } else if (hist.predicts_stop(g_enq, o->tol, c->predict_margin)) {
+            // predicted to end the step: measure only, keep u_{gL} in place
+            s2 = enqueue_residual(c, o, buf, slot);
+            if (s2) return s2;
+            JAC_HIP(hipEventRecord(c->ev[ev], c->stream));
+            final_enqueued = true;
+            predicted = g_enq;
         } else if (graph) {
             hipGraphExec_t gx;
             int flips;
@@ -664,7 +722,7 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
     st = enqueue_group();
     if (st) return st;
     for (int64_t g = 1;; ++g) {
-        if (!final_enqueued && g_enq <= g + 1) {  // keep one interval queued beyond check g
+        while (!final_enqueued && g_enq <= g + 1) {  // keep one interval queued beyond check g
             st = enqueue_group();
             if (st) return st;
         }
@@ -686,6 +744,14 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
             if (std::isnan(rho)) return fail(JAC_ENAN, "rho is NaN");
             if (!stop) return fail(JAC_ENOCONV, "max_sweeps reached before rho < tol");
             return JAC_OK;
+        }
+        hist.push(g, rho);
+        if (g == predicted) {
+            // the predicted final check did not converge: the skipped interval next
+            st = enqueue_plain_interval(g);
+            if (st) return st;
+            final_enqueued = false;
+            predicted = 0;
         }
         if (c->prof_every > 0 && c->recs.size() > 8192) {
             st = drain_profile(c, c->step_serial);  // keep this step's records (their class may change)
@@ -850,6 +916,13 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
     c->npart_cap = partial_cap(N);
     c->cur = 0;
     c->rhs_pending = false;
+    {
+        // JACOBI_PREDICT_MARGIN=m at create time: m = 0 turns the final-check
+        // prediction off; results never depend on it
+        const char* pm = std::getenv("JACOBI_PREDICT_MARGIN");
+        const float m = pm ? std::strtof(pm, nullptr) : kPredictMargin;
+        c->predict_margin = (std::isfinite(m) && m > 0.0f) ? m : 0.0f;
+    }
     c->prof_every = 0;
     c->step_serial = 0;
     c->cur_group = -1;

@@ -197,7 +197,8 @@ def test_repeat_and_reset_are_deterministic():
     assert np.array_equal(bits(u1), bits(u2))
 
 
-def test_profile_counts_launches():
+def test_profile_counts_launches(monkeypatch):
+    monkeypatch.setenv("JACOBI_PREDICT_MARGIN", "0")  # every check fused, as counted below
     N, r = 256, 1.0
     say("sync profile")
     s = workloads.gaussian_source(N, r)
