@@ -383,11 +383,33 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     float4 A[D], B[D], C[D];
 #pragma unroll
     for (int t = 0; t < D; ++t) { A[t] = zero; B[t] = zero; C[t] = zero; }
+    // Issue priority by progress (D >= 5).  The SIMD's arbiter favours the
+    // oldest wavefront, so of the three sharing a SIMD the first dispatched
+    // finished a band at ~158 us, the last at ~215 us, running alone for its
+    // final ~35 us, where one wavefront cannot keep the VALU busy.  Lowering
+    // the priority in steps at 75, 90 and 97 % of the band lets the others
+    // catch up before the end (8192^2, D = 8: 58.9 -> 57.5 ms per solve;
+    // 2048^2: 9.21 -> 8.69 ms).  The shallow, memory-bound depths gain nothing.
+    // Only the order of issue changes.
+    const int total = st.j1 - st.j0 + 1;
+    int level = -1;
+    auto set_prio = [&](int done) {
+        if constexpr (D < 5) return;
+        const int p = 100 * done;
+        const int l = p < 75 * total ? 0 : (p < 90 * total ? 1 : (p < 97 * total ? 2 : 3));
+        if (l == level) return;
+        level = l;
+        if (l == 0) __builtin_amdgcn_s_setprio(3);
+        else if (l == 1) __builtin_amdgcn_s_setprio(2);
+        else if (l == 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+    };
     // Three rows per trip, the level registers rotating A -> B -> C.  While
     // the pipeline fills (the first 2D rows of the band) a row computes only
     // the levels that are already exact.
     if constexpr (DIR > 0) {
         for (int j = st.j0; j <= st.j1; j += 3) {
+            set_prio(j - st.j0);
             st.row(j, A, B, C);
             if (j + 1 > st.j1) break;
             st.row(j + 1, B, C, A);
@@ -396,6 +418,7 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
         }
     } else {
         for (int j = st.j1; j >= st.j0; j -= 3) {
+            set_prio(st.j1 - j);
             st.row(j, A, B, C);
             if (j - 1 < st.j0) break;
             st.row(j - 1, B, C, A);
