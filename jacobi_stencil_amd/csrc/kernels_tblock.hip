@@ -387,16 +387,17 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     // oldest wavefront, so of the three sharing a SIMD the first dispatched
     // finished a band at ~158 us, the last at ~215 us, running alone for its
     // final ~35 us, where one wavefront cannot keep the VALU busy.  Lowering
-    // the priority in steps at 75, 90 and 97 % of the band lets the others
-    // catch up before the end (8192^2, D = 8: 58.9 -> 57.5 ms per solve;
-    // 2048^2: 9.21 -> 8.69 ms).  The shallow, memory-bound depths gain nothing.
-    // Only the order of issue changes.
+    // the priority in steps at 60, 85 and 97 % of the band lets the others
+    // catch up before the end (8192^2, D = 8: 58.9 -> 57.5 ms per solve with
+    // steps at 75/90/97 %, 0.5 % less again at 60/85/97; 2048^2: 9.21 ->
+    // 8.69 ms).  The shallow, memory-bound depths gain nothing.  Only the
+    // order of issue changes.
     const int total = st.j1 - st.j0 + 1;
     int level = -1;
     auto set_prio = [&](int done) {
         if constexpr (D < 5) return;
         const int p = 100 * done;
-        const int l = p < 75 * total ? 0 : (p < 90 * total ? 1 : (p < 97 * total ? 2 : 3));
+        const int l = p < 60 * total ? 0 : (p < 85 * total ? 1 : (p < 97 * total ? 2 : 3));
         if (l == level) return;
         level = l;
         if (l == 0) __builtin_amdgcn_s_setprio(3);
