@@ -80,13 +80,17 @@ enum jac_checks {
 
 /* Depth controllers for ASYNC (page "stencil-jacobian.vercel.app", section 02:
  * D is a launch argument and may change between launches).  They need the
- * LAUNCH driver; they imply JAC_CHECKS_BLOCKING.  The depths are powers of two
- * up to opts.D; each time step starts afresh. */
+ * LAUNCH driver; they imply JAC_CHECKS_BLOCKING.  G-asc and G-desc use the four
+ * levels 1, 2, 4, 8 (three thresholds, four depths), each capped at opts.D:
+ * the depth of a level L is min(L, opts.D), so with opts.D = 6 G-desc runs
+ * 6, 4, 2, 1 and with opts.D = 16 neither exceeds 8.  Each time step starts
+ * afresh. */
 enum jac_controller {
     JAC_STATIC = 0,  /* D = opts.D throughout */
-    JAC_G_ASC = 1,   /* start at 1; D steps up through 1, 2, 4, 8 as rho falls below 1e-2, 1e-3, 1e-4;
-                        latched (never steps back within a time step) */
-    JAC_G_DESC = 2,  /* start at 8; D steps down through 8, 4, 2, 1 at the same thresholds; latched */
+    JAC_G_ASC = 1,   /* start at 1; D steps up through 1, 2, 4, 8 (capped) as rho falls below 1e-2, 1e-3,
+                        1e-4; latched (never steps back within a time step) */
+    JAC_G_DESC = 2,  /* start at min(8, opts.D); D steps down through 8, 4, 2, 1 (capped) at the same
+                        thresholds; latched */
     JAC_G_FB = 3     /* hill climbing on the measured convergence rate -ln(rho_g / rho_{g-1}) per ms:
                         start at 1; after each check (except the one right after a change, the
                         settling window) double D while the rate holds, halve it when the rate drops

@@ -5,6 +5,7 @@ Run as ``python -m jacobi_stencil_amd.build`` or through
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -63,11 +64,14 @@ def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        _run([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+    objs = [os.path.join(objdir, os.path.splitext(src)[0] + ".o") for src in SOURCES]
+    # the sources compile independently; a few at a time keeps the build to the longest one
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "6"))))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+        futs = [pool.submit(_run, [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+                for src, obj in zip(SOURCES, objs)]
+        for f in futs:
+            f.result()
     tlib = torch_lib_dir()
     tmp = LIB + ".tmp"
     _run(["g++", "-shared", "-o", tmp, *objs, "-Wl,--no-undefined", "-L" + tlib, "-l:libamdhip64.so",

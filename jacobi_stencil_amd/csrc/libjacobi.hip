@@ -492,16 +492,17 @@ struct DepthControl {
     double prev_rate;  // G-fb: the last rate compared against (NaN: none yet)
     int settle;        // G-fb: checks still to skip after a change
 
+    // G-asc / G-desc take the levels 1, 2, 4, 8, each capped at Dmax.
     DepthControl(int k, int dmax) : kind(k), Dmax(dmax), D(dmax), prev_rho(NAN), prev_rate(NAN), settle(0) {
         if (kind == JAC_G_ASC || kind == JAC_G_FB) D = 1;
+        if (kind == JAC_G_DESC) D = std::min(8, Dmax);
     }
     // After a check of an interval run at depth D that took `ms` milliseconds.
     void update(float rho, double ms) {
-        auto clamp = [&](int v) { return v < 1 ? 1 : (v > Dmax ? Dmax : v); };
         if (kind == JAC_G_ASC) {
-            D = std::max(D, clamp(asc_level(rho)));
+            D = std::max(D, std::min(asc_level(rho), Dmax));
         } else if (kind == JAC_G_DESC) {
-            D = std::min(D, clamp(desc_level(rho) * Dmax / 8));
+            D = std::min(D, std::min(desc_level(rho), Dmax));
         } else if (kind == JAC_G_FB) {
             const float before = prev_rho;
             prev_rho = rho;

@@ -286,11 +286,13 @@ void orc_async_launch(int N, float r, const float* u, const float* b, float* out
 /*
  * Depth chosen by the threshold controllers of page "stencil-jacobian.vercel.
  * app", section 02 (block-async, "G-asc and G-desc"): the depth steps as rho
- * crosses 1e-2, 1e-3 and 1e-4.  Reading of the page: G-asc starts each time
- * step at D = 1 and moves through 1, 2, 4, 8 as rho falls below each
- * threshold; G-desc starts at 8 and moves through 8, 4, 2, 1.  Both are capped
- * to [1, Dmax] and latched: within a time step the depth never moves back.
- * rho is compared with the thresholds as binary32 values.
+ * crosses 1e-2, 1e-3 and 1e-4.  Reading of the page: three thresholds give
+ * four depths, 1, 2, 4 and 8.  G-asc starts each time step at D = 1 and moves
+ * through 1, 2, 4, 8 as rho falls below each threshold; G-desc starts at 8 and
+ * moves through 8, 4, 2, 1.  Each depth is capped at Dmax (min(level, Dmax):
+ * with Dmax = 6 G-desc runs 6, 4, 2, 1 and G-asc 1, 2, 4, 6; with Dmax = 16
+ * neither goes past 8).  Both are latched: within a time step the depth never
+ * moves back.  rho is compared with the thresholds as binary32 values.
  */
 static int asc_level(float q) {
     if (q >= 1e-2f) return 1;
@@ -304,7 +306,7 @@ static int desc_level(float q) {
     if (q >= 1e-4f) return 2;
     return 1;
 }
-static int clamp_depth(int v, int Dmax) { return v < 1 ? 1 : (v > Dmax ? Dmax : v); }
+static int cap_depth(int level, int Dmax) { return level > Dmax ? Dmax : level; }
 
 /*
  * Ten (or `steps`) backward-Euler steps, each iterated to rho < tol.
@@ -360,6 +362,7 @@ int orc_solve_ex(int N, float r, const float* s, float* u_io, int steps, float t
         int64_t k = 0;
         int D = Dmax;
         if (ctrl == ORC_G_ASC) D = 1;
+        if (ctrl == ORC_G_DESC) D = cap_depth(8, Dmax);
         for (;;) {
             if (ctrl == ORC_SCHED) {
                 if (nlog >= sched_n) { status = ORC_EINVAL; break; }
@@ -398,10 +401,10 @@ int orc_solve_ex(int N, float r, const float* s, float* u_io, int steps, float t
             if (isnan(q)) { status = ORC_ENAN; break; }
             if (k >= max_sweeps) { status = ORC_ENOCONV; break; }
             if (ctrl == ORC_G_ASC) {
-                int t = clamp_depth(asc_level(q), Dmax);
+                int t = cap_depth(asc_level(q), Dmax);
                 if (t > D) D = t;
             } else if (ctrl == ORC_G_DESC) {
-                int t = clamp_depth(desc_level(q) * Dmax / 8, Dmax);
+                int t = cap_depth(desc_level(q), Dmax);
                 if (t < D) D = t;
             }
         }

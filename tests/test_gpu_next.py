@@ -161,14 +161,15 @@ def test_overlap_rejections():
 # ------------------------------------------------------------ controllers
 
 @pytest.mark.parametrize("ctrl,oc", [(jac.JAC_G_ASC, oracle.G_ASC), (jac.JAC_G_DESC, oracle.G_DESC)])
-@pytest.mark.parametrize("r", [10.0, 100.0])
-def test_threshold_controllers_bitwise(ctrl, oc, r):
+@pytest.mark.parametrize("r,D", [(10.0, 8), (100.0, 8), (10.0, 4), (10.0, 6), (100.0, 6), (10.0, 16)])
+def test_threshold_controllers_bitwise(ctrl, oc, r, D):
+    """The capped levels min(level, D): D = 4 and 6 below the top level, 16 above it."""
     N = 64
-    say("controller", ctrl, r)
+    say("controller", ctrl, r, D)
     s = workloads.gaussian_source(N, r)
-    ref = oracle.solve(N, r, s, steps=2, M=8, mode=oracle.ASYNC, D=8, tx=32, ty=8, controller=oc,
+    ref = oracle.solve(N, r, s, steps=2, M=8, mode=oracle.ASYNC, D=D, tx=32, ty=8, controller=oc,
                        log_cap=100000)
-    got, dlog = solve_with_log(N, r, s, 2, opts(kernel=jac.JAC_ASYNC, D=8, tile_x=32, tile_y=8, controller=ctrl))
+    got, dlog = solve_with_log(N, r, s, 2, opts(kernel=jac.JAC_ASYNC, D=D, tile_x=32, tile_y=8, controller=ctrl))
     assert_same(got, ref, f"ctrl {ctrl} r={r}")
     assert dlog.tolist() == ref.D_log.tolist()
 

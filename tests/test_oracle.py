@@ -372,6 +372,45 @@ def test_controller_switch_points(orc, ctrl):
     assert changes == sorted(set(firsts)), (changes, firsts)
 
 
+@pytest.mark.parametrize("ctrl", ["asc", "desc"])
+@pytest.mark.parametrize("Dmax", [4, 6, 16])
+def test_controller_depths_capped(orc, ctrl, Dmax):
+    """Section 02 gives three thresholds (1e-2, 1e-3, 1e-4), hence four levels
+    1, 2, 4, 8; with opts.D below 8 each level is capped at it (depth =
+    min(level, Dmax)), and above 8 no depth passes 8.  Pinned on the first time step, whose rho is known from
+    R and the closed-form ||b_A|| of u^0 = 0: the schedule follows the capped,
+    latched rule check by check, and the depths it visits are the capped levels
+    in order.  A rule that scales the levels by Dmax / 8 instead gives G-desc
+    6, 3, 1 at Dmax = 6 and steps G-desc down from 4 already at 1e-2 at Dmax = 4,
+    and fails here."""
+    N, r = 64, 10.0
+    s = workloads.gaussian_source(N, r)
+    c = orc.G_ASC if ctrl == "asc" else orc.G_DESC
+    res = orc.solve(N, r, s, steps=1, mode=orc.ASYNC, D=Dmax, tx=32, ty=8, controller=c, log_cap=4096)
+    assert res.status == orc.OK
+    bA = orc.rhs_norm(orc.rhs(np.zeros((N, N), np.float32), s), r)
+    rho = (res.R_log / bA).astype(np.float32)
+
+    def level(q):  # the page's thresholds, compared in binary32
+        over = [q >= np.float32(t) for t in (1e-2, 1e-3, 1e-4)]
+        k = sum(over)  # thresholds rho is still at or above
+        return [8, 4, 2, 1][k] if ctrl == "asc" else [1, 2, 4, 8][k]
+
+    want = [1 if ctrl == "asc" else min(8, Dmax)]
+    for q in rho[:-1]:
+        t = min(level(q), Dmax)
+        want.append(max(want[-1], t) if ctrl == "asc" else min(want[-1], t))
+    assert res.D_log.tolist() == want
+    visited = [d for i, d in enumerate(want) if i == 0 or d != want[i - 1]]
+    expect = {("asc", 4): [1, 2, 4], ("asc", 6): [1, 2, 4, 6], ("asc", 16): [1, 2, 4, 8],
+              ("desc", 4): [4, 2, 1], ("desc", 6): [6, 4, 2, 1], ("desc", 16): [8, 4, 2, 1]}[(ctrl, Dmax)]
+    assert visited == expect
+    if ctrl == "desc" and Dmax == 4:
+        # the first step down (4 -> 2) follows the first check below 1e-3, not 1e-2
+        first_change = next(i for i in range(1, len(want)) if want[i] != want[i - 1])
+        assert rho[first_change - 1] < np.float32(1e-3) and np.all(rho[:first_change - 1] >= np.float32(1e-3))
+
+
 def test_controller_reduces_to_sync(orc):
     """With a loose tolerance (1e-2) every step stops before rho crosses 1e-2,
     so G-asc never leaves D = 1 -- the synchronous iterates exactly; and G-desc

@@ -40,6 +40,9 @@ MUTANTS = {
                                       "(size_t)(j - ex0 + 1)]; }"),
     "asc_not_latched": ("if (t > D) D = t;", "D = t;"),
     "desc_thresholds_shifted": ("if (q >= 1e-2f) return 8;", "if (q >= 1e-1f) return 8;"),
+    "desc_levels_scaled_by_dmax": ("int t = cap_depth(desc_level(q), Dmax);",
+                                   "int t = cap_depth(desc_level(q) * Dmax / 8 < 1 ? 1 : desc_level(q) * Dmax / 8, Dmax);"),
+    "desc_starts_at_dmax": ("if (ctrl == ORC_G_DESC) D = cap_depth(8, Dmax);", ""),
 }
 
 
