@@ -128,15 +128,23 @@ typedef struct {
 } jac_opts;
 
 /* SYNC, LAUNCH, D = 1, 32 x 8 tiles, M = 8, tol = 1e-5, band_rows = 0, max_sweeps = 1e6,
- * overlapped checks, static depth, no overlap. */
+ * overlapped checks, static depth, no overlap (tol and M as page
+ * "stencil-jacobian.vercel.app", section 01 fixes them; 32 x 8 blocks as its
+ * section 02 names them). */
 void jac_opts_default(jac_opts* opts);
 
-/* Bytes of device workspace a context of size N needs (u twice, b, dt*f,
- * scratch).  0 if N is out of range. */
+/* Bytes of device workspace a context of size N needs: the two ping-pong
+ * iterates, b and dt*f (the arrays of page "stencil-jacobian.vercel.app",
+ * section 02, each padded with a ghost ring), plus scratch for the per-block
+ * residual maxima and the persistent driver's barrier.  0 if N is out of
+ * range (1..65536). */
 size_t jac_workspace_bytes(int N);
 
 /*
- * Create a context for an N x N grid with coupling r = alpha*dt/h^2 (>= 0).
+ * Create a context for an N x N grid with coupling r = alpha*dt/h^2 (>= 0)
+ * (page "stencil-jacobian.vercel.app", section 01 "The problem": the N x N
+ * grid of unknowns, the source f, boundary 100 on top and 0 elsewhere; the
+ * coupling r is the one whose values 1, 10 and 100 set the sweeps per step).
  *   source_host  N*N floats, s = dt*f, copied during the call; NULL means 0.
  *   workspace    device memory of at least jac_workspace_bytes(N) bytes,
  *                256-byte aligned, owned by the caller, not freed by the
@@ -147,24 +155,37 @@ size_t jac_workspace_bytes(int N);
 int jac_create(int N, float r, const float* source_host, void* workspace, size_t ws_bytes,
                void* stream, jac_t* out);
 
-/* One backward-Euler step: b = u^n + s, then Jacobi until rho < tol.  On
- * return the field is u^{n+1} and *sweeps / *rho (either may be NULL) hold the
- * sweep count and the rho of the accepted iterate.  For SYNC and TBLOCK the
- * result is bitwise identical to the oracle's for the same M. */
+/* One backward-Euler step (page "stencil-jacobian.vercel.app", section 01:
+ * b = u^n + dt*f with u^n held fixed, then point Jacobi until rho < tol, tested
+ * every M sweeps; section 02 for the kernels): on return the field is u^{n+1}
+ * and *sweeps / *rho (either may be NULL) hold the sweep count and the rho of
+ * the accepted iterate.  For SYNC and TBLOCK the result is bitwise identical to
+ * the oracle's for the same M.  Blocks until the step's convergence is decided
+ * (work the step queued ahead may still be draining on the stream).  Errors:
+ * JAC_EINVAL for bad options (nothing is run), JAC_ENOCONV / JAC_ENAN (the field
+ * is the last checked iterate), JAC_EDEVICE on a HIP failure. */
 int jac_step(jac_t ctx, const jac_opts* opts, int64_t* sweeps, float* rho);
 
-/* nsteps steps; sweeps[n] and rho[n] for each (arrays of nsteps, may be NULL).
- * Stops at the first step that fails (ENOCONV / ENAN): the field is that
- * step's last checked iterate, later entries are 0 and NaN. */
+/* nsteps backward-Euler steps (page "stencil-jacobian.vercel.app", section 01:
+ * ten steps, each starting from the previous step's converged field);
+ * sweeps[n] and rho[n] for each (host arrays of nsteps, may be NULL).  Stops at
+ * the first step that fails (ENOCONV / ENAN): the field is that step's last
+ * checked iterate, later entries are 0 and NaN.  With JAC_PERSISTENT the whole
+ * solve is one device kernel and the host waits once. */
 int jac_solve(jac_t ctx, int nsteps, const jac_opts* opts, int64_t* sweeps, float* rho);
 
-/* Throughput entry: b = u^n + s, then exactly nsweeps sweeps with no checks;
- * the field is left at the last iterate.  If rho != NULL it receives the rho
- * of that iterate (one extra residual pass).  Launches one by one whatever
- * opts->driver says. */
+/* Throughput entry (the sweep kernels of page "stencil-jacobian.vercel.app",
+ * section 02, without the convergence test of section 01): b = u^n + s, then
+ * exactly nsweeps sweeps with no checks; the field is left at the last
+ * iterate.  If rho != NULL it receives the rho of that iterate (one extra
+ * residual pass).  Launches one by one whatever opts->driver says. */
 int jac_sweep(jac_t ctx, const jac_opts* opts, int64_t nsweeps, float* rho);
 
-/* Copy the current field to / from host memory (N*N floats).  Blocking. */
+/* Copy the current field u^n to / from host memory (N*N floats, row-major,
+ * row 0 next to the 100 boundary; the unknowns of page
+ * "stencil-jacobian.vercel.app", section 01), for checkpoint and resume.
+ * Blocking: waits for the context's stream.  jac_set_field also resets the
+ * bound the constant-divisor division path relies on (see below). */
 int jac_get_field(jac_t ctx, float* host_out);
 int jac_set_field(jac_t ctx, const float* host_in);
 
@@ -207,7 +228,8 @@ int jac_destroy(jac_t ctx);
 const char* jac_last_error(void);
 
 /*
- * Bandwidth probe (measurement only, no context needed): on `stream`,
+ * Bandwidth probe (measurement only, no context needed; the analogue of the
+ * bw_probe of page "cuda-solver-lab", section "Hardware ceilings"): on `stream`,
  * kind 0 copies a to c, kind 1 writes c = a + b (two reads, one write per
  * element, the traffic mix of a sweep); n floats, a multiple of 4, arrays
  * 16-byte aligned device memory owned by the caller; `blocks` workgroups of

@@ -80,5 +80,21 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+ABI_CLIENT_SRC = os.path.join(ROOT, "tests", "abi_client.c")
+ABI_CLIENT = os.path.join(ROOT, "tests", "abi_client")
+
+
+def build_abi_client(out: str = ABI_CLIENT, verbose: bool = False) -> str:
+    """Compile tests/abi_client.c, a plain C11 caller of include/jacobi.h, with
+    gcc against the built library and the HIP runtime the library uses (both
+    found at run time through the rpath)."""
+    tlib = torch_lib_dir()
+    _run(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          "-I" + os.path.join(ROOT, "include"), "-I/opt/rocm/include", ABI_CLIENT_SRC, "-o", out,
+          "-L" + HERE, "-l:libjacobi.so", "-L" + tlib, "-l:libamdhip64.so",
+          "-Wl,-rpath," + HERE + ",-rpath," + tlib], verbose)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

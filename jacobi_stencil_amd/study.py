@@ -4,6 +4,8 @@
     python -m jacobi_stencil_amd.study regimes     [--out FILE] [--quick]
     python -m jacobi_stencil_amd.study controllers [--out FILE]
     python -m jacobi_stencil_amd.study overlap     [--out FILE]
+    python -m jacobi_stencil_amd.study depths      [--out FILE]
+    python -m jacobi_stencil_amd.study launches    [--out FILE]
     python -m jacobi_stencil_amd.study fit REGIMES_JSONL
 
 What each one measures (page "stencil-jacobian.vercel.app" unless noted):
@@ -21,6 +23,18 @@ controllers  the depth controllers G-asc, G-desc and G-fb against static depths
 overlap      overlapping subdomains for the block-asynchronous kernel (Islam &
              Wang, "Hierarchical Jacobi Iteration ...", sections 3.5 and 4):
              sweeps and time against the overlap o.
+depths       the depth sweep D = 1..16 at N = 8192, r = 10 for exact temporal
+             blocking and for block-async at 32 x 16 tiles (section 05, Fig. 6 /
+             Table VIII): time to solution, sweeps, s and c, and for the
+             launches that carry the sweeps their mean device time, the HBM
+             fraction of 12 bytes per point moved once per launch (8 TB/s) and
+             the VALU fraction of 8 lane-operations per point-update (39.3 T/s).
+launches     the cost of one launch in the launch-bound regime (section 04:
+             about 4.4 us per synchronous sweep, 9.4 us for BA_D1, 19.4 us for
+             BA_D8): at N = 256 and 512, r = 10, the mean device time of each
+             launch class (HIP events around every launch) and the wall time per
+             launch of a whole solve (solve time / launches), per kernel and
+             driver, median of the repeats.
 fit          a depth-2 decision tree on (working set / cache, r) picking the
              fastest family of the regimes study, with leave-one-size-out
              accuracy (section 06, "Depth-2 decision tree").
@@ -181,6 +195,76 @@ def study_overlap(a):
                 _emit(a.out, rec)
 
 
+# MI355X: 8 TB/s of HBM; 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz non-packed float32 lane-operations.
+HBM_PEAK = 8.0e12
+VALU_PEAK = 256 * 4 * 16 * 2.4e9
+
+
+def _launch_profile(R, N, r, steps, kclass, every, **o):
+    """Mean device time (us) of the launches of one class over a profiled solve."""
+    sol = R.solver(N, r)
+    opts = R.jac.jac_opts_default(**o)
+    sol.reset()
+    sol.profile(every)
+    sol.solve(steps, opts)
+    R.torch.cuda.synchronize()
+    avg_ms, n, nt = sol.profile_read(kclass)
+    sol.profile(0)
+    return 1e3 * avg_ms, n, nt
+
+
+def study_depths(a):
+    R = Runner(a.repeats)
+    jac = R.jac
+    N, r, steps = 8192, 10.0, 10
+    base = R.run(N, r, steps, kernel=jac.JAC_SYNC)
+    base.update(study="depths", family="sync", D=1, s=1.0, c=1.0)
+    _emit(a.out, base)
+    for fam, kernel, kc in (("temporal", jac.JAC_TBLOCK, "tblock"), ("async_32x16", jac.JAC_ASYNC, "async")):
+        for D in range(1, 17):
+            o = dict(kernel=kernel, D=D, tile_x=32, tile_y=16)
+            rec = R.run(N, r, steps, **o)
+            us, n, nt = _launch_profile(R, N, r, steps, kc, 8, **o)
+            upd = D * N * N  # point-updates per launch of D sweeps
+            rec.update(study="depths", family=fam, D=D, interval=max(8, D),
+                       s=round(rec["sweeps"] / base["sweeps"], 4),
+                       c=round((rec["ms"] / rec["sweeps"]) / (base["ms"] / base["sweeps"]), 4),
+                       launch_us=round(us, 2), launches=n, timed=nt,
+                       hbm_frac=round(12.0 * N * N / (us * 1e-6) / HBM_PEAK, 4),
+                       valu_frac=round(8.0 * upd / (us * 1e-6) / VALU_PEAK, 4),
+                       exact_gpts=round(N * N * base["sweeps"] / (rec["ms"] / 1e3) / 1e9, 1))
+            _emit(a.out, rec)
+
+
+def study_launches(a):
+    R = Runner(a.repeats)
+    jac = R.jac
+    cases = [("sync", "sync_check", dict(kernel=jac.JAC_SYNC)),
+             ("async_D1_32x16", "async", dict(kernel=jac.JAC_ASYNC, D=1, tile_x=32, tile_y=16)),
+             ("async_D8_32x16", "async", dict(kernel=jac.JAC_ASYNC, D=8, tile_x=32, tile_y=16)),
+             ("temporal_D8", "tblock", dict(kernel=jac.JAC_TBLOCK, D=8))]
+    for N in (256, 512):
+        for name, kc, o in cases:
+            for driver in (jac.JAC_LAUNCH, jac.JAC_GRAPH, jac.JAC_PERSISTENT):
+                rec = R.run(N, 10.0, 10, driver=driver, **o)
+                D = o.get("D", 1)
+                launches = rec["sweeps"] / D
+                rec.update(study="launches", case=name, driver=["launch", "graph", "persistent"][driver],
+                           wall_us_per_launch=round(rec["ms"] * 1e3 / launches, 2),
+                           wall_us_per_sweep=rec["us_per_sweep"])
+                if driver == jac.JAC_LAUNCH:
+                    us = []
+                    for _ in range(max(5, a.repeats)):
+                        u, n, nt = _launch_profile(R, N, 10.0, 10, kc, 1, driver=driver, **o)
+                        us.append(u)
+                    rec.update(device_us_per_launch=round(statistics.median(us), 2), device_repeats=len(us))
+                    if kc == "sync_check":  # the other synchronous launches carry no check
+                        us = [_launch_profile(R, N, 10.0, 10, "sync", 1, driver=driver, **o)[0]
+                              for _ in range(max(5, a.repeats))]
+                        rec.update(device_us_per_plain_sweep=round(statistics.median(us), 2))
+                _emit(a.out, rec)
+
+
 def fit(a):
     """Depth-2 tree on (ws / L2, r) -> fastest family, leave-one-size-out."""
     from sklearn.tree import DecisionTreeClassifier, export_text
@@ -214,14 +298,14 @@ def fit(a):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("study", choices=("checks", "regimes", "controllers", "overlap", "fit"))
+    ap.add_argument("study", choices=("checks", "regimes", "controllers", "overlap", "depths", "launches", "fit"))
     ap.add_argument("regimes", nargs="?", help="fit: the regimes study's JSON lines")
     ap.add_argument("--out", default=None)
     ap.add_argument("--repeats", type=int, default=3)
     ap.add_argument("--quick", action="store_true")
     a = ap.parse_args()
     {"checks": study_checks, "regimes": study_regimes, "controllers": study_controllers,
-     "overlap": study_overlap, "fit": fit}[a.study](a)
+     "overlap": study_overlap, "depths": study_depths, "launches": study_launches, "fit": fit}[a.study](a)
 
 
 if __name__ == "__main__":

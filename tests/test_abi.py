@@ -101,3 +101,15 @@ def test_one_hip_runtime_in_process():
     maps = open(f"/proc/{os.getpid()}/maps").read()
     hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
     assert len(hip) == 1, hip
+
+
+def test_c_client_builds_and_checks_arguments(tmp_path):
+    """A plain C11 program compiled against include/jacobi.h (gcc -Werror, with
+    static assertions on the option block's layout) links against the library
+    and gets every argument error back as a status code before any device work."""
+    from jacobi_stencil_amd import build as libbuild
+
+    exe = str(tmp_path / "abi_client")
+    libbuild.build_abi_client(exe)
+    proc = subprocess.run([exe, "--cpu"], capture_output=True, text=True, timeout=60)
+    assert proc.returncode == 0, proc.stderr

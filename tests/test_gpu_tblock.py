@@ -164,6 +164,45 @@ def test_band_heights_bitwise(H):
     assert_same(lib_solve(N, r, s, 2, opts(kernel=TB, D=D, band_rows=H)), ref, f"H={H}")
 
 
+_ALIGNED_REF = {}
+
+
+@pytest.mark.parametrize("H", [4, 64, 0, 1040])
+@pytest.mark.parametrize("D", [5, 7, 8, 9, 12, 16])
+def test_aligned_layout_tall_bands_bitwise(D, H):
+    """The aligned strip layout (N a multiple of 4, N >= 256: windows inside the
+    grid, no column masking) with short, automatic and full-height bands, both
+    stream directions, buffer row I/O and the straight (all levels exact) row
+    path, against the oracle on a grid whose bands are taller than the
+    pipeline (N = 1040)."""
+    N, r = 1040, 10.0
+    say("tblock aligned", D, H)
+    s = workloads.gaussian_source(N, r)
+    M = interval(D)
+    if M not in _ALIGNED_REF:
+        _ALIGNED_REF[M] = oracle.solve(N, r, s, steps=2, M=M)
+    assert_same(lib_solve(N, r, s, 2, opts(kernel=TB, D=D, M=8, band_rows=H)), _ALIGNED_REF[M], f"D={D} H={H}")
+
+
+@pytest.mark.parametrize("D", list(range(1, 17)))
+def test_config_c3_every_depth_against_stored_oracle(D):
+    """N = 8192, r = 10, the benchmark workload, at every depth 1..16 in one
+    ten-step solve with the default options: per-step sweeps and rho bits and
+    the final field against the oracle's (check interval 8, or D above 8)."""
+    exp = load_expected("C3" if D <= 8 else f"C3_M{D}")
+    assert exp is not None and exp["M"] == interval(D)
+    say("tblock C3 depth", D)
+    N, r = exp["N"], exp["r"]
+    sol = jac.Solver(N, r, workloads.source(exp["source"], N, r))
+    try:
+        st, k, rho = sol.solve(exp["steps"], jac.jac_opts_default(kernel=TB, D=D))
+        assert st == jac.JAC_OK and k.tolist() == exp["sweeps"], (k.tolist(), exp["sweeps"])
+        assert [f"{np.float32(x).view(np.uint32):08x}" for x in rho] == exp["rho_bits"]
+        assert field_hash(sol.field()) == exp["field_sha256"][-1]
+    finally:
+        sol.close()
+
+
 @pytest.mark.parametrize("N,D,r", [(70, 8, 10.0), (300, 4, 0.05), (513, 3, 1.0), (1040, 8, 10.0)])
 def test_first_launch_forms_rhs_bitwise(N, D, r):
     """Overlapped checks through the launch driver: each step's first launch
