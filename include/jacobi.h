@@ -181,6 +181,24 @@ int jac_solve(jac_t ctx, int nsteps, const jac_opts* opts, int64_t* sweeps, floa
  * residual pass).  Launches one by one whatever opts->driver says. */
 int jac_sweep(jac_t ctx, const jac_opts* opts, int64_t nsweeps, float* rho);
 
+/*
+ * jac_sweep for callers that cannot allocate at call time (tight serving
+ * loops, harnesses that forbid hipMalloc): the same launches and results as
+ * jac_sweep, but the kernels' scratch -- the norm / check header and the
+ * per-block partial maxima of the right-hand side and residual passes -- is
+ * a static device array of the library (384 KiB, one copy per GPU, held until
+ * the process ends) instead of the context's workspace, and the launch timer
+ * is not used.  The call allocates no device or host memory and creates no
+ * HIP object.  Limits: N <= 16384 and at most 32768 partial slots per launch;
+ * beyond them JAC_EINVAL, nothing is run.  All calls on one GPU share the
+ * array and each leaves its contents behind; every call re-initialises what it
+ * reads before reading it, but calls that overlap in time on one GPU (two
+ * streams, two threads) race on it and must not.  The call synchronizes the
+ * context's stream, so it cannot be captured into a graph.  JAC_EDEVICE if the
+ * device address of the array could not be found at jac_create.
+ */
+int jac_sweep_static(jac_t ctx, const jac_opts* opts, int64_t nsweeps, float* rho);
+
 /* Copy the current field u^n to / from host memory (N*N floats, row-major,
  * row 0 next to the 100 boundary; the unknowns of page
  * "stencil-jacobian.vercel.app", section 01), for checkpoint and resume.

@@ -30,6 +30,7 @@ STATUS_NAMES = {0: "JAC_OK", -1: "JAC_EINVAL", -2: "JAC_ENOMEM", -3: "JAC_EDEVIC
                 -5: "JAC_ENAN"}
 
 EXPORTS = ("jac_opts_default", "jac_workspace_bytes", "jac_create", "jac_step", "jac_solve", "jac_sweep",
+           "jac_sweep_static",
            "jac_get_field", "jac_set_field", "jac_reset", "jac_fast_division", "jac_last_division", "jac_depth_log",
            "jac_destroy", "jac_last_error",
            "jac_profile", "jac_profile_read", "jac_stream_probe")
@@ -73,6 +74,7 @@ def load_library():
         lib.jac_step.argtypes = [vp, ctypes.POINTER(jac_opts), ctypes.POINTER(i64), ctypes.POINTER(f32)]
         lib.jac_solve.argtypes = [vp, ctypes.c_int, ctypes.POINTER(jac_opts), vp, vp]
         lib.jac_sweep.argtypes = [vp, ctypes.POINTER(jac_opts), i64, ctypes.POINTER(f32)]
+        lib.jac_sweep_static.argtypes = [vp, ctypes.POINTER(jac_opts), i64, ctypes.POINTER(f32)]
         lib.jac_get_field.argtypes = [vp, vp]
         lib.jac_set_field.argtypes = [vp, vp]
         lib.jac_reset.argtypes = [vp]
@@ -145,6 +147,15 @@ def jac_sweep(ctx, opts: jac_opts, nsweeps: int, want_rho: bool = False):
     """Returns (status, rho or None)."""
     rho = ctypes.c_float(0)
     st = load_library().jac_sweep(ctx, ctypes.byref(opts), int(nsweeps), ctypes.byref(rho) if want_rho else None)
+    return st, (float(rho.value) if want_rho else None)
+
+
+def jac_sweep_static(ctx, opts: jac_opts, nsweeps: int, want_rho: bool = False):
+    """jac_sweep with the library's static device scratch (allocates nothing).
+    Returns (status, rho or None)."""
+    rho = ctypes.c_float(0)
+    st = load_library().jac_sweep_static(ctx, ctypes.byref(opts), int(nsweeps),
+                                         ctypes.byref(rho) if want_rho else None)
     return st, (float(rho.value) if want_rho else None)
 
 

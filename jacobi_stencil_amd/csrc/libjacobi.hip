@@ -19,6 +19,7 @@
 #include "check_predict.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cfloat>
 #include <chrono>
 #include <thread>
@@ -26,6 +27,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -69,6 +71,23 @@ struct Rec {
     hipEvent_t e0, e1;  // timing pair when this launch was sampled, else null
 };
 
+// ---- static scratch for jac_sweep_static (an entry point that allocates nothing)
+//
+// The scratch header, the (unused) barrier-flag lines and kStaticPartials
+// per-block partial maxima, laid out as in a workspace's scratch region.  Each
+// GPU the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: its device
+// address comes from hipGetSymbolAddress, once per device (static_scratch_on).
+constexpr int64_t kStaticPartials = 32768;
+constexpr int kStaticMaxN = 16384;
+constexpr size_t kStaticScratchBytes =
+    sizeof(Scratch) + (size_t)kMaxPersistBlocks * kFlagStride * 4 + (size_t)kStaticPartials * 4;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex g_static_mu;
+Scratch* g_static_sc[kMaxDevices];      // device address of `scratch` on each device (null: none)
+hipError_t g_static_err[kMaxDevices];  // why a device's lookup failed (hipSuccess: not failed)
+
 }  // namespace
 
 struct jac_ctx {
@@ -103,6 +122,8 @@ struct jac_ctx {
     float* s;
     Scratch* sc;
     int64_t npart_cap;
+    Scratch* static_sc;      // this device's copy of the static scratch array (jac_sweep_static)
+    hipError_t static_err;   // why it is missing, if it is
     Mailbox* mail;   // pinned host memory written by the device
     int cur;         // u[cur] holds u^n
     hipEvent_t ev[kRing];
@@ -883,6 +904,25 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
     c->s = base + 3 * c->g.plane;
     c->sc = (Scratch*)(base + 4 * c->g.plane);
     c->npart_cap = partial_cap(N);
+    c->static_sc = nullptr;
+    c->static_err = hipErrorInvalidDevice;
+    if (dev >= 0 && dev < kMaxDevices) {
+        // once per device, with that device current: the device address of the
+        // static scratch array (each GPU holds its own copy)
+        // (a failed lookup is reported by jac_sweep_static, not here: the
+        // context itself does not need the array)
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        if (!g_static_sc[dev] && g_static_err[dev] == hipSuccess) {
+            void* ptr = nullptr;
+            const hipError_t se = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (se == hipSuccess && ptr)
+                g_static_sc[dev] = (Scratch*)ptr;
+            else
+                g_static_err[dev] = se != hipSuccess ? se : hipErrorInvalidSymbol;
+        }
+        c->static_sc = g_static_sc[dev];
+        c->static_err = g_static_err[dev];
+    }
     c->cur = 0;
     c->rhs_pending = false;
     {
@@ -1026,6 +1066,34 @@ int jac_sweep(jac_t c, const jac_opts* o, int64_t nsweeps, float* rho) {
     }
     if (c->prof_every > 0) return drain_profile(c);
     return JAC_OK;
+}
+
+int jac_sweep_static(jac_t c, const jac_opts* o, int64_t nsweeps, float* rho) {
+    if (!c) return fail(JAC_EINVAL, "context is NULL");
+    if (!c->static_sc)
+        return fail(JAC_EDEVICE, std::string("no static scratch on this context's device: hipGetSymbolAddress: ") +
+                                     hipGetErrorString(c->static_err));
+    if (c->N > kStaticMaxN) return fail(JAC_EINVAL, "jac_sweep_static supports N up to 16384");
+    int st = check_opts(c, o);
+    if (st) return st;
+    // every reducing launch of jac_sweep must fit the static partial slots
+    int64_t need = std::max(rhs_blocks(c->N), sync_blocks(c->N, c->sync_rows));
+    if (need > kStaticPartials)
+        return fail(JAC_EINVAL, "jac_sweep_static: the launch needs more than 32768 partial slots");
+    // jac_sweep with the static scratch and the launch timer off (its records
+    // are the only host allocations jac_sweep makes); everything else -- the
+    // kernels, the field, the caller's workspace planes -- is the same
+    Scratch* const saved_sc = c->sc;
+    const int64_t saved_cap = c->npart_cap;
+    const int saved_prof = c->prof_every;
+    c->sc = c->static_sc;
+    c->npart_cap = kStaticPartials;
+    c->prof_every = 0;
+    st = jac_sweep(c, o, nsweeps, rho);
+    c->sc = saved_sc;
+    c->npart_cap = saved_cap;
+    c->prof_every = saved_prof;
+    return st;
 }
 
 int jac_get_field(jac_t c, float* host_out) {
