@@ -55,6 +55,35 @@ def test_config_c5_bitwise(kernel, D, r):
     assert_same(lib_solve(256, r, s, 10, opts(kernel=kernel, D=D, driver=PER)), ref, f"C5 {kernel} r={r}")
 
 
+@pytest.mark.parametrize("N,side", [(700, 0), (1024, 0), (300, 16), (33, 8), (300, 88), (1500, 0)])
+def test_sync_resident_and_staged_tiles_bitwise(N, side):
+    """The synchronous sweep under the persistent driver takes resident tiles
+    (each block keeps its tile in LDS and trades edges with its neighbours)
+    where every tile fits one round -- automatic 32- or 64-cell tiles up to
+    N = 1024, 16- and 8-cell tiles -- and re-staged tiles otherwise (88-cell
+    tiles, N = 1500); both are the oracle's bits."""
+    r = 10.0
+    say("persist sync tiles", N, side)
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=3)
+    assert_same(lib_solve(N, r, s, 3, opts(driver=PER, band_rows=side)), ref, f"N={N} side={side}")
+
+
+def test_sync_resident_nan_and_noconv():
+    """A failed step ends the resident solve with the oracle's status and field."""
+    N, r = 200, 10.0
+    say("persist sync resident noconv/nan")
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=2, max_sweeps=40)
+    assert ref.status == oracle.ENOCONV
+    assert_same(lib_solve(N, r, s, 2, opts(driver=PER, max_sweeps=40)), ref, "noconv")
+    u0 = np.zeros((N, N), np.float32)
+    u0[N // 3, N // 2] = np.inf
+    ref = oracle.solve(N, r, s, u0=u0, steps=2)
+    assert ref.status == oracle.ENAN
+    assert_same(lib_solve(N, r, s, 2, opts(driver=PER), u0=u0), ref, "nan")
+
+
 def test_config_c1_bitwise():
     say("persist C1")
     s = workloads.point_source(512, 1.0)
