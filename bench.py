@@ -13,6 +13,7 @@ Beside it, on the same JSON line:
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--kernel sync|tblock|async] [--D D]
+                       [--config C1..C5] [--driver launch|graph|persistent]
 """
 from __future__ import annotations
 
@@ -37,6 +38,7 @@ VALU_OPS_PER_UPDATE = 8
 METRIC = "Gpoint-updates/s + time-to-solution (10 steps), N=8192 r=10; % HBM roofline"
 KERNELS = {"sync": 0, "tblock": 1, "async": 2}
 DOMINANT_CLASS = {"sync": "sync", "tblock": "tblock", "async": "async"}
+DRIVERS = {"launch": 0, "graph": 1, "persistent": 2}
 
 
 def parse():
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--tile-x", type=int, default=32)
     ap.add_argument("--tile-y", type=int, default=8)
     ap.add_argument("--band-rows", type=int, default=0, help="TBLOCK rows per band (0: automatic)")
+    ap.add_argument("--driver", default="launch", choices=sorted(DRIVERS),
+                    help="how the launches are issued (the launch-bound sizes compare them)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--profile-every", type=int, default=16,
                     help="bracket every k-th launch of a class with HIP events (0: none)")
@@ -239,7 +243,7 @@ def main():
     stream = torch.cuda.current_stream()
     sol = jac.Solver(N, r, s, stream=stream)
     opts = jac.jac_opts_default(kernel=KERNELS[args.kernel], D=args.D, tile_x=args.tile_x,
-                                tile_y=args.tile_y, band_rows=args.band_rows)
+                                tile_y=args.tile_y, band_rows=args.band_rows, driver=DRIVERS[args.driver])
 
     def one_solve():
         sol.reset()
@@ -257,7 +261,8 @@ def main():
         _, sweeps, rho = one_solve()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    cls = DOMINANT_CLASS[args.kernel]
+    # the persistent driver runs each whole solve as one launch
+    cls = "persistent" if args.driver == "persistent" else DOMINANT_CLASS[args.kernel]
     launch_ms, k_n, k_timed = sol.profile_read(cls)
     _, noop_n, _ = sol.profile_read("noop")
     sol.profile(0)
@@ -273,7 +278,9 @@ def main():
         exact_sweeps = int(ex.sum())
     value = N * N * exact_sweeps / (ms_per_step / 1e3) / 1e9
     D = 1 if args.kernel == "sync" else args.D
-    bytes_per_launch = BYTES_PER_POINT_PASS * N * N
+    # one pass over memory per D sweeps; a persistent launch makes all of a solve's passes
+    passes_per_launch = total_sweeps / D if args.driver == "persistent" else 1
+    bytes_per_launch = BYTES_PER_POINT_PASS * N * N * passes_per_launch
     achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
     traffic = None
     if os.path.exists(args.traffic):
@@ -291,7 +298,7 @@ def main():
         roofline = dict(hbm, **common)
     else:
         # D sweeps per launch: bound by VALU instruction issue (SQ counters), not by HBM
-        tops = N * N * D * VALU_OPS_PER_UPDATE / (launch_ms / 1e3) / 1e12
+        tops = N * N * D * passes_per_launch * VALU_OPS_PER_UPDATE / (launch_ms / 1e3) / 1e12
         roofline = dict({"bound": "alu", "achieved": round(tops, 2), "peak": round(VALU_PEAK_TOPS, 2),
                          "unit": "TVALUop/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
                          "valu_ops_per_update": VALU_OPS_PER_UPDATE, "hbm_view": hbm}, **common)
@@ -311,7 +318,8 @@ def main():
         "config": {"workload": f"{args.config}: N={N} r={r:g} {cfg['source']} source, {nsteps} backward-Euler "
                                f"steps, Jacobi to rho<1e-5 checked every 8 sweeps",
                    "N": N, "r": r, "source": cfg["source"], "time_steps": nsteps, "kernel": args.kernel,
-                   "D": D, "tile": [args.tile_x, args.tile_y] if args.kernel == "async" else None},
+                   "D": D, "tile": [args.tile_x, args.tile_y] if args.kernel == "async" else None,
+                   "driver": args.driver},
         "time_to_solution_ms": round(ms_per_step, 3),
         "sweeps_per_solve": total_sweeps,
         "sweeps_per_step": sweeps.tolist(),

@@ -25,8 +25,9 @@ overlap      overlapping subdomains for the block-asynchronous kernel (Islam &
              sweeps and time against the overlap o.
 depths       the depth sweep D = 1..16 at N = 8192, r = 10 for exact temporal
              blocking and for block-async at 32 x 16 tiles (section 05, Fig. 6 /
-             Table VIII): time to solution, sweeps, s and c, and for the
-             launches that carry the sweeps their mean device time, the HBM
+             Table VIII): time to solution, sweeps, s and c (checks every 8
+             sweeps, every D above 8), and for launches of D sweeps (timed in a
+             solve that checks every D sweeps) their mean device time, the HBM
              fraction of 12 bytes per point moved once per launch (8 TB/s) and
              the VALU fraction of 8 lane-operations per point-update (39.3 T/s).
 launches     the cost of one launch in the launch-bound regime (section 04:
@@ -224,7 +225,10 @@ def study_depths(a):
         for D in range(1, 17):
             o = dict(kernel=kernel, D=D, tile_x=32, tile_y=16)
             rec = R.run(N, r, steps, **o)
-            us, n, nt = _launch_profile(R, N, r, steps, kc, 8, **o)
+            # per-launch time from a solve checking every D sweeps, so that every
+            # profiled launch does D sweeps (with M = 8 a depth that does not
+            # divide 8 also issues shorter launches to reach each check)
+            us, n, nt = _launch_profile(R, N, r, steps, kc, 8, M=max(D, 1), **o)
             upd = D * N * N  # point-updates per launch of D sweeps
             rec.update(study="depths", family=fam, D=D, interval=max(8, D),
                        s=round(rec["sweeps"] / base["sweeps"], 4),
