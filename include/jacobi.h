@@ -102,8 +102,10 @@ enum jac_driver {
     JAC_LAUNCH = 0,      /* host enqueues each launch; reads each check back */
     JAC_GRAPH = 1,       /* each check interval captured once as a HIP graph and replayed */
     JAC_PERSISTENT = 2   /* one cooperative kernel per jac_solve: every step, check and decision on the
-                            device; SYNC and TBLOCK use 2-D tiles staged in LDS with a D-cell ghost zone,
-                            ASYNC its own tiles; same results as JAC_LAUNCH */
+                            device; SYNC and TBLOCK use 2-D tiles in LDS with a D-cell ghost zone (held in
+                            LDS for the whole solve when every tile fits one round of resident blocks,
+                            re-staged per D sweeps otherwise), ASYNC its own tiles; same results as
+                            JAC_LAUNCH */
 };
 
 typedef struct {
@@ -136,8 +138,8 @@ void jac_opts_default(jac_opts* opts);
 /* Bytes of device workspace a context of size N needs: the two ping-pong
  * iterates, b and dt*f (the arrays of page "stencil-jacobian.vercel.app",
  * section 02, each padded with a ghost ring), plus scratch for the per-block
- * residual maxima and the persistent driver's barrier.  0 if N is out of
- * range (1..65536). */
+ * residual maxima, the persistent driver's barrier and its resident tiles'
+ * edge exchange (at most 40 MiB).  0 if N is out of range (1..65536). */
 size_t jac_workspace_bytes(int N);
 
 /*

@@ -83,6 +83,20 @@ __host__ __device__ inline uint32_t* scratch_partials(Scratch* sc) {
 // partials is launched with at most this many blocks (checked on the host).
 inline int64_t partial_cap(int N) { return (int64_t)N * N / 64 + 65536; }
 
+// Workspace after the partial slots (256-byte aligned): the edge-exchange words
+// of the persistent kernel's resident tiles, 64 bits each.  min(5 Mi, 5 (N+31)^2)
+// words: a tile of side T with halo depth H takes 8 H T words, at most 4.25
+// per cell for T >= 32 and H <= 17, and one round holds at most 512 tiles of
+// 64 x 64 (8704 words each).
+inline int64_t exchange_words_cap(int N) {
+    const int64_t a = 5 * (int64_t)(N + 31) * (N + 31);
+    return a < ((int64_t)5 << 20) ? a : ((int64_t)5 << 20);
+}
+inline int64_t exchange_offset_floats(const Geom& g, int64_t npart_cap) {
+    const int64_t end = 4 * g.plane + (int64_t)(sizeof(Scratch) / 4) + (int64_t)kMaxPersistBlocks * kFlagStride + npart_cap;
+    return (end + 63) / 64 * 64;
+}
+
 // Host-visible results, in coherent pinned host memory that the device writes
 // directly with system-scope stores (not held in its caches), so the host sees
 // them without a system-wide cache flush behind every check.
@@ -270,10 +284,12 @@ int tblock_max_rows(int N, int D);
 int64_t async_blocks(int N, int tx, int ty, int o);
 // The whole solve of nsteps steps in one cooperative kernel (see
 // kernels_persist.hip).  `out` is pinned host memory for nsteps records of
-// persist_out_bytes() each; `partial` needs 2 x grid slots.
+// persist_out_bytes() each; `partial` needs 4 x grid slots; `xchg` holds
+// xchg_words 64-bit words for the resident tiles' edge exchange.
 hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, const float* s, uint32_t* partial,
-                          void* out, int nsteps, int cur0, bool async_mode, int D, int L, int tile_x, int tile_y,
-                          int side, int64_t max_sweeps, int cus, int* grid_used, hipStream_t stream);
+                          uint64_t* xchg, int64_t xchg_words, void* out, int nsteps, int cur0, bool async_mode, int D,
+                          int L, int tile_x, int tile_y, int side, int64_t max_sweeps, int cus, int* grid_used,
+                          hipStream_t stream);
 size_t persist_out_bytes();
 // Block-asynchronous launch: tiles tx x ty (each 1..256), each worked on
 // widened by o overlap cells per side ((tx+2o)*(ty+2o) <= 4096, o <= 64), a

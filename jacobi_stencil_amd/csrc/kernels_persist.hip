@@ -8,7 +8,12 @@
 // the paperlayer summary of arXiv 2610.15878, sections 3-4: persistent
 // kernels, device-side barriers, no host in the loop).
 //
-// Every block runs the same program:
+// Two kernels.  k_persist_res (below) keeps every tile resident in LDS for the
+// whole solve and trades tile edges point to point; it serves SYNC and TBLOCK
+// wherever all tiles fit one round of co-resident blocks.  k_persist re-stages
+// tiles per chunk behind grid barriers and serves everything else.
+//
+// k_persist: every block runs the same program:
 //   per step:   b = u^n + s and a partial max of |b_A|;  grid barrier;  every
 //               block reduces the partials to ||b_A|| (the same value in all)
 //   per chunk:  for each of its tiles, stage the tile plus an H-cell halo of
@@ -51,7 +56,8 @@ struct PersistArgs {
     float* u1;
     float* b;
     const float* s;
-    uint32_t* partial;   // 2 x gridDim.x slots (double-buffered)
+    uint32_t* partial;   // 2 x gridDim.x slots (double-buffered); resident tiles: 2 x gridDim.x 64-bit words
+    uint64_t* xchg;      // resident tiles: the edge exchange (see below)
     PersistOut* out;     // nsteps records, pinned host memory
     int nsteps, cur0;
     int async_mode;      // 0: exact tiles (ghost zone), 1: block-asynchronous tiles
@@ -337,178 +343,463 @@ __global__ __launch_bounds__(kPersistThreads) void k_persist(PersistArgs a) {
 
 // ---------------------------------------------------------------- resident tiles
 //
-// The synchronous sweep (D = 1) on grids whose tiles all fit one round of
-// co-resident blocks: each block owns one tile for the whole solve and keeps
-// its two iterates (core plus a one-cell halo) and b in LDS, and s in
-// registers.  After each sweep a block publishes the four edges of its new
-// iterate and a flag; before the next sweep it waits for its (up to) four
-// neighbours' flags and copies their edges into its halo.  A sweep then costs
-// one point-to-point exchange instead of a re-staged tile and a grid-wide
-// barrier; the norm of each step and each check's residual are grid-wide
-// maxima of tagged words, again without a barrier (tagged_max).  Every block takes the same decisions from the same reduced values,
-// so all sweep the same number of times; at a stop the result u_k is the
-// block's current iterate, whose halo already holds the neighbours' u_k edges
-// -- the next step starts from it without re-reading the grid.  The field is
-// written back to memory when the solve ends (or a step fails).
+// The exact kernels (SYNC, TBLOCK) on grids whose tiles all fit one round of
+// co-resident blocks: each block owns one square tile for the whole solve and
+// keeps, in LDS, its region -- the tile plus a halo H = D + 1 cells deep -- as
+// two iterates and s, with b of its cells in registers.  A chunk of Dc <= D
+// sweeps updates the region's interior every sweep; after sweep t the cells at
+// least t cells inside the region's edge are exact (the ghost-zone scheme of
+// page "stencil-jacobian.vercel.app", section 02), so afterwards the core and
+// the ring around it hold exactly Dc synchronous sweeps.  The ring lets the block measure the residual of its
+// core at the end of a chunk without waiting for its neighbours.  The block
+// then publishes the four H-deep strips along its core's edges, and the
+// partial maximum of a check beside them, and refills its halo from its (up to)
+// eight neighbours' strips; ghost cells (outside the grid) keep their fixed
+// values.  A chunk costs one point-to-point exchange, and a check's grid-wide
+// maximum completes under that same exchange -- no re-staged tile and no
+// grid-wide barrier.  Every block takes the same decisions from the same
+// reduced values; at a stop the result u_k is the block's current iterate,
+// whose halo already holds the neighbours' u_k, so the next step starts from
+// it without re-reading the grid.  The field goes back to memory when the
+// solve ends (or a step fails).
 //
-// Exchange memory: the b plane (b lives in LDS here), per tile and parity 4
-// edges of up to T cells -- top row, bottom row, left column, right column --
-// each cell one 64-bit word: the value in the low half, the number of the
-// sweep that produced it in the high half.  A writer stores each word with one
-// coherent 64-bit store; a reader polls the word until its tag is the sweep it
-// needs, then takes the value from the same word.  A 64-bit word is read and
-// written whole, so no fence and no separate flag are needed.  Two parities:
-// a block overwrites its sweep-s words with sweep s+2 only after it has read
-// its neighbours' sweep-s+1 edges, which they publish only after reading its
-// sweep-s ones.  The host clears the words before each solve.
+// Exchange memory (the workspace's exchange region, cleared by the host before
+// each solve): per tile and parity four strips of up to H x T cells -- top
+// rows, bottom rows, left columns, right columns of the core -- each cell one
+// 64-bit word, the value in the low half and the number of the chunk that
+// produced it in the high half.  A writer stores each word with one coherent
+// 64-bit store; a reader polls the word until its tag is the chunk it needs
+// and takes the value from the same word, so no fence or flag is needed.  Two
+// parities: a block overwrites its chunk-c words with chunk c+2 only after it
+// has read its neighbours' chunk-c+1 strips, which they publish only after
+// reading its chunk-c ones.  Tiles are at least H cells on each side, so every
+// halo cell lies in one neighbour's strip.
 
 constexpr int kResThreads = 1024;
-constexpr int kResCellsPerThread = 4;  // core cells per thread: tiles of at most 64 x 64
+constexpr int kResWaves = kResThreads / 64;
+constexpr int kResCells = 9;   // interior cells per thread: (T + 2H - 2)^2 <= 9216
+constexpr int kResPub = 5;     // strip words per thread: 4 H T <= 5120
+constexpr int kResRef = 6;     // halo words per thread: 4 H T + 4 H^2 <= 6144
+constexpr int kResPoll = 2;    // partial slots per thread: grid <= 2048
 
-__device__ __forceinline__ uint64_t* res_edges(uint64_t* xbuf, int tile, int parity, int T) {
-    return xbuf + ((int64_t)tile * 2 + parity) * 4 * T;
+// words of the edge exchange of a resident solve with halo depth H
+int64_t resident_exchange_words(int ntiles, int H, int T) { return (int64_t)ntiles * 8 * H * T; }
+
+// Max over the 64 lanes of a wavefront with DPP moves (no LDS round trips):
+// within each quad, across the quads of a 16-lane row (row rotations), then
+// across rows (row broadcasts of lanes 15 and 31); lane 63 ends with the max.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xb1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4e, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xf, 0xf, false));  // row_ror 4
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xf, 0xf, false));  // row_ror 8
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast 15
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast 31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// words of the edge exchange of a resident solve (cleared by the host)
-int64_t resident_exchange_words(int ntiles, int T) { return (int64_t)ntiles * 8 * T; }
-
-// Grid-wide max of `m` without a barrier: every block stores its block max
-// tagged with the reduction number `serial` into its slot of buffer `which`
-// (2 x gridDim.x 64-bit words, cleared by the host before the solve), then
-// waits until every slot carries that tag and takes the max.  The same value
-// in every block.  Two buffers: a block's next-but-one reduction can overwrite
-// a slot only after every block has published the one in between, which each
-// does only after reading this one.  Returns false (every block leaves) when a
-// wait outlasts the spin budget or another block's did.
-__device__ bool tagged_max(uint64_t* part, int which, uint32_t serial, uint32_t m, Scratch* sc, uint32_t* out) {
-    __shared__ uint32_t wmax[kResThreads / 64];
-    __shared__ uint32_t bad;
-    const int G = gridDim.x;
-    m = wave_max_u32(m);
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-    if (threadIdx.x == 0) bad = 0;
-    __syncthreads();
-    uint64_t* slots = part + (int64_t)which * G;
-    if (threadIdx.x == 0) {
-        uint32_t r = wmax[0];
-        for (int w = 1; w < kResThreads / 64; ++w) r = r > wmax[w] ? r : wmax[w];
-        __hip_atomic_store(&slots[blockIdx.x], ((uint64_t)serial << 32) | r, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-    uint32_t v = 0;
-    for (int i = threadIdx.x; i < G; i += kResThreads) {
-        uint32_t spins = 0;
-        uint64_t x;
-        for (;;) {
-            x = __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((uint32_t)(x >> 32) == serial) break;
-            if ((++spins & 1023u) == 0u &&
-                (__hip_atomic_load(&sc->bar_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
-                 spins > kBarrierSpins)) {
-                __hip_atomic_store(&sc->bar_error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                bad = 1;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        const uint32_t xv = (uint32_t)x;
-        v = v > xv ? v : xv;
-    }
-    __syncthreads();  // every thread is done with wmax before it is reused
-    v = wave_max_u32(v);
+// Block max of one value per thread through `wmax` (kResWaves words of LDS);
+// the caller places the barrier between the two halves.
+__device__ __forceinline__ void block_max_put(uint32_t* wmax, uint32_t v) {
+    v = wave_max_dpp(v);
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = v;
-    __syncthreads();
-    uint32_t r = wmax[0];
-    for (int w = 1; w < kResThreads / 64; ++w) r = r > wmax[w] ? r : wmax[w];
-    const bool ok = bad == 0;
-    __syncthreads();
-    *out = r;
-    return ok;
 }
+__device__ __forceinline__ uint32_t block_max_get(const uint32_t* wmax) {
+    uint32_t r = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kResWaves; ++w) r = r > wmax[w] ? r : wmax[w];
+    return r;
+}
+
+// Polls two groups of tagged 64-bit words -- n1 at base1 + off1[q] that must
+// carry tag1, n2 at base2 + off2[q] that must carry tag2 (offset -1: none) --
+// with every load of a round in flight at once, until each carries its tag.
+// Returns false when the wait outlasts the spin budget or another block gave
+// up (the error word), after setting that word.
+template <int n1, int n2>
+__device__ __forceinline__ bool poll_tagged(const uint64_t* base1, const int* off1, uint32_t tag1, uint64_t* x1,
+                                            const uint64_t* base2, const int* off2, uint32_t tag2, uint64_t* x2,
+                                            Scratch* sc) {
+#pragma unroll
+    for (int q = 0; q < n1; ++q)
+        x1[q] = off1[q] >= 0 ? __hip_atomic_load(&base1[off1[q]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : ((uint64_t)tag1 << 32);
+#pragma unroll
+    for (int q = 0; q < n2; ++q)
+        x2[q] = off2[q] >= 0 ? __hip_atomic_load(&base2[off2[q]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : ((uint64_t)tag2 << 32);
+    uint32_t spins = 0;
+    for (;;) {
+        bool pending = false;
+#pragma unroll
+        for (int q = 0; q < n1; ++q) pending |= (uint32_t)(x1[q] >> 32) != tag1;
+#pragma unroll
+        for (int q = 0; q < n2; ++q) pending |= (uint32_t)(x2[q] >> 32) != tag2;
+        if (!pending) return true;
+        if ((++spins & 1023u) == 0u &&
+            (__hip_atomic_load(&sc->bar_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
+             spins > kBarrierSpins)) {
+            __hip_atomic_store(&sc->bar_error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int q = 0; q < n1; ++q)
+            if ((uint32_t)(x1[q] >> 32) != tag1)
+                x1[q] = __hip_atomic_load(&base1[off1[q]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int q = 0; q < n2; ++q)
+            if ((uint32_t)(x2[q] >> 32) != tag2)
+                x2[q] = __hip_atomic_load(&base2[off2[q]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Per-cell bits of the resident kernel: an unknown (a grid point), in the
+// core, in the grid's top row.
+constexpr uint32_t kCellUnk = 1u, kCellCore = 2u, kCellTop = 4u;
+
+// LDS word at a byte offset (the neighbour offsets below fold into the
+// instructions' immediate fields).
+__device__ __forceinline__ float& lds_at(float* lds, int byte) {
+    return *reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + byte);
+}
+
+// One sweep over this thread's NQ cells of the region's interior (every cell
+// but the outermost ring), without branches.  `at[q]` is the byte offset of
+// the cell's west neighbour in buffer 0; `oa` and `ob` are the byte offsets of
+// the source and target buffers, lp4 the region pitch in bytes.  Every cell is
+// updated every sweep; a cell fewer than `sw` cells inside the region's edge
+// gets a value nothing reads before the halo refill overwrites it (the exact
+// cells lie ever deeper inside), so only the grid's fixed cells are masked.
+template <bool FAST, int NQ>
+__device__ __forceinline__ void res_sweep(float* lds, int oa, int ob, int lp4, const int* at, const uint32_t* info,
+                                          const float* bv, float r, float d, float y) {
+#pragma unroll
+    for (int g0 = 0; g0 < NQ; g0 += 4) {  // four cells at a time: all loads, then all stores
+        constexpr int kG = 4;
+        float v[kG];
+#pragma unroll
+        for (int q = g0; q < (g0 + kG < NQ ? g0 + kG : NQ); ++q) {
+            const int w = at[q] + oa;
+            v[q - g0] = jacobi_update<FAST>(lds_at(lds, w + 8), lds_at(lds, w), lds_at(lds, w - lp4 + 4),
+                                            lds_at(lds, w + lp4 + 4), bv[q], r, d, y);
+        }
+#pragma unroll
+        for (int q = g0; q < (g0 + kG < NQ ? g0 + kG : NQ); ++q)
+            if (info[q] & kCellUnk) lds_at(lds, at[q] + ob + 4) = v[q - g0];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Dc sweeps, buffers alternating from `cur` (R floats apart); returns the
+// buffer that holds the last sweep.
+template <bool FAST, int NQ>
+__device__ __forceinline__ int res_sweeps(float* lds, int cur, int Dc, int R, int lp4, const int* at,
+                                          const uint32_t* info, const float* bv, float r, float d, float y) {
+    for (int sw = 1; sw <= Dc; ++sw) {
+        res_sweep<FAST, NQ>(lds, cur * R * 4, (cur ^ 1) * R * 4, lp4, at, info, bv, r, d, y);
+        __syncthreads();
+        cur ^= 1;
+    }
+    return cur;
+}
+
+// The residual bits max over this thread's core cells (buffer at byte offset oa).
+template <int NQ>
+__device__ __forceinline__ uint32_t res_check(float* lds, int oa, int lp4, const int* at, const uint32_t* info,
+                                              const float* bv, float r) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int g0 = 0; g0 < NQ; g0 += 4) {
+#pragma unroll
+        for (int q = g0; q < (g0 + 4 < NQ ? g0 + 4 : NQ); ++q) {
+            const int w = at[q] + oa;
+            const uint32_t v = residual_bits(lds_at(lds, w + 4), lds_at(lds, w + 8), lds_at(lds, w),
+                                             lds_at(lds, w - lp4 + 4), lds_at(lds, w + lp4 + 4), bv[q], r);
+            m = (info[q] & kCellCore) && v > m ? v : m;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return m;
+}
+
+#define JAC_RES_NQ(CALL)                 \
+    switch (nq) {                        \
+        case 1: CALL(1); break;          \
+        case 2: CALL(2); break;          \
+        case 3: CALL(3); break;          \
+        case 4: CALL(4); break;          \
+        case 5: CALL(5); break;          \
+        case 6: CALL(6); break;          \
+        case 7: CALL(7); break;          \
+        case 8: CALL(8); break;          \
+        default: CALL(9); break;         \
+    }
 
 template <bool FAST>
 __global__ __launch_bounds__(kResThreads) void k_persist_res(PersistArgs a) {
     extern __shared__ float lds[];
+    __shared__ uint32_t wmax[kResWaves];
+    __shared__ uint32_t gave_up;  // a wait of this block outlasted the spin budget
+    __shared__ int nbase[8];      // exchange offset of each neighbour's strips (N S W E NW NE SW SE)
     const Geom g = a.g;
     const int N = g.N, P = g.P;
-    const int T = a.tx;  // square tiles
+    const int T = a.tx, H = a.D + 1;  // square tiles; halo one deeper than a chunk
     const int ntx = (N + T - 1) / T;
     const int tile = blockIdx.x;
-    const int tx0 = (tile % ntx) * T, ty0 = (tile / ntx) * T;
+    const int ti = tile / ntx, tj = tile % ntx;
+    const int tx0 = tj * T, ty0 = ti * T;
     const int w = tx0 + T <= N ? T : N - tx0, h = ty0 + T <= N ? T : N - ty0;
-    const int lp = w + 2, lh = h + 2;
-    float* U[2] = {lds, lds + (T + 2) * (T + 2)};
-    float* BL = lds + 2 * (T + 2) * (T + 2);
-    uint64_t* xbuf = reinterpret_cast<uint64_t*>(a.b);  // edge exchange (see above)
+    const int lp = w + 2 * H, lh = h + 2 * H;  // region pitch and height
+    // LDS: iterates at [0, R) and [R, 2R), s at [2R, 3R), the dummy word at 3R
+    const int R = (T + 2 * H) * (T + 2 * H), dummy = 3 * R;
     const float r = a.r, d = a.d, y = a.y;
-    // neighbours: 0 north, 1 south, 2 west, 3 east (-1: none)
-    const int nb_n = ty0 > 0 ? tile - ntx : -1, nb_s = ty0 + T < N ? tile + ntx : -1;
-    const int nb_w = tx0 > 0 ? tile - 1 : -1, nb_e = tx0 + T < N ? tile + 1 : -1;
+    const int tid = threadIdx.x;
+    if (tid == 0) gave_up = 0;
 
-    // stage u^n with its halo (ghost ring included) into both buffers, s into registers
+    // the region of u^n (ghost ring and padding included) into both buffers,
+    // s of its unknowns beside them
     {
-        const float* src = (a.cur0 ? a.u1 : a.u0) + g.origin + (int64_t)(ty0 - 1) * P + (tx0 - 1);
-        for (int k = threadIdx.x; k < lp * lh; k += kResThreads) {
+        const float* src = (a.cur0 ? a.u1 : a.u0) + g.origin + (int64_t)(ty0 - H) * P + (tx0 - H);
+        for (int k = tid; k < lp * lh; k += kResThreads) {
             const int rr = k / lp, cc = k - rr * lp;
+            const int gi = ty0 - H + rr, gj = tx0 - H + cc;
             const float v = src[(int64_t)rr * P + cc];
-            U[0][rr * lp + cc] = v;
-            U[1][rr * lp + cc] = v;
+            lds[k] = v;
+            lds[R + k] = v;
+            lds[2 * R + k] = (gi >= 0 && gi < N && gj >= 0 && gj < N) ? a.s[g.origin + (int64_t)gi * P + gj] : 0.0f;
         }
     }
-    float sv[kResCellsPerThread];
-    int cell[kResCellsPerThread];  // LDS index of each core cell of this thread (-1: none)
+    // this thread's cells of the region's interior (inner cell k = tid +
+    // q*kResThreads, row 1 + k / (lp-2), column 1 + k % (lp-2)): the byte offset
+    // of its west neighbour and its bits; a lane past the interior keeps an
+    // interior cell's offset and no bits
+    const int nin = (lp - 2) * (lh - 2);
+    const int nq = (nin + kResThreads - 1) / kResThreads;
+    int at[kResCells];
+    uint32_t info[kResCells];
 #pragma unroll
-    for (int q = 0; q < kResCellsPerThread; ++q) {
-        const int k = threadIdx.x + q * kResThreads;
-        cell[q] = -1;
-        sv[q] = 0.0f;
-        if (k < w * h) {
-            const int i = k / w, j = k - i * w;
-            cell[q] = (i + 1) * lp + (j + 1);
-            sv[q] = a.s[g.origin + (int64_t)(ty0 + i) * P + (tx0 + j)];
+    for (int q = 0; q < kResCells; ++q) {
+        const int k = tid + q * kResThreads;
+        const int kk = k < nin ? k : 0;
+        const int rr = 1 + kk / (lp - 2), cc = 1 + kk % (lp - 2);
+        const int gi = ty0 - H + rr, gj = tx0 - H + cc;
+        at[q] = (rr * lp + cc - 1) * 4;
+        info[q] = 0;
+        if (k < nin && gi >= 0 && gi < N && gj >= 0 && gj < N) {
+            info[q] = kCellUnk;
+            if (rr >= H && rr < H + h && cc >= H && cc < H + w) info[q] |= kCellCore;
+            if (gi == 0) info[q] |= kCellTop;
+        }
+    }
+    // the exchange maps in LDS: per strip word this block publishes, LDS cell
+    // << 16 | slot; per halo word it takes, neighbour << 27 | slot << 14 | LDS
+    // cell (all ones: a ghost cell)
+    const int HT = H * T;
+    const int npub = 2 * H * w + 2 * h * H, nref = npub + 4 * H * H;
+    uint32_t* pubmap = reinterpret_cast<uint32_t*>(lds + dummy + 1);
+    uint32_t* refmap = pubmap + 4 * HT;
+    if (tid < 8) {
+        const int di = (tid == 0 || tid == 4 || tid == 5) ? -1 : (tid == 1 || tid == 6 || tid == 7) ? 1 : 0;
+        const int dj = (tid == 2 || tid == 4 || tid == 6) ? -1 : (tid == 3 || tid == 5 || tid == 7) ? 1 : 0;
+        nbase[tid] = ((ti + di) * ntx + (tj + dj)) * 8 * HT;  // used only where that neighbour exists
+    }
+    {
+        const int nrow = H * w, ncol = h * H;
+        for (int q = tid; q < npub; q += kResThreads) {
+            int src, slot;
+            if (q < nrow) {  // top H rows of the core
+                const int i = q / w, j = q - i * w;
+                src = (H + i) * lp + H + j;
+                slot = i * T + j;
+            } else if (q < 2 * nrow) {  // bottom H rows
+                const int qq = q - nrow, i = qq / w, j = qq - i * w;
+                src = (h + i) * lp + H + j;
+                slot = HT + i * T + j;
+            } else if (q < 2 * nrow + ncol) {  // left H columns
+                const int qq = q - 2 * nrow, i = qq / H, j = qq - i * H;
+                src = (H + i) * lp + H + j;
+                slot = 2 * HT + i * H + j;
+            } else {  // right H columns
+                const int qq = q - 2 * nrow - ncol, i = qq / H, j = qq - i * H;
+                src = (H + i) * lp + w + j;
+                slot = 3 * HT + i * H + j;
+            }
+            pubmap[q] = ((uint32_t)src << 16) | (uint32_t)slot;
+        }
+        const int ncor = H * H;
+        auto has = [&](int di, int dj) {
+            const int i = ti + di, j = tj + dj;
+            return i >= 0 && i < ntx && j >= 0 && j < ntx;
+        };
+        for (int q = tid; q < nref; q += kResThreads) {
+            int dir, slot, dst;
+            bool ok;
+            if (q < nrow) {  // north neighbour's bottom rows -> halo rows 0..H-1
+                const int i = q / w, j = q - i * w;
+                dir = 0; ok = has(-1, 0); slot = HT + i * T + j; dst = i * lp + H + j;
+            } else if (q < 2 * nrow) {  // south's top rows -> rows H+h..
+                const int qq = q - nrow, i = qq / w, j = qq - i * w;
+                dir = 1; ok = has(1, 0); slot = i * T + j; dst = (H + h + i) * lp + H + j;
+            } else if (q < 2 * nrow + ncol) {  // west's right columns -> columns 0..H-1
+                const int qq = q - 2 * nrow, i = qq / H, j = qq - i * H;
+                dir = 2; ok = has(0, -1); slot = 3 * HT + i * H + j; dst = (H + i) * lp + j;
+            } else if (q < 2 * nrow + 2 * ncol) {  // east's left columns -> columns H+w..
+                const int qq = q - 2 * nrow - ncol, i = qq / H, j = qq - i * H;
+                dir = 3; ok = has(0, 1); slot = 2 * HT + i * H + j; dst = (H + i) * lp + H + w + j;
+            } else {  // corners: the diagonal neighbours' bottom / top rows
+                const int qq = q - 2 * nrow - 2 * ncol, c4 = qq / ncor, i = (qq - c4 * ncor) / H,
+                          j = qq - c4 * ncor - i * H;
+                dir = 4 + c4;
+                if (c4 == 0) {         // north-west: bottom rows, last H columns (a full-width tile)
+                    ok = has(-1, -1); slot = HT + i * T + (T - H + j); dst = i * lp + j;
+                } else if (c4 == 1) {  // north-east: bottom rows, first H columns
+                    ok = has(-1, 1); slot = HT + i * T + j; dst = i * lp + H + w + j;
+                } else if (c4 == 2) {  // south-west: top rows, last H columns
+                    ok = has(1, -1); slot = i * T + (T - H + j); dst = (H + h + i) * lp + j;
+                } else {               // south-east: top rows, first H columns
+                    ok = has(1, 1); slot = i * T + j; dst = (H + h + i) * lp + H + w + j;
+                }
+            }
+            refmap[q] = ok ? ((uint32_t)dir << 27) | ((uint32_t)slot << 14) | (uint32_t)dst : 0xFFFFFFFFu;
         }
     }
     __syncthreads();
+    uint64_t* xbuf = a.xchg;
+    uint64_t* part64 = reinterpret_cast<uint64_t*>(a.partial);  // 2 x grid tagged words
+    const int G = gridDim.x;
     int cur = 0;            // LDS buffer holding the current iterate
     int red = 0;            // reductions so far: selects the partial buffer, tags the next
-    uint32_t serial = 0;    // sweeps published by this block in this solve
+    uint32_t serial = 0;    // chunks published by this block in this solve
     uint32_t bA_bits = 0;
-    uint64_t* part64 = reinterpret_cast<uint64_t*>(a.partial);  // 2 x grid tagged words
     int status = 1;
+    float bv[kResCells];    // b of this thread's cells
     for (int step = 0; step < a.nsteps; ++step) {
-        // ---- b = u^n + s on the core, partial max |b + r*g|
+        // ---- b = u^n + s on the region's unknowns, max |b + r*g| on the core
         {
+            __syncthreads();  // every thread has read the last reduction from wmax
+            const int ob4 = cur * R * 4;
             uint32_t m = 0;
 #pragma unroll
-            for (int q = 0; q < kResCellsPerThread; ++q) {
-                if (cell[q] < 0) continue;
-                const int i = ty0 + (cell[q] / lp - 1);
-                const float bb = U[cur][cell[q]] + sv[q];
-                BL[cell[q]] = bb;
-                const float rg = r * (i == 0 ? kTop : 0.0f);
-                const uint32_t v = __float_as_uint(fabsf(bb + rg));
-                m = m > v ? m : v;
+            for (int q = 0; q < kResCells; ++q) {
+                bv[q] = 0.0f;
+                if (!(info[q] & kCellUnk)) continue;
+                bv[q] = lds_at(lds, at[q] + ob4 + 4) + lds_at(lds, at[q] + 2 * R * 4 + 4);
+                if (info[q] & kCellCore) {
+                    float tg = kTop;
+                    asm volatile("" : "+v"(tg));
+                    const float rg = r * ((info[q] & kCellTop) ? tg : 0.0f);
+                    const uint32_t v = __float_as_uint(fabsf(bv[q] + rg));
+                    m = m > v ? m : v;
+                }
             }
-            if (!tagged_max(part64, red & 1, (uint32_t)red + 1u, m, a.sc, &bA_bits)) return;
+            block_max_put(wmax, m);
+            __syncthreads();
+            if (tid == 0)
+                __hip_atomic_store(&part64[(int64_t)(red & 1) * G + blockIdx.x],
+                                   ((uint64_t)(red + 1) << 32) | block_max_get(wmax), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            int off[kResPoll];
+            uint64_t x[kResPoll];
+#pragma unroll
+            for (int q = 0; q < kResPoll; ++q) {
+                const int i = tid + q * kResThreads;
+                off[q] = i < G ? (red & 1) * G + i : -1;
+            }
+            if (!poll_tagged<0, kResPoll>(nullptr, nullptr, 0u, nullptr, part64, off, (uint32_t)red + 1u, x, a.sc))
+                gave_up = 1;
+            uint32_t v = 0;
+#pragma unroll
+            for (int q = 0; q < kResPoll; ++q) v = off[q] >= 0 && (uint32_t)x[q] > v ? (uint32_t)x[q] : v;
+            __syncthreads();  // wmax read by thread 0 above
+            block_max_put(wmax, v);
+            __syncthreads();
+            bA_bits = block_max_get(wmax);
+            if (gave_up) return;
             ++red;
         }
         const float bA = __uint_as_float(bA_bits);
         int64_t k = 0;
+        int done = 0;
         uint32_t R_bits = 0;
         status = 1;
         for (;;) {
-            if (k > 0 && k % a.L == 0) {
-                // check: the residual of u_k on the core (the halo holds the neighbours' u_k)
-                const float* A = U[cur];
-                uint32_t m = 0;
+            const int left = a.L - done;
+            const int Dc = a.D < left ? a.D : left;
+            // ---- Dc sweeps; the exact region shrinks by a cell per sweep
+#define JAC_RES_SWEEPS(NQ) cur = res_sweeps<FAST, NQ>(lds, cur, Dc, R, lp * 4, at, info, bv, r, d, y)
+            JAC_RES_NQ(JAC_RES_SWEEPS)
+#undef JAC_RES_SWEEPS
+            k += Dc;
+            done += Dc;
+            if (done == a.L) done = 0;
+            ++serial;
+            const int ob = cur * R;
+            const bool check = done == 0;
+            // ---- publish the core's H-deep edge strips, tagged with the chunk number
+            {
+                uint64_t* e = xbuf + ((int64_t)tile * 2 + (serial & 1)) * 4 * HT;
+                const uint64_t tag = (uint64_t)serial << 32;
 #pragma unroll
-                for (int q = 0; q < kResCellsPerThread; ++q) {
-                    if (cell[q] < 0) continue;
-                    const int c = cell[q];
-                    const uint32_t v = residual_bits(A[c], A[c + 1], A[c - 1], A[c - lp], A[c + lp], BL[c], r);
-                    m = m > v ? m : v;
+                for (int q = 0; q < kResPub; ++q) {
+                    const int i = tid + q * kResThreads;
+                    if (i >= npub) break;
+                    const uint32_t m = pubmap[i];
+                    __hip_atomic_store(&e[m & 0xFFFFu], tag | __float_as_uint(lds[ob + (int)(m >> 16)]),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                if (!tagged_max(part64, red & 1, (uint32_t)red + 1u, m, a.sc, &R_bits)) return;
+            }
+            // ---- a check: the residual of u_k on the core (its ring is exact);
+            // the block's partial goes out before the halo wait
+            if (check) {
+                uint32_t m = 0;
+#define JAC_RES_CHECK(NQ) m = res_check<NQ>(lds, ob * 4, lp * 4, at, info, bv, r)
+                JAC_RES_NQ(JAC_RES_CHECK)
+#undef JAC_RES_CHECK
+                block_max_put(wmax, m);
+                __syncthreads();
+                if (tid == 0)
+                    __hip_atomic_store(&part64[(int64_t)(red & 1) * G + blockIdx.x],
+                                       ((uint64_t)(red + 1) << 32) | block_max_get(wmax), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+            // ---- refill the halo from the neighbours' strips of this chunk, and
+            // at a check take every block's partial: all words in flight at once
+            uint32_t pv = 0;
+            {
+                const int par = (int)(serial & 1) * 4 * HT;
+                int off1[kResRef], off2[kResPoll], dst1[kResRef];
+                uint64_t x1[kResRef], x2[kResPoll];
+#pragma unroll
+                for (int q = 0; q < kResRef; ++q) {
+                    const int i = tid + q * kResThreads;
+                    const uint32_t m = i < nref ? refmap[i] : 0xFFFFFFFFu;
+                    off1[q] = m == 0xFFFFFFFFu ? -1 : nbase[m >> 27] + par + (int)((m >> 14) & 8191u);
+                    dst1[q] = m == 0xFFFFFFFFu ? dummy : ob + (int)(m & 16383u);
+                }
+#pragma unroll
+                for (int q = 0; q < kResPoll; ++q) {
+                    const int i = tid + q * kResThreads;
+                    off2[q] = check && i < G ? (red & 1) * G + i : -1;
+                }
+                if (!poll_tagged<kResRef, kResPoll>(xbuf, off1, serial, x1, part64, off2, (uint32_t)red + 1u, x2,
+                                                    a.sc))
+                    gave_up = 1;
+#pragma unroll
+                for (int q = 0; q < kResRef; ++q)
+                    lds[dst1[q]] = __uint_as_float((uint32_t)x1[q]);
+#pragma unroll
+                for (int q = 0; q < kResPoll; ++q) pv = off2[q] >= 0 && (uint32_t)x2[q] > pv ? (uint32_t)x2[q] : pv;
+            }
+            if (check) {
+                __syncthreads();  // thread 0 has read wmax
+                block_max_put(wmax, pv);
+            }
+            __syncthreads();
+            if (gave_up) return;
+            if (check) {
+                R_bits = block_max_get(wmax);
                 ++red;
                 const float rho = __uint_as_float(R_bits) / bA;
                 if (!(rho >= a.tol)) {
@@ -520,67 +811,6 @@ __global__ __launch_bounds__(kResThreads) void k_persist_res(PersistArgs a) {
                     break;
                 }
             }
-            // ---- one sweep of the core into the other buffer
-            {
-                const float* A = U[cur];
-                float* Bn = U[cur ^ 1];
-#pragma unroll
-                for (int q = 0; q < kResCellsPerThread; ++q) {
-                    if (cell[q] < 0) continue;
-                    const int c = cell[q];
-                    Bn[c] = jacobi_update<FAST>(A[c + 1], A[c - 1], A[c - lp], A[c + lp], BL[c], r, d, y);
-                }
-            }
-            __syncthreads();
-            cur ^= 1;
-            ++k;
-            ++serial;
-            // ---- publish this tile's new edges, tagged with the sweep number
-            {
-                const float* A = U[cur];
-                uint64_t* e = res_edges(xbuf, tile, serial & 1, T);
-                const uint64_t tag = (uint64_t)serial << 32;
-                for (int q = threadIdx.x; q < 2 * (w + h); q += kResThreads) {
-                    float v;
-                    int slot;
-                    if (q < w) { v = A[1 * lp + 1 + q]; slot = q; }                                    // top row
-                    else if (q < 2 * w) { v = A[h * lp + 1 + (q - w)]; slot = T + (q - w); }            // bottom row
-                    else if (q < 2 * w + h) { v = A[(1 + q - 2 * w) * lp + 1]; slot = 2 * T + (q - 2 * w); }  // left
-                    else { v = A[(1 + q - 2 * w - h) * lp + w]; slot = 3 * T + (q - 2 * w - h); }           // right
-                    __hip_atomic_store(&e[slot], tag | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-            // ---- take the neighbours' edges of this sweep into the halo:
-            // north's bottom row -> halo row 0, south's top row -> row h+1,
-            // west's right column -> column 0, east's left column -> column w+1
-            {
-                float* A = U[cur];
-                for (int q = threadIdx.x; q < 2 * (w + h); q += kResThreads) {
-                    int nbv, slot, dst;
-                    if (q < w) { nbv = nb_n; slot = T + q; dst = 0 * lp + 1 + q; }
-                    else if (q < 2 * w) { nbv = nb_s; slot = q - w; dst = (h + 1) * lp + 1 + (q - w); }
-                    else if (q < 2 * w + h) { nbv = nb_w; slot = 3 * T + (q - 2 * w); dst = (1 + q - 2 * w) * lp; }
-                    else { nbv = nb_e; slot = 2 * T + (q - 2 * w - h); dst = (1 + q - 2 * w - h) * lp + w + 1; }
-                    if (nbv < 0) continue;  // a ghost cell: it keeps its fixed value
-                    const uint64_t* src = res_edges(xbuf, nbv, serial & 1, T) + slot;
-                    uint64_t x;
-                    uint32_t spins = 0;
-                    for (;;) {
-                        x = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if ((uint32_t)(x >> 32) == serial) break;
-                        if ((++spins & 1023u) == 0u &&
-                            (__hip_atomic_load(&a.sc->bar_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
-                             spins > kBarrierSpins)) {
-                            __hip_atomic_store(&a.sc->bar_error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
-                    A[dst] = __uint_as_float((uint32_t)x);
-                }
-            }
-            __syncthreads();
-            if (__hip_atomic_load(&a.sc->bar_error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
         }
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             PersistOut o;
@@ -596,11 +826,10 @@ __global__ __launch_bounds__(kResThreads) void k_persist_res(PersistArgs a) {
     // the field: the core of the current iterate, into the buffer u^n came from
     {
         float* dst = (a.cur0 ? a.u1 : a.u0) + g.origin + (int64_t)ty0 * P + tx0;
-#pragma unroll
-        for (int q = 0; q < kResCellsPerThread; ++q) {
-            if (cell[q] < 0) continue;
-            const int i = cell[q] / lp - 1, j = cell[q] - (i + 1) * lp - 1;
-            dst[(int64_t)i * P + j] = U[cur][cell[q]];
+        const int ob = cur * R;
+        for (int k = tid; k < w * h; k += kResThreads) {
+            const int i = k / w, j = k - i * w;
+            dst[(int64_t)i * P + j] = lds[ob + (H + i) * lp + H + j];
         }
     }
 }
@@ -647,8 +876,9 @@ hipError_t persist_plan(int N, int D, bool async_mode, int tile_x, int tile_y, i
 }
 
 hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, const float* s, uint32_t* partial,
-                          void* out, int nsteps, int cur0, bool async_mode, int D, int L, int tile_x, int tile_y,
-                          int side, int64_t max_sweeps, int cus, int* grid_used, hipStream_t stream) {
+                          uint64_t* xchg, int64_t xchg_words, void* out, int nsteps, int cur0, bool async_mode, int D,
+                          int L, int tile_x, int tile_y, int side, int64_t max_sweeps, int cus, int* grid_used,
+                          hipStream_t stream) {
     PersistPlan p;
     hipError_t e = persist_plan(sa.g.N, D, async_mode, tile_x, tile_y, side, sa.fastdiv != 0, cus, &p);
     if (e != hipSuccess) return e;
@@ -663,6 +893,7 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
     a.b = b;
     a.s = s;
     a.partial = partial;
+    a.xchg = xchg;
     a.out = reinterpret_cast<PersistOut*>(out);
     a.nsteps = nsteps;
     a.cur0 = cur0;
@@ -674,24 +905,44 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
     a.lds_cells = p.cells;
     a.sc = sa.sc;
     a.max_sweeps = max_sweeps;
-    // The synchronous sweep on a grid whose tiles all fit one round: resident
-    // tiles (k_persist_res); otherwise re-staged tiles (k_persist).
+    // The exact kernels on a grid whose tiles all fit one round of co-resident
+    // blocks: resident tiles (k_persist_res); otherwise re-staged tiles
+    // (k_persist).  Resident tiles are square, side T: the band_rows option, else
+    // the smallest of 16, 32, 64 that fits (smaller tiles put more CUs on the
+    // grid).  A tile is at least H = D + 1 cells on each side (a ragged last
+    // tile too), the region's interior (T + 2H - 2)^2 fits the block's cells,
+    // the region and the exchange maps its LDS, the exchange its words.
     bool resident = false;
     int rgrid = 0, T = 0;
+    const int H = D + 1;
     size_t rlds = 0;
-    if (!async_mode && D == 1) {
-        T = side > 0 ? side : (sa.g.N <= 384 ? 32 : 64);
-        const int64_t nt = (int64_t)((sa.g.N + T - 1) / T) * ((sa.g.N + T - 1) / T);
-        rlds = (size_t)3 * (T + 2) * (T + 2) * sizeof(float);
-        int per_cu = 0;
-        if (T >= 1 && T * T <= kResThreads * kResCellsPerThread &&
-            (sa.fastdiv ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_persist_res<true>, kResThreads, rlds)
-                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_persist_res<false>, kResThreads,
-                                                                       rlds)) == hipSuccess &&
-            per_cu > 0 && nt <= (int64_t)cus * per_cu && nt <= kMaxPersistBlocks &&
-            2 * resident_exchange_words((int)nt, T) <= sa.g.plane) {  // the edge exchange fits the b plane
-            resident = true;
-            rgrid = (int)nt;
+    if (!async_mode) {
+        const int N = sa.g.N;
+        int dev = 0, max_lds = 0;
+        const bool have_lds = hipGetDevice(&dev) == hipSuccess &&
+                              hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
+                                  hipSuccess;
+        const int sides[3] = {16, 32, 64};
+        for (int si = 0; si < 3 && !resident && have_lds; ++si) {
+            T = side > 0 ? side : sides[si];
+            const int64_t nt = (int64_t)((N + T - 1) / T) * ((N + T - 1) / T);
+            const int R = (T + 2 * H) * (T + 2 * H);
+            // two iterates, s, a dummy word, the publish and refill maps
+            rlds = (size_t)(3 * R + 1 + 8 * H * T + 4 * H * H) * sizeof(float);
+            int per_cu = 0;
+            if (H <= T && (N % T == 0 || N % T >= H) && (T + 2 * H - 2) * (T + 2 * H - 2) <= kResThreads * kResCells &&
+                4 * H * T <= kResThreads * kResPub && 4 * H * T + 4 * H * H <= kResThreads * kResRef &&
+                rlds <= (size_t)max_lds &&
+                (sa.fastdiv
+                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_persist_res<true>, kResThreads, rlds)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_persist_res<false>, kResThreads,
+                                                                    rlds)) == hipSuccess &&
+                per_cu > 0 && nt <= (int64_t)cus * per_cu && nt <= kMaxPersistBlocks &&
+                resident_exchange_words((int)nt, H, T) <= xchg_words) {
+                resident = true;
+                rgrid = (int)nt;
+            }
+            if (side > 0) break;
         }
     }
     if (resident) {
@@ -707,7 +958,7 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
                         stream);
     // tags of an earlier solve must not match: clear the exchange words
     if (e == hipSuccess && resident)
-        e = launch_fill(b, 2 * resident_exchange_words(rgrid, T), 0.0f, stream);
+        e = launch_fill(reinterpret_cast<float*>(xchg), 2 * resident_exchange_words(rgrid, H, T), 0.0f, stream);
     if (e == hipSuccess && resident)  // the 2 x grid tagged partial words
         e = launch_fill(reinterpret_cast<float*>(partial), 4 * (int64_t)rgrid, 0.0f, stream);
     if (e != hipSuccess) return e;

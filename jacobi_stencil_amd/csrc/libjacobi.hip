@@ -122,6 +122,7 @@ struct jac_ctx {
     float* s;
     Scratch* sc;
     int64_t npart_cap;
+    uint64_t* xchg;          // edge exchange of the persistent kernel's resident tiles
     Scratch* static_sc;      // this device's copy of the static scratch array (jac_sweep_static)
     hipError_t static_err;   // why it is missing, if it is
     Mailbox* mail;   // pinned host memory written by the device
@@ -778,12 +779,12 @@ int run_persistent(jac_ctx* c, const jac_opts* o, int nsteps, int64_t* sweeps, f
     int grid = 0;
     c->cur_group = -1;
     int st = timed(c, KC_PERSIST, [&] {
-        return launch_persist(a, c->u[0], c->u[1], c->b, c->s, scratch_partials(c->sc), c->pout, nsteps, c->cur,
-                              async_mode, D, L, o->tile_x, o->tile_y, o->band_rows, o->max_sweeps, c->cus, &grid,
-                              c->stream);
+        return launch_persist(a, c->u[0], c->u[1], c->b, c->s, scratch_partials(c->sc), c->xchg,
+                              exchange_words_cap(c->g.N), c->pout, nsteps, c->cur, async_mode, D, L, o->tile_x,
+                              o->tile_y, o->band_rows, o->max_sweeps, c->cus, &grid, c->stream);
     });
     if (st) return st;
-    if (2 * (int64_t)grid > c->npart_cap) return fail(JAC_EDEVICE, "persistent grid exceeds partial slots");
+    if (4 * (int64_t)grid > c->npart_cap) return fail(JAC_EDEVICE, "persistent grid exceeds partial slots");
     JAC_HIP(hipStreamSynchronize(c->stream));
     uint32_t bar_error = 0;
     JAC_HIP(hipMemcpy(&bar_error, &c->sc->bar_error, 4, hipMemcpyDeviceToHost));
@@ -836,8 +837,8 @@ void jac_opts_default(jac_opts* o) {
 size_t jac_workspace_bytes(int N) {
     if (N < 1 || N > kMaxN) return 0;
     Geom g = make_geom(N);
-    size_t bytes = (size_t)g.plane * 4 * sizeof(float) + sizeof(Scratch) +
-                   (size_t)kMaxPersistBlocks * kFlagStride * 4 + (size_t)partial_cap(N) * 4;
+    const size_t bytes =
+        (size_t)exchange_offset_floats(g, partial_cap(N)) * sizeof(float) + (size_t)exchange_words_cap(N) * 8;
     return (bytes + 255) / 256 * 256;
 }
 
@@ -904,6 +905,7 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
     c->s = base + 3 * c->g.plane;
     c->sc = (Scratch*)(base + 4 * c->g.plane);
     c->npart_cap = partial_cap(N);
+    c->xchg = reinterpret_cast<uint64_t*>(base + exchange_offset_floats(c->g, c->npart_cap));
     c->static_sc = nullptr;
     c->static_err = hipErrorInvalidDevice;
     if (dev >= 0 && dev < kMaxDevices) {

@@ -247,7 +247,7 @@ def study_launches(a):
              ("async_D1_32x16", "async", dict(kernel=jac.JAC_ASYNC, D=1, tile_x=32, tile_y=16)),
              ("async_D8_32x16", "async", dict(kernel=jac.JAC_ASYNC, D=8, tile_x=32, tile_y=16)),
              ("temporal_D8", "tblock", dict(kernel=jac.JAC_TBLOCK, D=8))]
-    for N in (256, 512):
+    for N in (256, 512, 1024):
         for name, kc, o in cases:
             for driver in (jac.JAC_LAUNCH, jac.JAC_GRAPH, jac.JAC_PERSISTENT):
                 rec = R.run(N, 10.0, 10, driver=driver, **o)

@@ -48,12 +48,15 @@ def test_workspace_bytes():
     n1 = jac.jac_workspace_bytes(1)
     assert n1 > 0 and n1 % 256 == 0
     # four planes of (N+128) rows, pitch rounded to 64 floats, a 256-byte scratch
-    # header, 2048 barrier flag lines of 128 bytes, and one partial-maximum slot
-    # per 64 unknowns plus 65536
-    N = 8192
-    P = (N + 128 + 63) // 64 * 64
-    want = 4 * 4 * P * (N + 128) + 256 + 4 * 2048 * 32 + 4 * (N * N // 64 + 65536)
-    assert jac.jac_workspace_bytes(N) == (want + 255) // 256 * 256
+    # header, 2048 barrier flag lines of 128 bytes, one partial-maximum slot
+    # per 64 unknowns plus 65536, then (from a 256-byte boundary) the resident
+    # tiles' exchange: min(5 Mi, 5 (N+31)^2) words of 8 bytes
+    for N in (8192, 256, 33):
+        P = (N + 128 + 63) // 64 * 64
+        head = 4 * 4 * P * (N + 128) + 256 + 4 * 2048 * 32 + 4 * (N * N // 64 + 65536)
+        head = (head + 255) // 256 * 256
+        want = head + 8 * min(5 << 20, 5 * (N + 31) ** 2)
+        assert jac.jac_workspace_bytes(N) == (want + 255) // 256 * 256, N
 
 
 @pytest.mark.parametrize("N,r,ws", [(0, 1.0, 1 << 20), (-3, 1.0, 1 << 20), (65537, 1.0, 1 << 20),

@@ -55,13 +55,16 @@ def test_config_c5_bitwise(kernel, D, r):
     assert_same(lib_solve(256, r, s, 10, opts(kernel=kernel, D=D, driver=PER)), ref, f"C5 {kernel} r={r}")
 
 
-@pytest.mark.parametrize("N,side", [(700, 0), (1024, 0), (300, 16), (33, 8), (300, 88), (1500, 0)])
+@pytest.mark.parametrize("N,side", [(700, 0), (1024, 0), (300, 16), (33, 8), (300, 88), (300, 100), (1500, 0),
+                                    (256, 0), (2, 0), (1, 0)])
 def test_sync_resident_and_staged_tiles_bitwise(N, side):
     """The synchronous sweep under the persistent driver takes resident tiles
-    (each block keeps its tile in LDS and trades edges with its neighbours)
-    where every tile fits one round -- automatic 32- or 64-cell tiles up to
-    N = 1024, 16- and 8-cell tiles -- and re-staged tiles otherwise (88-cell
-    tiles, N = 1500); both are the oracle's bits."""
+    (each block keeps its tile and a two-cell halo in LDS and trades edges with
+    its neighbours after every sweep) where every tile fits one round --
+    automatic 16-, 32- or 64-cell tiles up to N = 1024, 16-, 8- and 88-cell
+    tiles, a lone 2 x 2 tile -- and re-staged tiles otherwise (100-cell tiles
+    whose interior exceeds the block's cells, N = 1500, N = 1); both are the
+    oracle's bits."""
     r = 10.0
     say("persist sync tiles", N, side)
     s = workloads.gaussian_source(N, r)
@@ -82,6 +85,45 @@ def test_sync_resident_nan_and_noconv():
     ref = oracle.solve(N, r, s, u0=u0, steps=2)
     assert ref.status == oracle.ENAN
     assert_same(lib_solve(N, r, s, 2, opts(driver=PER), u0=u0), ref, "nan")
+
+
+@pytest.mark.parametrize("N,side,D", [(101, 32, 4), (100, 32, 4), (256, 16, 15), (40, 8, 7), (256, 0, 8),
+                                      (700, 0, 8), (1024, 0, 5), (1500, 0, 4), (257, 0, 16), (40, 8, 8)])
+def test_tblock_resident_and_staged_tiles_bitwise(N, side, D):
+    """Temporal blocking under the persistent driver keeps each tile and a
+    halo H = D + 1 cells deep in LDS and takes the halo from its eight
+    neighbours after every D sweeps where all tiles fit one round and every
+    tile is at least H cells on a side: a ragged tile of exactly H (N = 101),
+    tiles of side H (256, 16, 15 and 40, 8, 7), automatic 16-cell tiles
+    (256), 64-cell tiles with an 82-cell region (700, 1024).  A ragged tile
+    under H (N = 100, 257), a tile side under H (40, 8, 8) or more tiles than
+    one round (1500) takes re-staged tiles.  Both are the oracle's bits."""
+    r = 10.0
+    say("persist tblock tiles", N, side, D)
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=2, M=max(8, D))
+    got = lib_solve(N, r, s, 2, opts(kernel=jac.JAC_TBLOCK, D=D, driver=PER, band_rows=side))
+    assert_same(got, ref, f"N={N} side={side} D={D}")
+
+
+@pytest.mark.parametrize("D", [3, 5, 8])
+def test_tblock_resident_nan_and_noconv(D):
+    """A failed step ends the resident temporal-blocking solve with the
+    oracle's status and field, also where the sweep limit falls inside an
+    interval of partial chunks (D = 3, 5 against an interval of 8)."""
+    N, r = 200, 10.0
+    say("persist tblock resident noconv/nan", D)
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=2, M=8, max_sweeps=40)
+    assert ref.status == oracle.ENOCONV
+    got = lib_solve(N, r, s, 2, opts(kernel=jac.JAC_TBLOCK, D=D, driver=PER, max_sweeps=40))
+    assert_same(got, ref, f"noconv D={D}")
+    u0 = np.zeros((N, N), np.float32)
+    u0[N // 3, N // 2] = np.inf
+    ref = oracle.solve(N, r, s, u0=u0, steps=2, M=8)
+    assert ref.status == oracle.ENAN
+    got = lib_solve(N, r, s, 2, opts(kernel=jac.JAC_TBLOCK, D=D, driver=PER), u0=u0)
+    assert_same(got, ref, f"nan D={D}")
 
 
 def test_config_c1_bitwise():
