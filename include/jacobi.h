@@ -73,7 +73,11 @@ enum jac_checks {
                                    residual pass alone; if it does not converge, the interval it
                                    skipped follows.  Results never depend on this.  Environment
                                    variable JACOBI_PREDICT_MARGIN=m at create time replaces 0.97
-                                   (0 turns the prediction off) */
+                                   (0 turns the prediction off).  TBLOCK with D >= 9 and D > M under
+                                   LAUNCH: launches of up to D sweeps measure the residual of the
+                                   levels where checks fall (at most two); a check that stops at an
+                                   inner level is followed by a launch that recomputes that iterate
+                                   from the launch's input; a launch ends on a predicted check */
     JAC_CHECKS_BLOCKING = 1     /* after each interval a standalone residual kernel, then the host waits
                                    for R and decides before anything more is queued */
 };
@@ -114,7 +118,9 @@ typedef struct {
     int32_t D;           /* sweeps per launch: TBLOCK 1..16, ASYNC 1..32; ignored for SYNC */
     int32_t tile_x;      /* ASYNC tile width in columns (1..256; tile_x * tile_y <= 4096) */
     int32_t tile_y;      /* ASYNC tile height in rows (1..256) */
-    int32_t M;           /* check interval in sweeps (>= 1); the interval is max(M, D) */
+    int32_t M;           /* check interval in sweeps (>= 1).  SYNC and TBLOCK check every M sweeps
+                            whatever D (a TBLOCK launch deeper than M measures the residual at the
+                            levels where checks fall); ASYNC every max(M, D) */
     float tol;           /* rho threshold (> 0) */
     int32_t band_rows;   /* TBLOCK: rows per wavefront band (LAUNCH; for D >= 5 lowered where a band's rows
                             would span 2 GiB or more, which changes no result), tile side (PERSISTENT);

@@ -25,7 +25,7 @@ JAC_LAUNCH, JAC_GRAPH, JAC_PERSISTENT = 0, 1, 2
 JAC_CHECKS_OVERLAPPED, JAC_CHECKS_BLOCKING = 0, 1
 JAC_STATIC, JAC_G_ASC, JAC_G_DESC, JAC_G_FB = 0, 1, 2, 3
 KCLASS = {"rhs": 0, "sync": 1, "sync_check": 2, "tblock": 3, "async": 4, "residual": 5, "persistent": 6,
-          "noop": 7, "reduce": 8, "tblock_rhs": 9}
+          "noop": 7, "reduce": 8, "tblock_rhs": 9, "tblock_part": 10}
 STATUS_NAMES = {0: "JAC_OK", -1: "JAC_EINVAL", -2: "JAC_ENOMEM", -3: "JAC_EDEVICE", -4: "JAC_ENOCONV",
                 -5: "JAC_ENAN"}
 

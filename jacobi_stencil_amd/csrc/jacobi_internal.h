@@ -117,6 +117,12 @@ struct StepArgs {
     Scratch* sc;
     Mailbox* mail;
     int slot;       // mailbox slot for this kernel's check; < 0: the device's check counter
+    // temporal blocking deeper than 8: the levels whose residual a checking
+    // launch measures (chk[0], and chk[1] or -1); its block maxima go to
+    // partial slots [0, grid) and [grid, 2 grid)
+    int chk[2];
+    int force;         // 1: run even if a check has stopped the step (a redo)
+    int64_t part_off;  // the reduction reads partial slots from here
 };
 
 // ---------------------------------------------------------------- device

@@ -111,7 +111,7 @@ constexpr int kReduceThreads = 1024;
 __global__ __launch_bounds__(kReduceThreads) void k_reduce(int64_t npart, int norm, StepArgs a) {
     Scratch* sc = a.sc;
     if (!norm && sc->stop) return;  // the step stopped at an earlier check
-    const uint32_t* part = scratch_partials(sc);
+    const uint32_t* part = scratch_partials(sc) + a.part_off;
     uint32_t m = 0;
     for (int64_t i = threadIdx.x; i < npart; i += kReduceThreads) {
         const uint32_t v = part[i];

@@ -37,6 +37,7 @@
 // others skip that work.
 #include "jacobi_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace jac {
@@ -285,7 +286,7 @@ using TBIO = typename std::conditional<(D >= 5), TBBufferIO, TBGlobalIO>::type;
 // the "before" rows lie below, so the update and the residual are handed the
 // old and new rows as south and north instead of north and south -- every
 // point sees the same neighbours in the same order either way.
-template <int D, bool CHK, int EK, bool FAST, int DIR, bool RHS>
+template <int D, bool CHK, int EK, bool FAST, int DIR, bool RHS, int CL>
 struct TBStream {
     TBIO<D> io;
     float r, d, y;
@@ -295,6 +296,8 @@ struct TBStream {
     float4 nu, nb;  // row j+1 of u_k and b, loaded one row ahead
     int s;          // ring slot of the current row
     uint32_t m;     // running max |res| (CHK) or |b_A| (RHS), as bits
+    uint32_t m2;    // D >= 9: running max |res| of the second checked level
+    int chk0, chk1; // D >= 9: the checked levels (chk1 < 0: one)
 
     // One row j: read it, push every level one row further, store level D.
     // UP/MID/NEW are the level registers in this row's rotation.
@@ -334,7 +337,23 @@ struct TBStream {
             if (2 * t <= depth) {
                 const float4 bb = bq[t & 1];
                 if (t < D) bq[(t + 1) & 1] = ring[slot(t + 1)][lane];
-                if (CHK && t == 1) {
+                if constexpr (CHK && D >= 9) {
+                    // residual of level t-1 where a check falls, on the row level t
+                    // computes, from the stencil it reads: levels fixed at compile time
+                    // (CL >= 0: C0 = CL & 15, C1 = (CL >> 4) - 1) or passed at run time
+                    constexpr int C0 = CL >= 0 ? (CL & 15) : -1, C1 = CL >= 0 ? (CL >> 4) - 1 : -1;
+                    const bool at0 = CL >= 0 ? (t - 1 == C0) : (t - 1 == chk0);
+                    const bool at1 = CL >= 0 ? (t - 1 == C1) : (t - 1 == chk1);
+                    if (at0 || at1) {
+                        const int i = j - DIR * t;
+                        if (i >= y0 && i <= last) {
+                            const uint32_t v = DIR > 0 ? level_residual(UP[t - 1], MID[t - 1], NEW[t - 1], bb, r, L)
+                                                       : level_residual(NEW[t - 1], MID[t - 1], UP[t - 1], bb, r, L);
+                            if (at0) m = m > v ? m : v;
+                            else m2 = m2 > v ? m2 : v;
+                        }
+                    }
+                } else if (CHK && t == 1) {
                     // residual of u_k on the row level 1 computes, from the stencil it reads
                     const int i = j - DIR;
                     if (i >= y0 && i <= last) {
@@ -356,12 +375,12 @@ struct TBStream {
     }
 };
 
-template <int D, bool CHK, int EK, bool FAST, int DIR, bool RHS>
+template <int D, bool CHK, int EK, bool FAST, int DIR, bool RHS, int CL>
 __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const float* __restrict__ bin,
                                             float* __restrict__ uout, float* __restrict__ bout, const StepArgs& a,
                                             const TBLane& L, int X, bool lane_loads, int y0, int last,
-                                            float4 (*ring)[64]) {
-    TBStream<D, CHK, EK, FAST, DIR, RHS> st;
+                                            float4 (*ring)[64], uint32_t& m2) {
+    TBStream<D, CHK, EK, FAST, DIR, RHS, CL> st;
     st.N = a.g.N;
     st.r = a.r;
     st.d = a.d;
@@ -375,6 +394,9 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     st.ring = ring;
     st.s = 0;
     st.m = 0;
+    st.m2 = 0;
+    st.chk0 = a.chk[0];
+    st.chk1 = a.chk[1];
     const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     st.nu = zero;
     st.nb = zero;
@@ -427,31 +449,37 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
             st.row(j - 2, C, A, B);
         }
     }
+    m2 = st.m2;
     return st.m;
 }
 
-template <int D, bool CHK, bool FAST, int DIR, bool RHS>
+template <int D, bool CHK, bool FAST, int DIR, bool RHS, int CL>
 __device__ __forceinline__ uint32_t tb_band_kind(const float* __restrict__ uin, const float* __restrict__ bin,
                                                  float* __restrict__ uout, float* __restrict__ bout,
                                                  const StepArgs& a, const TBLane& L, int X, bool lane_loads, int y0,
-                                                 int last, float4 (*ring)[64], bool cols, bool rows) {
+                                                 int last, float4 (*ring)[64], bool cols, bool rows, uint32_t& m2) {
     if (cols)
-        return tb_band<D, CHK, kEdgeCols, FAST, DIR, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring);
+        return tb_band<D, CHK, kEdgeCols, FAST, DIR, RHS, CL>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring,
+                                                          m2);
     if (rows)
-        return tb_band<D, CHK, kEdgeRows, FAST, DIR, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring);
-    return tb_band<D, CHK, kEdgeNone, FAST, DIR, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring);
+        return tb_band<D, CHK, kEdgeRows, FAST, DIR, RHS, CL>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring,
+                                                          m2);
+    return tb_band<D, CHK, kEdgeNone, FAST, DIR, RHS, CL>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring,
+                                                      m2);
 }
 
 // Register budget per depth: up to 4, four wavefronts per SIMD (128 VGPRs);
-// 5..8 three (168 VGPRs: the launch sizes its bands for three wavefronts per
-// SIMD anyway); deeper pipelines two.
+// 5..11 three (168 VGPRs: the launch sizes its bands for three wavefronts per
+// SIMD anyway; the pipelines of 9..11 levels fit without spilling); deeper
+// pipelines two.
 template <int D>
-constexpr int tb_waves_per_simd() { return D <= 4 ? 4 : (D <= 8 ? 3 : 2); }
+constexpr int tb_waves_per_simd() { return D <= 4 ? 4 : (D <= 11 ? 3 : 2); }
 
 // RHS (the first launch of a step): bin is s, bout receives b; it runs
 // whatever the stop flag says, since the norm reduction after it clears the
-// flag the previous step left set.
-template <int D, bool CHK, bool FAST, bool RHS>
+// flag the previous step left set.  CL (D >= 9, CHK): the checked levels fixed
+// at compile time (see TBStream::row), or -1 to take them from the arguments.
+template <int D, bool CHK, bool FAST, bool RHS, int CL = -1>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(tb_waves_per_simd<D>())))
 void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
                                                float* __restrict__ uout, StepArgs a, int H,
@@ -459,13 +487,13 @@ void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
     static_assert(!(CHK && RHS), "a launch either checks or forms b");
     constexpr int Dp = (D + 3) & ~3;
     __shared__ float4 ring[D + 1][64];
-    if (!RHS && a.sc->stop) return;  // a previous check already stopped the step
+    if (!RHS && !a.force && a.sc->stop) return;  // a previous check already stopped the step
     const int N = a.g.N;
     const int lane = threadIdx.x;
     const int strips = tb_strip_count(N, Dp);
     const int bands = (N + H - 1) / H;
     const int t = xcd_logical_block(blockIdx.x, gridDim.x);
-    uint32_t m = 0;
+    uint32_t m = 0, m2 = 0;
     if (t < strips * bands) {
         const TBStrip sp = tb_strip(N, Dp, t % strips, strips);
         const int X = sp.X;                  // first column of the window
@@ -493,27 +521,46 @@ void k_tblock(const float* __restrict__ uin, const float* __restrict__ bin,
         // slower (D = 4: 169 -> 182 us, D = 2: 169 -> 177 us).
         if constexpr (D >= 5) {
             if ((t / strips) & 1)
-                m = tb_band_kind<D, CHK, FAST, -1, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring,
-                                                        cols, rows);
+                m = tb_band_kind<D, CHK, FAST, -1, RHS, CL>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring,
+                                                        cols, rows, m2);
             else
-                m = tb_band_kind<D, CHK, FAST, 1, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring,
-                                                       cols, rows);
+                m = tb_band_kind<D, CHK, FAST, 1, RHS, CL>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring,
+                                                       cols, rows, m2);
         } else {
-            m = tb_band_kind<D, CHK, FAST, 1, RHS>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring, cols,
-                                                   rows);
+            m = tb_band_kind<D, CHK, FAST, 1, RHS, CL>(uin, bin, uout, bout, a, L, X, lane_loads, y0, last, ring, cols,
+                                                   rows, m2);
         }
     }
     if (CHK || RHS) store_block_max<1>(m, a.sc, blockIdx.x);
+    if (CHK && D >= 9) store_block_max<1>(m2, a.sc, (int64_t)gridDim.x + blockIdx.x);
 }
 
 // Resident wavefronts per CU for the checking variant of depth D (the one with
 // the most registers), from the runtime's occupancy calculator.
+template <int D, int CL = -1>
+static int tb_waves_per_cu_cl(bool fast) {
+    int n = 0;
+    hipError_t e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tblock<D, true, true, false, CL>, 64, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tblock<D, true, false, false, CL>, 64, 0);
+    return (e == hipSuccess && n > 0) ? n : 4;
+}
+
+// (of every checking kernel a launch of depth D may use: bands sized for more
+// wavefronts than one of them holds would leave a second, partial round)
 template <int D>
 static int tb_waves_per_cu(bool fast) {
-    int n = 0;
-    hipError_t e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tblock<D, true, true, false>, 64, 0)
-                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tblock<D, true, false, false>, 64, 0);
-    return (e == hipSuccess && n > 0) ? n : 4;
+    int n = tb_waves_per_cu_cl<D>(fast);
+    if constexpr (D == 11) {
+        n = std::min(n, tb_waves_per_cu_cl<11, 0 | (9 << 4)>(fast));
+        n = std::min(n, tb_waves_per_cu_cl<11, 1 | (10 << 4)>(fast));
+        n = std::min(n, tb_waves_per_cu_cl<11, 2 | (11 << 4)>(fast));
+        n = std::min(n, tb_waves_per_cu_cl<11, 3>(fast));
+        n = std::min(n, tb_waves_per_cu_cl<11, 4>(fast));
+        n = std::min(n, tb_waves_per_cu_cl<11, 5>(fast));
+        n = std::min(n, tb_waves_per_cu_cl<11, 6>(fast));
+        n = std::min(n, tb_waves_per_cu_cl<11, 7>(fast));
+    }
+    return n;
 }
 
 int tblock_waves_per_cu(int D, bool fast) {
@@ -582,11 +629,48 @@ int64_t tblock_blocks(int N, int D, int H) {
     return (tiles + 7) / 8 * 8;
 }
 
+// Launches of 11 sweeps over checks every 8 (the deep driver's common case)
+// run one of eight kernels with the checked levels fixed at compile time
+// -- (0, 8), (1, 9), (2, 10), 3, 4, 5, 6, 7: every launch of that schedule --
+// so no run-time test sits between the levels of the unrolled pipeline
+// (8192^2: 249 -> ~224 us per launch).  Other levels take the general kernel.
+template <int CL, bool FAST>
+static void launch_tb11_cl(int blocks, const float* uin, const float* b, float* uout, const StepArgs& a, int H,
+                           hipStream_t s) {
+    float* none = nullptr;
+    hipLaunchKernelGGL((k_tblock<11, true, FAST, false, CL>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H,
+                       none);
+}
+
+template <bool FAST>
+static bool launch_tb11_fixed(int blocks, const float* uin, const float* b, float* uout, const StepArgs& a, int H,
+                              hipStream_t s) {
+    const int c0 = a.chk[0], c1 = a.chk[1];
+    if (c1 >= 0 && !(c1 == c0 + 8 && c0 <= 2)) return false;
+    if (c1 < 0 && !(c0 >= 3 && c0 <= 7)) return false;
+    switch (c0) {
+        case 0: launch_tb11_cl<0 | (9 << 4), FAST>(blocks, uin, b, uout, a, H, s); return true;
+        case 1: launch_tb11_cl<1 | (10 << 4), FAST>(blocks, uin, b, uout, a, H, s); return true;
+        case 2: launch_tb11_cl<2 | (11 << 4), FAST>(blocks, uin, b, uout, a, H, s); return true;
+        case 3: launch_tb11_cl<3, FAST>(blocks, uin, b, uout, a, H, s); return true;
+        case 4: launch_tb11_cl<4, FAST>(blocks, uin, b, uout, a, H, s); return true;
+        case 5: launch_tb11_cl<5, FAST>(blocks, uin, b, uout, a, H, s); return true;
+        case 6: launch_tb11_cl<6, FAST>(blocks, uin, b, uout, a, H, s); return true;
+        case 7: launch_tb11_cl<7, FAST>(blocks, uin, b, uout, a, H, s); return true;
+        default: return false;
+    }
+}
+
 template <int D>
 static hipError_t launch_tb_d(const float* uin, const float* b, float* uout, bool check, const StepArgs& a,
                               int H, hipStream_t s) {
     const int blocks = (int)tblock_blocks(a.g.N, D, H);
     float* none = nullptr;
+    if constexpr (D == 11) {
+        if (check && (a.fastdiv ? launch_tb11_fixed<true>(blocks, uin, b, uout, a, H, s)
+                                : launch_tb11_fixed<false>(blocks, uin, b, uout, a, H, s)))
+            return hipGetLastError();
+    }
     if (check) {
         if (a.fastdiv)
             hipLaunchKernelGGL((k_tblock<D, true, true, false>), dim3(blocks), dim3(64), 0, s, uin, b, uout, a, H,

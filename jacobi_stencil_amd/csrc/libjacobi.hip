@@ -53,13 +53,14 @@ int fail(int code, const std::string& msg) {
 constexpr int kMaxN = 65536;
 constexpr int kMaxD = 32;
 constexpr int kMaxTBlockD = 16;
-constexpr int kClasses = 10;
+constexpr int kClasses = 11;
 
 enum KClass {
     KC_RHS = 0, KC_SYNC = 1, KC_SYNC_CHECK = 2, KC_TBLOCK = 3, KC_ASYNC = 4, KC_RESID = 5, KC_PERSIST = 6,
     KC_NOOP = 7,   // launches issued ahead of a check that then stopped the step: they return at once
     KC_REDUCE = 8,  // one-block reductions of a check's or a norm's partial maxima
-    KC_TBLOCK_RHS = 9  // a step's first temporal-blocking launch, which also forms b
+    KC_TBLOCK_RHS = 9,  // a step's first temporal-blocking launch, which also forms b
+    KC_TBLOCK_PART = 10  // deep temporal blocking: a launch shorter than D (ends on a check, or a redo)
 };
 
 // One launch as seen by the launch timer.
@@ -185,6 +186,10 @@ StepArgs base_args(const jac_ctx* c, float tol) {
     a.sc = c->sc;
     a.mail = c->mail;
     a.slot = 0;
+    a.chk[0] = 0;
+    a.chk[1] = -1;
+    a.force = 0;
+    a.part_off = 0;
     return a;
 }
 
@@ -288,7 +293,12 @@ int check_opts(const jac_ctx* c, const jac_opts* o) {
 
 // Sweeps per launch and the check interval for these options.
 int sweeps_per_launch(const jac_opts* o) { return is_sync(o) ? 1 : o->D; }
+// Temporal blocking checks every M sweeps whatever D: a launch deeper than M
+// measures the residual at the levels where checks fall (run_step_deep), and
+// the other drivers launch at most M sweeps at a time.  The block-asynchronous
+// kernel checks every max(M, D): its in-tile sweeps are not global iterates.
 int64_t check_interval(const jac_opts* o) {
+    if (o->kernel == JAC_TBLOCK) return o->M;
     int spl = sweeps_per_launch(o);
     return spl > o->M ? spl : o->M;
 }
@@ -611,11 +621,196 @@ int run_step_blocking(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float*
     }
 }
 
+// One temporal-blocking launch of m sweeps from u[*buf] into the other buffer
+// for the deep driver.  levels[q] (q < 2; -1: none) are the launch's levels
+// whose residual it measures, for checks g[q]: each is reduced into mailbox slot
+// (g - 1) % kRing and followed by that check's event.  `force` runs it even
+// after a check has stopped the step (a redo).
+int enqueue_tb_deep(jac_ctx* c, const jac_opts* o, int m, const int* levels, const int64_t* g, bool force,
+                    int* buf) {
+    StepArgs a = base_args(c, o->tol);
+    const bool check = levels[0] >= 0;
+    a.chk[0] = levels[0];
+    a.chk[1] = levels[1];
+    a.force = force ? 1 : 0;
+    a.slot = check ? (int)((g[0] - 1) % kRing) : 0;
+    if (check && m <= 8 && (levels[0] != 0 || levels[1] >= 0))
+        return fail(JAC_EDEVICE, "a launch of 8 sweeps or fewer checks only its input");
+    if (o->band_rows == 0 && c->tb_rows[m] == 0)
+        c->tb_rows[m] = tblock_rows(c->N, m, c->cus, tblock_waves_per_cu(m, c->fastdiv != 0));
+    const int Hmax = tblock_max_rows(c->N, m);
+    const int H = std::min(o->band_rows > 0 ? o->band_rows : c->tb_rows[m], Hmax);
+    const int64_t npart = tblock_blocks(c->N, m, H);
+    if (check && 2 * npart > c->npart_cap)
+        return fail(JAC_EINVAL, "band_rows too small for this N: too many wavefront bands");
+    const float* in = c->u[*buf];
+    float* out = c->u[*buf ^ 1];
+    int st = timed(c, m == o->D ? KC_TBLOCK : KC_TBLOCK_PART,
+                   [&] { return launch_tblock(in, c->b, out, m, check, a, H, c->stream); });
+    if (st) return st;
+    for (int q = 0; q < 2 && check && levels[q] >= 0; ++q) {
+        StepArgs ra = base_args(c, o->tol);
+        ra.slot = (int)((g[q] - 1) % kRing);
+        ra.part_off = q == 0 ? 0 : npart;
+        st = timed(c, KC_REDUCE, [&] { return launch_reduce(npart, false, ra, c->stream); });
+        if (st) return st;
+        JAC_HIP(hipEventRecord(c->ev[g[q] % kRing], c->stream));
+    }
+    *buf ^= 1;
+    return JAC_OK;
+}
+
+// One step through the launch driver for temporal blocking deeper than the
+// check interval (D >= 9, D > M): launches of up to D sweeps, each measuring
+// the residual of the levels where a check falls (at most two per launch),
+// checks every M sweeps as the oracle does.  A check that stops the step at an
+// inner level c of a launch leaves its result unstored: the launch's input
+// u_k is intact (every later launch returns at once on the stop flag), so a
+// redo launch of c sweeps from it produces u_{k+c}.  A launch ends on any
+// check predicted to stop (which then runs as a residual pass on the exact
+// iterate, as in run_step) and on the last allowed check.
+int run_step_deep(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out) {
+    const int64_t L = o->M;
+    const int D = o->D;
+    // sweeps this step may run: launches end on the last allowed check (below
+    // max_sweeps + L), one launch of D beyond a stopping check, a redo
+    c->fast_now = division_path(c, 1, (double)o->max_sweeps + (double)L + 2.0 * (double)D);
+    c->step_serial += 1;
+    c->cur_group = -1;
+    c->cur_first = false;
+    if (c->prof_every > 0) {
+        int s0 = drain_profile(c, c->step_serial - 1);
+        if (s0) return s0;
+    }
+    const bool fuse_rhs = c->fast_now != 0;
+    int st = fuse_rhs ? JAC_OK : enqueue_rhs(c, o);
+    if (st) return st;
+    int buf = c->cur;
+    int64_t launch_no = 0;  // profiling group of each launch
+    // the first launch: L sweeps (it may form b), no check inside
+    c->cur_group = launch_no++;
+    c->cur_first = true;
+    c->rhs_pending = fuse_rhs;
+    st = enqueue_sweeps(c, o, L, false, 0, &buf);
+    c->rhs_pending = false;
+    if (st) return st;
+    int64_t k = L;           // sweeps enqueued; u_k is in u[buf]
+    int64_t g_next = 1;      // the first check not yet enqueued (g_next * L >= k)
+    const int64_t gmax = (o->max_sweeps + L - 1) / L;  // the last allowed check
+    bool final_enqueued = false;
+    int64_t predicted = 0;
+    CheckHistory hist;
+    struct Pending {
+        int buf;            // the buffer holding the input of the launch that measured it
+        int level;          // its level in that launch (0: the input itself)
+        int64_t launch;     // that launch's profiling group
+    };
+    Pending info[kRing];
+    auto stops_here = [&](int64_t g) {
+        return g >= gmax || hist.predicts_stop(g, o->tol, c->predict_margin);
+    };
+    auto enqueue_more = [&]() -> int {
+        const int64_t gk = g_next;
+        if (gk * L == k && stops_here(gk)) {
+            // measure only, keep u_{gL} in place
+            const int slot = (int)((gk - 1) % kRing);
+            c->mail->R[slot] = kEmpty;
+            c->cur_group = launch_no++;
+            c->cur_first = true;
+            int s2 = enqueue_residual(c, o, buf, slot);
+            if (s2) return s2;
+            JAC_HIP(hipEventRecord(c->ev[gk % kRing], c->stream));
+            info[gk % kRing] = Pending{buf, 0, c->cur_group};
+            final_enqueued = true;
+            if (gk < gmax) predicted = gk;
+            g_next = gk + 1;
+            return JAC_OK;
+        }
+        // a launch from k: at most two checks inside, and it ends on a check
+        // that stops here
+        int64_t m = std::min<int64_t>(D, gk * L - k + 2 * L);
+        for (int64_t g = gk; g * L < k + m; ++g)
+            if (g * L > k && stops_here(g)) {
+                m = g * L - k;
+                break;
+            }
+        if (m <= 8) m = std::min<int64_t>(m, gk * L == k ? L : gk * L - k);  // the shallow kernels check only their input
+        int levels[2] = {-1, -1};
+        int64_t gs[2] = {0, 0};
+        int n = 0;
+        for (int64_t g = gk; g * L < k + m && n < 2; ++g, ++n) {
+            levels[n] = (int)(g * L - k);
+            gs[n] = g;
+            c->mail->R[(g - 1) % kRing] = kEmpty;
+        }
+        c->cur_group = launch_no++;
+        c->cur_first = true;
+        const int in_buf = buf;
+        int s2 = enqueue_tb_deep(c, o, (int)m, levels, gs, false, &buf);
+        if (s2) return s2;
+        for (int q = 0; q < n; ++q) info[gs[q] % kRing] = Pending{in_buf, levels[q], c->cur_group};
+        k += m;
+        g_next = gk + n;
+        return JAC_OK;
+    };
+
+    for (int64_t g = 1;; ++g) {
+        while (!final_enqueued && g_next <= g + 1) {  // keep one check queued beyond check g
+            st = enqueue_more();
+            if (st) return st;
+        }
+        const int ev = (int)(g % kRing);
+        const int slot = (int)((g - 1) % kRing);
+        JAC_HIP(hipEventSynchronize(c->ev[ev]));
+        const uint32_t Rb = await_mail(c, &c->mail->R[slot]);
+        if (Rb == kEmpty) return fail(JAC_EDEVICE, "a residual check did not report");
+        const float R = mail_float(&c->mail->R[slot]);
+        const float rho = R / mail_float(&c->mail->bA_bits);
+        const int64_t kk = g * L;
+        const bool stop = !(rho >= o->tol);
+        if (stop || kk >= o->max_sweeps) {
+            const Pending p = info[ev];
+            if (c->prof_every > 0 && stop) mark_noops(c, p.launch);
+            for (int64_t i = 0; i < g; ++i) c->dlog.push_back(D);
+            if (p.level == 0) {
+                c->cur = p.buf;
+            } else {
+                // the result u_{gL} lies p.level sweeps past the intact input
+                int b2 = p.buf;
+                const int none[2] = {-1, -1};
+                const int64_t g0[2] = {0, 0};
+                c->cur_group = p.launch;
+                c->cur_first = true;
+                st = enqueue_tb_deep(c, o, p.level, none, g0, true, &b2);
+                if (st) return st;
+                c->cur = b2;
+            }
+            if (sweeps_out) *sweeps_out = kk;
+            if (rho_out) *rho_out = rho;
+            if (std::isnan(rho)) return fail(JAC_ENAN, "rho is NaN");
+            if (!stop) return fail(JAC_ENOCONV, "max_sweeps reached before rho < tol");
+            return JAC_OK;
+        }
+        hist.push(g, rho);
+        if (g == predicted) {
+            // the predicted final check did not converge: launches go on from u_{gL}
+            final_enqueued = false;
+            predicted = 0;
+        }
+        if (c->prof_every > 0 && c->recs.size() > 8192) {
+            st = drain_profile(c, c->step_serial);
+            if (st) return st;
+        }
+    }
+}
+
 // One step through the launch or the graph driver.  Check g (g >= 1) examines
 // u_{gL}; its R lands in mailbox slot (g - 1) % kRing.
 int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out) {
     if (o->checks == JAC_CHECKS_BLOCKING || o->controller != JAC_STATIC)
         return run_step_blocking(c, o, sweeps_out, rho_out);
+    if (o->kernel == JAC_TBLOCK && o->driver == JAC_LAUNCH && o->D >= 9 && o->D > o->M)
+        return run_step_deep(c, o, sweeps_out, rho_out);
     const int64_t L = check_interval(o);
     const bool graph = o->driver == JAC_GRAPH;
     // sweeps this step may run: up to max_sweeps, plus the interval queued beyond a check
@@ -772,8 +967,9 @@ int run_persistent(jac_ctx* c, const jac_opts* o, int nsteps, int64_t* sweeps, f
     PersistRec* rec = reinterpret_cast<PersistRec*>(c->pout);
     for (int n = 0; n < nsteps; ++n) rec[n] = PersistRec{0, 0, 0, 1, c->cur};
     const bool async_mode = o->kernel == JAC_ASYNC;
-    const int D = o->kernel == JAC_SYNC ? 1 : o->D;
     const int L = (int)check_interval(o);
+    // temporal blocking runs chunks of at most one check interval
+    const int D = o->kernel == JAC_SYNC ? 1 : (o->kernel == JAC_TBLOCK ? std::min(o->D, L) : o->D);
     c->fast_now = division_path(c, nsteps, (double)o->max_sweeps + 2.0 * (double)L);
     StepArgs a = base_args(c, o->tol);
     int grid = 0;

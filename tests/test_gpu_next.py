@@ -41,10 +41,10 @@ def test_blocking_checks_bitwise(kernel, D, driver, M):
     N, r = 70, 10.0
     say("blocking", kernel, D, driver, M)
     s = workloads.gaussian_source(N, r)
-    ref = oracle.solve(N, r, s, steps=2, M=max(M, D))
+    ref = oracle.solve(N, r, s, steps=2, M=M)  # synchronous and temporal blocking: checks every M
     got, dlog = solve_with_log(N, r, s, 2, opts(kernel=kernel, D=D, M=M, driver=driver, checks=B))
     assert_same(got, ref, f"blocking {kernel} D={D} M={M}")
-    assert len(dlog) == int(ref.sweeps.sum()) // max(M, D)
+    assert len(dlog) == int(ref.sweeps.sum()) // M
 
 
 def test_blocking_async_bitwise():

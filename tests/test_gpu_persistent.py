@@ -32,7 +32,8 @@ def test_tblock_every_depth_bitwise(D):
     say("persist tblock", D)
     s = workloads.gaussian_source(N, r)
     ref = oracle.solve(N, r, s, steps=2, M=max(8, D))
-    assert_same(lib_solve(N, r, s, 2, opts(kernel=jac.JAC_TBLOCK, D=D, driver=PER)), ref, f"D={D}")
+    got = lib_solve(N, r, s, 2, opts(kernel=jac.JAC_TBLOCK, D=D, M=max(8, D), driver=PER))
+    assert_same(got, ref, f"D={D}")
 
 
 @pytest.mark.parametrize("tile,D", [((32, 8), 8), ((32, 16), 8), ((7, 5), 3), ((64, 16), 12)])
@@ -102,7 +103,7 @@ def test_tblock_resident_and_staged_tiles_bitwise(N, side, D):
     say("persist tblock tiles", N, side, D)
     s = workloads.gaussian_source(N, r)
     ref = oracle.solve(N, r, s, steps=2, M=max(8, D))
-    got = lib_solve(N, r, s, 2, opts(kernel=jac.JAC_TBLOCK, D=D, driver=PER, band_rows=side))
+    got = lib_solve(N, r, s, 2, opts(kernel=jac.JAC_TBLOCK, D=D, M=max(8, D), driver=PER, band_rows=side))
     assert_same(got, ref, f"N={N} side={side} D={D}")
 
 

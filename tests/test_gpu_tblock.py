@@ -1,8 +1,9 @@
 """Kernel (b), exact temporal blocking, against the oracle bit for bit (page
 "stencil-jacobian.vercel.app", section 02: after D sweeps the tile holds exactly
-what D synchronous sweeps would produce).  A launch does D sweeps; the check
-interval is M = 8, or D when D > 8, and launches of min(D, left) sweeps keep
-the checks on the oracle's sweep counts."""
+what D synchronous sweeps would produce).  A launch does up to D sweeps; checks
+fall every M = 8 sweeps whatever D (a launch deeper than 8 measures the residual
+at the levels where checks fall), so every depth gives the oracle's sweep
+counts at M = 8; with M = D the interval is D."""
 import numpy as np
 import pytest
 
@@ -17,7 +18,7 @@ TB = jac.JAC_TBLOCK
 
 
 def interval(D, M=8):
-    return max(M, D)
+    return M
 
 
 @pytest.mark.parametrize("D", list(range(1, 17)))
@@ -184,23 +185,38 @@ def test_aligned_layout_tall_bands_bitwise(D, H):
     assert_same(lib_solve(N, r, s, 2, opts(kernel=TB, D=D, M=8, band_rows=H)), _ALIGNED_REF[M], f"D={D} H={H}")
 
 
-@pytest.mark.parametrize("D", list(range(1, 17)))
-def test_config_c3_every_depth_against_stored_oracle(D):
-    """N = 8192, r = 10, the benchmark workload, at every depth 1..16 in one
-    ten-step solve with the default options: per-step sweeps and rho bits and
-    the final field against the oracle's (check interval 8, or D above 8)."""
-    exp = load_expected("C3" if D <= 8 else f"C3_M{D}")
-    assert exp is not None and exp["M"] == interval(D)
-    say("tblock C3 depth", D)
+def _c3_against(exp, o):
     N, r = exp["N"], exp["r"]
     sol = jac.Solver(N, r, workloads.source(exp["source"], N, r))
     try:
-        st, k, rho = sol.solve(exp["steps"], jac.jac_opts_default(kernel=TB, D=D))
+        st, k, rho = sol.solve(exp["steps"], o)
         assert st == jac.JAC_OK and k.tolist() == exp["sweeps"], (k.tolist(), exp["sweeps"])
         assert [f"{np.float32(x).view(np.uint32):08x}" for x in rho] == exp["rho_bits"]
         assert field_hash(sol.field()) == exp["field_sha256"][-1]
     finally:
         sol.close()
+
+
+@pytest.mark.parametrize("D", list(range(1, 17)))
+def test_config_c3_every_depth_against_stored_oracle(D):
+    """N = 8192, r = 10, the benchmark workload, at every depth 1..16 in one
+    ten-step solve with the default options (checks every 8 sweeps; from D = 9
+    on deep launches check inner levels): per-step sweeps and rho bits and the
+    final field against the oracle's."""
+    exp = load_expected("C3")
+    assert exp is not None and exp["M"] == 8
+    say("tblock C3 depth", D)
+    _c3_against(exp, jac.jac_opts_default(kernel=TB, D=D))
+
+
+@pytest.mark.parametrize("D", list(range(9, 17)))
+def test_config_c3_interval_d_against_stored_oracle(D):
+    """The same workload checked every D sweeps (M = D): launches of D sweeps
+    that check their input, against the oracle run with M = D."""
+    exp = load_expected(f"C3_M{D}")
+    assert exp is not None and exp["M"] == D
+    say("tblock C3 interval D", D)
+    _c3_against(exp, jac.jac_opts_default(kernel=TB, D=D, M=D))
 
 
 @pytest.mark.parametrize("N,D,r", [(70, 8, 10.0), (300, 4, 0.05), (513, 3, 1.0), (1040, 8, 10.0)])
