@@ -3,7 +3,9 @@
 One bench "step" is one whole solve: reset the field to u^0 = 0, then ten
 time steps, each Jacobi-iterated until rho < 1e-5 (checked every 8 sweeps),
 everything resident in HBM.  The reported value is Gpoint-updates/s =
-N^2 * (sweeps of the exact method) / time-to-solution.
+N^2 * (sweeps of the exact method) / time-to-solution.  Default kernel: exact
+temporal blocking, launches of D = 11 sweeps that measure the residual at the
+levels where the checks every 8 sweeps fall.
 
 Beside it, on the same JSON line:
   roofline      the dominant kernel's algorithmic bytes per launch (12 bytes per
@@ -48,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="C3")
     ap.add_argument("--kernel", default="tblock", choices=sorted(KERNELS))
-    ap.add_argument("--D", type=int, default=8)
+    ap.add_argument("--D", type=int, default=11)
     ap.add_argument("--tile-x", type=int, default=32)
     ap.add_argument("--tile-y", type=int, default=8)
     ap.add_argument("--band-rows", type=int, default=0, help="TBLOCK rows per band (0: automatic)")
@@ -147,8 +149,8 @@ def traffic_from(fetch_csv, write_csv, probe_mib, out_path, key):
                 vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]) * 1024.0)
         return vals
 
-    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
-    write = per_kernel(write_csv, "WRITE_SIZE")
+    fetch = _grouped(per_kernel(fetch_csv, "FETCH_SIZE"))
+    write = _grouped(per_kernel(write_csv, "WRITE_SIZE"))
     known = probe_mib * (1 << 20)
     probe = next(k for k in fetch if "k_probe<0" in k)
     f_scale = known / fetch[probe][0]    # the first probe launch is the copy of `probe_mib`
@@ -173,6 +175,22 @@ def traffic_from(fetch_csv, write_csv, probe_mib, out_path, key):
     print(json.dumps({key: res}, indent=1))
 
 
+def _kernel_group(name):
+    """A kernel's name without the compile-time check levels: the deep
+    temporal-blocking launches of one depth run as several kernels that differ
+    only in the levels they check, with the same data movement."""
+    import re
+
+    return re.sub(r"(k_tblock<\d+, \w+, \w+, \w+), -?\d+>", r"\1>", name)
+
+
+def _grouped(vals):
+    out = {}
+    for k, v in vals.items():
+        out.setdefault(_kernel_group(k), []).extend(v)
+    return out
+
+
 def counters_from(paths, kclass):
     """Median per launch of every counter or derived metric in rocprofv3 --pmc
     files, for the most-called kernel of a class.  Launches queued after a
@@ -185,7 +203,7 @@ def counters_from(paths, kclass):
     per = {}  # kernel -> dispatch -> (duration ns, {counter: value})
     for path in paths:
         for row in csv.DictReader(open(path)):
-            k = row["Kernel_Name"]
+            k = _kernel_group(row["Kernel_Name"])
             if pattern not in k:
                 continue
             key = (path, row["Dispatch_Id"])

@@ -225,12 +225,16 @@ def study_depths(a):
         for D in range(1, 17):
             o = dict(kernel=kernel, D=D, tile_x=32, tile_y=16)
             rec = R.run(N, r, steps, **o)
-            # per-launch time from a solve checking every D sweeps, so that every
-            # profiled launch does D sweeps (with M = 8 a depth that does not
-            # divide 8 also issues shorter launches to reach each check)
-            us, n, nt = _launch_profile(R, N, r, steps, kc, 8, M=max(D, 1), **o)
+            # per-launch time of launches of D sweeps: below 9, from a solve checking
+            # every D sweeps (with M = 8 a depth that does not divide 8 also issues
+            # shorter launches to reach each check); from 9 on, temporal blocking's
+            # own solve (its launches of D sweeps check inner levels; shorter ones
+            # have a class of their own), block-async checking every D
+            deep = kernel == jac.JAC_TBLOCK and D >= 9
+            us, n, nt = _launch_profile(R, N, r, steps, kc, 8, **(o if deep else dict(o, M=max(D, 1))))
             upd = D * N * N  # point-updates per launch of D sweeps
-            rec.update(study="depths", family=fam, D=D, interval=max(8, D),
+            rec.update(study="depths", family=fam, D=D,
+                       interval=8 if kernel == jac.JAC_TBLOCK else max(8, D),
                        s=round(rec["sweeps"] / base["sweeps"], 4),
                        c=round((rec["ms"] / rec["sweeps"]) / (base["ms"] / base["sweeps"]), 4),
                        launch_us=round(us, 2), launches=n, timed=nt,
