@@ -55,7 +55,7 @@ def test_random_fields_bitwise(D):
     assert_same(lib_solve(N, r, s, 1, opts(kernel=TB, D=D), u0=u0), ref, f"D={D}")
 
 
-@pytest.mark.parametrize("D", [2, 4, 8])
+@pytest.mark.parametrize("D", [2, 4, 8, 11])
 def test_config_c1_bitwise(D):
     say("tblock C1", D)
     s = workloads.point_source(512, 1.0)
@@ -279,10 +279,11 @@ def test_band_spanning_more_than_2gib_bitwise():
         assert np.array_equal(bits(got), bits(want)), f"rows {r0}..{r0 + 4095}"
 
 
-@pytest.mark.parametrize("kernel,D", [(TB, 8), (jac.JAC_SYNC, 1)])
+@pytest.mark.parametrize("kernel,D", [(TB, 8), (TB, 11), (jac.JAC_SYNC, 1)])
 def test_config_c4_against_stored_oracle(kernel, D):
     """N = 18432, r = 100, point source, ten steps (14160 sweeps), every step
-    against the oracle's stored field hash."""
+    against the oracle's stored field hash (D = 11: launches of 11 sweeps over
+    checks every 8, the fastest form at this size)."""
     exp = load_expected("C4")
     assert exp is not None
     say("C4", kernel, D)
