@@ -123,6 +123,8 @@ struct StepArgs {
     int chk[2];
     int force;         // 1: run even if a check has stopped the step (a redo)
     int64_t part_off;  // the reduction reads partial slots from here
+    int slot2;         // >= 0: the reduction also reduces the next npart slots, a second check, into this
+                       // mailbox slot (a launch that checks two levels)
 };
 
 // ---------------------------------------------------------------- device

@@ -108,10 +108,7 @@ hipError_t launch_rhs(const float* u, const float* src, float* b, bool keep_u, c
 
 constexpr int kReduceThreads = 1024;
 
-__global__ __launch_bounds__(kReduceThreads) void k_reduce(int64_t npart, int norm, StepArgs a) {
-    Scratch* sc = a.sc;
-    if (!norm && sc->stop) return;  // the step stopped at an earlier check
-    const uint32_t* part = scratch_partials(sc) + a.part_off;
+__device__ __forceinline__ uint32_t block_reduce_partials(const uint32_t* part, int64_t npart) {
     uint32_t m = 0;
     for (int64_t i = threadIdx.x; i < npart; i += kReduceThreads) {
         const uint32_t v = part[i];
@@ -121,21 +118,41 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(int64_t npart, int no
     __shared__ uint32_t w[kReduceThreads / 64];
     if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = m;
     __syncthreads();
+    uint32_t bm = w[0];
+    for (int k = 1; k < kReduceThreads / 64; ++k) bm = bm > w[k] ? bm : w[k];
+    __syncthreads();  // w is free again
+    return bm;
+}
+
+__global__ __launch_bounds__(kReduceThreads) void k_reduce(int64_t npart, int norm, StepArgs a) {
+    Scratch* sc = a.sc;
+    if (!norm && sc->stop) return;  // the step stopped at an earlier check
+    const uint32_t* part = scratch_partials(sc) + a.part_off;
+    const uint32_t bm = block_reduce_partials(part, npart);
+    // a second check of the same launch: the next npart slots
+    const uint32_t bm2 = (!norm && a.slot2 >= 0) ? block_reduce_partials(part + npart, npart) : 0u;
     if (threadIdx.x == 0) {
-        uint32_t bm = w[0];
-        for (int k = 1; k < kReduceThreads / 64; ++k) bm = bm > w[k] ? bm : w[k];
         if (norm) {
             sc->bA_bits = bm;
             sc->stop = 0u;
             sc->check_seq = 0u;
             __hip_atomic_store(&a.mail->bA_bits, bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         } else {
-            const float rho = __uint_as_float(bm) / __uint_as_float(sc->bA_bits);
-            sc->stop = (rho >= a.tol) ? 0u : 1u;
+            const float bA = __uint_as_float(sc->bA_bits);
+            const float rho = __uint_as_float(bm) / bA;
+            bool stop = !(rho >= a.tol);
             const uint32_t seq = sc->check_seq;
             const int slot = a.slot >= 0 ? a.slot : (int)(seq % (uint32_t)kRing);
             sc->check_seq = seq + 1u;
             __hip_atomic_store(&a.mail->R[slot], bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            if (a.slot2 >= 0) {
+                // the host reads the first check before the second; either one stops the step
+                const float rho2 = __uint_as_float(bm2) / bA;
+                stop = stop || !(rho2 >= a.tol);
+                sc->check_seq = seq + 2u;
+                __hip_atomic_store(&a.mail->R[a.slot2], bm2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+            sc->stop = stop ? 1u : 0u;
         }
     }
 }

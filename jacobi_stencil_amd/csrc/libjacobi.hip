@@ -190,6 +190,7 @@ StepArgs base_args(const jac_ctx* c, float tol) {
     a.chk[1] = -1;
     a.force = 0;
     a.part_off = 0;
+    a.slot2 = -1;
     return a;
 }
 
@@ -648,13 +649,14 @@ int enqueue_tb_deep(jac_ctx* c, const jac_opts* o, int m, const int* levels, con
     int st = timed(c, m == o->D ? KC_TBLOCK : KC_TBLOCK_PART,
                    [&] { return launch_tblock(in, c->b, out, m, check, a, H, c->stream); });
     if (st) return st;
-    for (int q = 0; q < 2 && check && levels[q] >= 0; ++q) {
+    if (check) {
+        // one reduction for both checked levels: partial slots [0, npart) and [npart, 2 npart)
         StepArgs ra = base_args(c, o->tol);
-        ra.slot = (int)((g[q] - 1) % kRing);
-        ra.part_off = q == 0 ? 0 : npart;
+        ra.slot = (int)((g[0] - 1) % kRing);
+        ra.slot2 = levels[1] >= 0 ? (int)((g[1] - 1) % kRing) : -1;
         st = timed(c, KC_REDUCE, [&] { return launch_reduce(npart, false, ra, c->stream); });
         if (st) return st;
-        JAC_HIP(hipEventRecord(c->ev[g[q] % kRing], c->stream));
+        for (int q = 0; q < 2 && levels[q] >= 0; ++q) JAC_HIP(hipEventRecord(c->ev[g[q] % kRing], c->stream));
     }
     *buf ^= 1;
     return JAC_OK;
