@@ -17,7 +17,7 @@ from tests.gpu_helpers import field_hash, load_expected, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("kernel,D", [(jac.JAC_SYNC, 1), (jac.JAC_TBLOCK, 8)])
+@pytest.mark.parametrize("kernel,D", [(jac.JAC_SYNC, 1), (jac.JAC_TBLOCK, 8), (jac.JAC_TBLOCK, 11)])
 def test_c_client_matches_stored_oracle(kernel, D, tmp_path):
     exp = load_expected("C1")
     assert exp is not None and exp["source"] == "point"
