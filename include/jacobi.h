@@ -108,8 +108,8 @@ enum jac_driver {
     JAC_PERSISTENT = 2   /* one cooperative kernel per jac_solve: every step, check and decision on the
                             device; SYNC and TBLOCK use 2-D tiles in LDS with a D-cell ghost zone (held in
                             LDS for the whole solve when every tile fits one round of resident blocks,
-                            re-staged per D sweeps otherwise), ASYNC its own tiles; same results as
-                            JAC_LAUNCH */
+                            re-staged per D sweeps otherwise), ASYNC its own tiles (held in LDS with a
+                            one-cell halo under the same condition); same results as JAC_LAUNCH */
 };
 
 typedef struct {

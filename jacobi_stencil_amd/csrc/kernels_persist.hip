@@ -8,10 +8,11 @@
 // the paperlayer summary of arXiv 2610.15878, sections 3-4: persistent
 // kernels, device-side barriers, no host in the loop).
 //
-// Two kernels.  k_persist_res (below) keeps every tile resident in LDS for the
-// whole solve and trades tile edges point to point; it serves SYNC and TBLOCK
-// wherever all tiles fit one round of co-resident blocks.  k_persist re-stages
-// tiles per chunk behind grid barriers and serves everything else.
+// Three kernels.  k_persist_res (below) keeps every tile resident in LDS for
+// the whole solve and trades tile edges point to point; it serves SYNC and
+// TBLOCK wherever all tiles fit one round of co-resident blocks, and
+// k_persist_ares does the same for ASYNC.  k_persist re-stages tiles per chunk
+// behind grid barriers and serves everything else.
 //
 // k_persist: every block runs the same program:
 //   per step:   b = u^n + s and a partial max of |b_A|;  grid barrier;  every
@@ -834,6 +835,303 @@ __global__ __launch_bounds__(kResThreads) void k_persist_res(PersistArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- resident block-asynchronous tiles
+//
+// The block-asynchronous kernel (ASYNC) on grids whose tiles all fit one round
+// of co-resident blocks: each block owns one tx x ty tile and keeps three
+// copies of it, each with a one-cell halo, in LDS, and b of its cells in
+// registers.  A chunk of Dc sweeps updates the tile with its halo frozen --
+// exactly one block-asynchronous launch (page "stencil-jacobian.vercel.app",
+// section 02) -- and writes only the two copies other than its input, so the
+// chunk's input survives it.  The block then publishes its four edges and
+// refills its halo from its neighbours' edges (no corners: the five-point
+// stencil never reads them), in the tagged-word exchange described above,
+// here one cell deep.  A check at k = gL (g >= 1) measures the residual of
+// u_k once the halo holds the neighbours' u_k, as the re-staged kernel
+// measures it at the start of the next chunk; the grid-wide maximum completes
+// under the next chunk's exchange, and a stop keeps u_k, that chunk's
+// preserved input, whose halo the dropped refill has left as it was.
+//
+// Exchange memory: per tile and parity 2 (tx + ty) words -- the top row
+// [0, tx), the bottom row [tx, 2tx), the left column [2tx, 2tx + ty), the
+// right column [2tx + ty, 2tx + 2ty) of the tile.  Tiles in one column share
+// a width and tiles in one row a height, so every halo cell lies in one
+// neighbour's edge, whatever the ragged last tiles.
+
+constexpr int kAresEdge = 2;  // edge words published and taken per thread: tx + ty <= block size
+constexpr int kAresPoll = 4;  // partial slots per thread: grid <= 4 x block size
+
+int64_t ares_exchange_words(int ntiles, int tx, int ty) { return (int64_t)ntiles * 4 * (tx + ty); }
+
+// Dc sweeps from copy `in` (copies R floats apart) through the other two
+// copies; returns the copy that holds the last sweep.
+template <bool FAST, int NQ>
+__device__ __forceinline__ int ares_sweeps(float* lds, int in, int Dc, int R, int lp4, const int* at,
+                                           const uint32_t* info, const float* bv, float r, float d, float y) {
+    const int x = in == 2 ? 0 : in + 1, z = 3 - in - x;
+    int src = in, dst = x;
+    for (int sw = 1; sw <= Dc; ++sw) {
+        res_sweep<FAST, NQ>(lds, src * R * 4, dst * R * 4, lp4, at, info, bv, r, d, y);
+        __syncthreads();
+        src = dst;
+        dst = dst == x ? z : x;
+    }
+    return src;
+}
+
+template <bool FAST>
+__global__ __launch_bounds__(kResThreads) void k_persist_ares(PersistArgs a) {
+    extern __shared__ float lds[];
+    __shared__ uint32_t wmax[kResWaves];
+    __shared__ uint32_t gave_up;  // a wait of this block outlasted the spin budget
+    const Geom g = a.g;
+    const int N = g.N, P = g.P;
+    const int TX = a.tx, TY = a.ty;
+    const int ntx = (N + TX - 1) / TX, nty = (N + TY - 1) / TY;
+    const int tile = blockIdx.x;
+    const int ti = tile / ntx, tj = tile % ntx;
+    const int tx0 = tj * TX, ty0 = ti * TY;
+    const int w = tx0 + TX <= N ? TX : N - tx0, h = ty0 + TY <= N ? TY : N - ty0;
+    const int lp = TX + 2;          // copy pitch; the tile's cells sit at rows 1..h, columns 1..w
+    const int R = lp * (TY + 2);    // floats per copy
+    const int EW = 2 * (TX + TY);   // exchange words per tile and parity
+    const float r = a.r, d = a.d, y = a.y;
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    if (tid < kResWaves) wmax[tid] = 0;  // the words of absent waves stay 0
+    if (tid == 0) gave_up = 0;
+    // the tile and its halo of u^n (ghost cells included) into all three copies
+    {
+        const float* src = (a.cur0 ? a.u1 : a.u0) + g.origin + (int64_t)(ty0 - 1) * P + (tx0 - 1);
+        const int rw = w + 2;
+        for (int k = tid; k < rw * (h + 2); k += nthr) {
+            const int rr = k / rw, cc = k - rr * rw;
+            const float v = src[(int64_t)rr * P + cc];
+            const int c = rr * lp + cc;
+            lds[c] = v;
+            lds[R + c] = v;
+            lds[2 * R + c] = v;
+        }
+    }
+    // this thread's tile cells k = tid + q*nthr (row k / w, column k % w): the
+    // byte offset of the west neighbour and its bits; a lane past the tile
+    // keeps cell 0's offset and no bits
+    const int ncell = w * h;
+    const int nq = (ncell + nthr - 1) / nthr;
+    int at[kResCells];
+    uint32_t info[kResCells];
+#pragma unroll
+    for (int q = 0; q < kResCells; ++q) {
+        const int k = tid + q * nthr;
+        const int kk = k < ncell ? k : 0;
+        const int i = kk / w, j = kk - (kk / w) * w;
+        at[q] = ((1 + i) * lp + j) * 4;
+        info[q] = k < ncell ? (kCellUnk | kCellCore | (ty0 + i == 0 ? kCellTop : 0u)) : 0u;
+    }
+    // the edge words this thread publishes (LDS cell, slot) and takes
+    // (neighbour word without parity, LDS cell; -1: none or a ghost)
+    int psrc[kAresEdge], pslot[kAresEdge], roff[kAresEdge], rdst[kAresEdge];
+#pragma unroll
+    for (int p = 0; p < kAresEdge; ++p) {
+        const int e = tid + p * nthr;
+        psrc[p] = -1;
+        pslot[p] = 0;
+        roff[p] = -1;
+        rdst[p] = 0;
+        int nb = -1;
+        if (e < w) {  // top row; the halo row above from the north tile's bottom row
+            psrc[p] = lp + 1 + e;
+            pslot[p] = e;
+            if (ti > 0) nb = (ti - 1) * ntx + tj, roff[p] = TX + e, rdst[p] = 1 + e;
+        } else if (e < 2 * w) {  // bottom row; the halo row below from the south tile's top row
+            const int jj = e - w;
+            psrc[p] = h * lp + 1 + jj;
+            pslot[p] = TX + jj;
+            if (ti + 1 < nty) nb = (ti + 1) * ntx + tj, roff[p] = jj, rdst[p] = (h + 1) * lp + 1 + jj;
+        } else if (e < 2 * w + h) {  // left column; the halo column left from the west tile's right column
+            const int ii = e - 2 * w;
+            psrc[p] = (1 + ii) * lp + 1;
+            pslot[p] = 2 * TX + ii;
+            if (tj > 0) nb = ti * ntx + tj - 1, roff[p] = 2 * TX + TY + ii, rdst[p] = (1 + ii) * lp;
+        } else if (e < 2 * w + 2 * h) {  // right column; the halo column right from the east tile's left column
+            const int ii = e - 2 * w - h;
+            psrc[p] = (1 + ii) * lp + w;
+            pslot[p] = 2 * TX + TY + ii;
+            if (tj + 1 < ntx) nb = ti * ntx + tj + 1, roff[p] = 2 * TX + ii, rdst[p] = (1 + ii) * lp + w + 1;
+        }
+        if (nb >= 0) roff[p] += nb * 2 * EW;
+    }
+    __syncthreads();
+    uint64_t* xbuf = a.xchg;
+    uint64_t* part64 = reinterpret_cast<uint64_t*>(a.partial);  // 2 x grid tagged words
+    const int G = gridDim.x;
+    int cur = 0;            // copy holding the current iterate
+    int red = 0;            // reductions so far: selects the partial buffer, tags the next
+    uint32_t serial = 0;    // chunks published by this block in this solve
+    uint32_t bA_bits = 0;
+    int status = 1;
+    float bv[kResCells];    // b of this thread's cells
+    for (int step = 0; step < a.nsteps; ++step) {
+        // ---- b = u^n + s on the tile, max |b + r*g|
+        {
+            __syncthreads();  // every thread has read the last reduction from wmax
+            const int ob4 = cur * R * 4;
+            uint32_t m = 0;
+#pragma unroll
+            for (int q = 0; q < kResCells; ++q) {
+                bv[q] = 0.0f;
+                if (!(info[q] & kCellUnk)) continue;
+                const int k = tid + q * nthr, i = k / w, j = k - (k / w) * w;
+                bv[q] = lds_at(lds, at[q] + ob4 + 4) + a.s[g.origin + (int64_t)(ty0 + i) * P + tx0 + j];
+                float tg = kTop;
+                asm volatile("" : "+v"(tg));
+                const float rg = r * ((info[q] & kCellTop) ? tg : 0.0f);
+                const uint32_t v = __float_as_uint(fabsf(bv[q] + rg));
+                m = m > v ? m : v;
+            }
+            block_max_put(wmax, m);
+            __syncthreads();
+            if (tid == 0)
+                __hip_atomic_store(&part64[(int64_t)(red & 1) * G + blockIdx.x],
+                                   ((uint64_t)(red + 1) << 32) | block_max_get(wmax), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            int off[kAresPoll];
+            uint64_t x[kAresPoll];
+#pragma unroll
+            for (int q = 0; q < kAresPoll; ++q) {
+                const int i = tid + q * nthr;
+                off[q] = i < G ? (red & 1) * G + i : -1;
+            }
+            if (!poll_tagged<0, kAresPoll>(nullptr, nullptr, 0u, nullptr, part64, off, (uint32_t)red + 1u, x, a.sc))
+                gave_up = 1;
+            uint32_t v = 0;
+#pragma unroll
+            for (int q = 0; q < kAresPoll; ++q) v = off[q] >= 0 && (uint32_t)x[q] > v ? (uint32_t)x[q] : v;
+            __syncthreads();  // wmax read by thread 0 above
+            block_max_put(wmax, v);
+            __syncthreads();
+            bA_bits = block_max_get(wmax);
+            if (gave_up) return;
+            ++red;
+        }
+        const float bA = __uint_as_float(bA_bits);
+        int64_t k = 0, kc = 0;  // sweeps; the pending check's sweep count
+        int done = 0;
+        bool pending = false;   // a check's partial is out; its decision comes with this chunk's exchange
+        uint32_t R_bits = 0;
+        status = 1;
+        for (;;) {
+            const int left = a.L - done;
+            const int Dc = a.D < left ? a.D : left;
+            const int in = cur;
+            // ---- Dc sweeps with the halo frozen, into the copies other than `in`
+#define JAC_ARES_SWEEPS(NQ) cur = ares_sweeps<FAST, NQ>(lds, in, Dc, R, lp * 4, at, info, bv, r, d, y)
+            JAC_RES_NQ(JAC_ARES_SWEEPS)
+#undef JAC_ARES_SWEEPS
+            k += Dc;
+            done += Dc;
+            if (done == a.L) done = 0;
+            ++serial;
+            const int ob = cur * R;
+            // ---- publish the tile's edges, tagged with the chunk number
+            {
+                uint64_t* e = xbuf + ((int64_t)tile * 2 + (serial & 1)) * EW;
+                const uint64_t tag = (uint64_t)serial << 32;
+#pragma unroll
+                for (int p = 0; p < kAresEdge; ++p)
+                    if (psrc[p] >= 0)
+                        __hip_atomic_store(&e[pslot[p]], tag | __float_as_uint(lds[ob + psrc[p]]), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            }
+            // ---- the neighbours' edges of this chunk, and with a pending check
+            // every block's partial: all words in flight at once
+            uint64_t x1[kAresEdge];
+            uint32_t pv = 0;
+            {
+                const int par = (int)(serial & 1) * EW;
+                int off1[kAresEdge], off2[kAresPoll];
+                uint64_t x2[kAresPoll];
+#pragma unroll
+                for (int p = 0; p < kAresEdge; ++p) off1[p] = roff[p] >= 0 ? roff[p] + par : -1;
+#pragma unroll
+                for (int q = 0; q < kAresPoll; ++q) {
+                    const int i = tid + q * nthr;
+                    off2[q] = pending && i < G ? (red & 1) * G + i : -1;
+                }
+                if (!poll_tagged<kAresEdge, kAresPoll>(xbuf, off1, serial, x1, part64, off2, (uint32_t)red + 1u, x2,
+                                                       a.sc))
+                    gave_up = 1;
+#pragma unroll
+                for (int q = 0; q < kAresPoll; ++q) pv = off2[q] >= 0 && (uint32_t)x2[q] > pv ? (uint32_t)x2[q] : pv;
+            }
+            // ---- the pending check's decision (wmax was last read before this
+            // chunk's sweeps, each of which ends at a block barrier)
+            if (pending) {
+                block_max_put(wmax, pv);
+                __syncthreads();
+                if (gave_up) return;
+                R_bits = block_max_get(wmax);
+                ++red;
+                pending = false;
+                const float rho = __uint_as_float(R_bits) / bA;
+                const bool stop = !(rho >= a.tol);
+                if (stop || kc >= a.max_sweeps) {
+                    // JAC_ENAN : JAC_OK : JAC_ENOCONV; the result is u_kc, this chunk's input
+                    status = stop ? ((rho != rho) ? -5 : 0) : -4;
+                    cur = in;
+                    k = kc;
+                    break;
+                }
+            }
+            // ---- the halo of the next chunk, in all three copies
+#pragma unroll
+            for (int p = 0; p < kAresEdge; ++p)
+                if (roff[p] >= 0) {
+                    const float v = __uint_as_float((uint32_t)x1[p]);
+                    lds[rdst[p]] = v;
+                    lds[R + rdst[p]] = v;
+                    lds[2 * R + rdst[p]] = v;
+                }
+            __syncthreads();
+            if (gave_up) return;
+            // ---- a check point: the residual of u_k, whose halo is now the
+            // neighbours' u_k; the block's partial goes out for the next exchange
+            if (done == 0) {
+                uint32_t m = 0;
+#define JAC_ARES_CHECK(NQ) m = res_check<NQ>(lds, ob * 4, lp * 4, at, info, bv, r)
+                JAC_RES_NQ(JAC_ARES_CHECK)
+#undef JAC_ARES_CHECK
+                block_max_put(wmax, m);
+                __syncthreads();
+                if (tid == 0)
+                    __hip_atomic_store(&part64[(int64_t)(red & 1) * G + blockIdx.x],
+                                       ((uint64_t)(red + 1) << 32) | block_max_get(wmax), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                pending = true;
+                kc = k;
+            }
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            PersistOut o;
+            o.sweeps = k;
+            o.R_bits = R_bits;
+            o.bA_bits = bA_bits;
+            o.status = status;
+            o.cur = a.cur0;
+            a.out[step] = o;
+        }
+        if (status != 0) break;
+    }
+    // the field: the tile of the current iterate, into the buffer u^n came from
+    {
+        float* dst = (a.cur0 ? a.u1 : a.u0) + g.origin + (int64_t)ty0 * P + tx0;
+        const int ob = cur * R;
+        for (int k = tid; k < w * h; k += nthr) {
+            const int i = k / w, j = k - i * w;
+            dst[(int64_t)i * P + j] = lds[ob + (1 + i) * lp + 1 + j];
+        }
+    }
+}
+
 // Tile core for the exact tiles: large enough that staging and halo work stay
 // moderate, small enough to give several blocks work on small grids.
 static void persist_tiles(int N, int D, bool async_mode, int tile_x, int tile_y, int side, int* tx, int* ty) {
@@ -879,9 +1177,7 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
                           uint64_t* xchg, int64_t xchg_words, void* out, int nsteps, int cur0, bool async_mode, int D,
                           int L, int tile_x, int tile_y, int side, int64_t max_sweeps, int cus, int* grid_used,
                           hipStream_t stream) {
-    PersistPlan p;
-    hipError_t e = persist_plan(sa.g.N, D, async_mode, tile_x, tile_y, side, sa.fastdiv != 0, cus, &p);
-    if (e != hipSuccess) return e;
+    const int N = sa.g.N;
     PersistArgs a;
     a.g = sa.g;
     a.r = sa.r;
@@ -900,15 +1196,16 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
     a.async_mode = async_mode ? 1 : 0;
     a.D = D;
     a.L = L;
-    a.tx = p.tx;
-    a.ty = p.ty;
-    a.lds_cells = p.cells;
     a.sc = sa.sc;
     a.max_sweeps = max_sweeps;
-    // The exact kernels on a grid whose tiles all fit one round of co-resident
-    // blocks: resident tiles (k_persist_res); otherwise re-staged tiles
-    // (k_persist).  Resident tiles are square, side T: the band_rows option, else
-    // the smallest of 16, 32, 64 that fits (smaller tiles put more CUs on the
+    int dev = 0, max_lds = 0;
+    const bool have_lds = hipGetDevice(&dev) == hipSuccess &&
+                          hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess;
+    // Grids whose tiles all fit one round of co-resident blocks keep them
+    // resident: k_persist_res for the exact kernels, k_persist_ares for the
+    // block-asynchronous one; otherwise tiles are re-staged (k_persist).
+    // Exact resident tiles are square, side T: the band_rows option, else the
+    // smallest of 16, 32, 64 that fits (smaller tiles put more CUs on the
     // grid).  A tile is at least H = D + 1 cells on each side (a ragged last
     // tile too), the region's interior (T + 2H - 2)^2 fits the block's cells,
     // the region and the exchange maps its LDS, the exchange its words.
@@ -917,11 +1214,6 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
     const int H = D + 1;
     size_t rlds = 0;
     if (!async_mode) {
-        const int N = sa.g.N;
-        int dev = 0, max_lds = 0;
-        const bool have_lds = hipGetDevice(&dev) == hipSuccess &&
-                              hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
-                                  hipSuccess;
         const int sides[3] = {16, 32, 64};
         for (int si = 0; si < 3 && !resident && have_lds; ++si) {
             T = side > 0 ? side : sides[si];
@@ -945,21 +1237,58 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
             if (side > 0) break;
         }
     }
+    // Block-asynchronous resident tiles are the tile_x x tile_y tiles of the
+    // launch kernel, one thread per cell (at most 9 cells per thread past 1024
+    // cells, and at least tx + ty threads for the edges); three copies in LDS.
+    bool ares = false;
+    int athr = 0;
+    size_t alds = 0;
+    if (async_mode && have_lds) {
+        const int TX = tile_x, TY = tile_y;
+        const int want = TX * TY > TX + TY ? TX * TY : TX + TY;
+        athr = want >= kResThreads ? kResThreads : (want + 63) / 64 * 64;
+        const int64_t nt = (int64_t)((N + TX - 1) / TX) * ((N + TY - 1) / TY);
+        alds = (size_t)3 * (TX + 2) * (TY + 2) * sizeof(float);
+        int per_cu = 0;
+        if (TX * TY <= athr * kResCells && TX + TY <= athr && alds <= (size_t)max_lds &&
+            (sa.fastdiv ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_persist_ares<true>, athr, alds)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_persist_ares<false>, athr, alds)) ==
+                hipSuccess &&
+            per_cu > 0 && nt <= (int64_t)cus * per_cu && nt <= kMaxPersistBlocks && nt <= (int64_t)kAresPoll * athr &&
+            ares_exchange_words((int)nt, TX, TY) <= xchg_words) {
+            ares = true;
+            rgrid = (int)nt;
+        }
+    }
+    PersistPlan p;
     if (resident) {
         a.tx = a.ty = T;
+        a.lds_cells = 0;
+        *grid_used = rgrid;
+    } else if (ares) {
+        a.tx = tile_x;
+        a.ty = tile_y;
+        a.lds_cells = 0;
         *grid_used = rgrid;
     } else {
+        hipError_t e = persist_plan(N, D, async_mode, tile_x, tile_y, side, sa.fastdiv != 0, cus, &p);
+        if (e != hipSuccess) return e;
+        a.tx = p.tx;
+        a.ty = p.ty;
+        a.lds_cells = p.cells;
         *grid_used = p.grid;
     }
     // clear the barrier words (release, error) and the grid's flag lines with kernel fills
-    e = launch_fill(reinterpret_cast<float*>(&sa.sc->bar_release), 48, 0.0f, stream);
+    hipError_t e = launch_fill(reinterpret_cast<float*>(&sa.sc->bar_release), 48, 0.0f, stream);
     if (e == hipSuccess)
         e = launch_fill(reinterpret_cast<float*>(scratch_flags(sa.sc)), (int64_t)(*grid_used) * kFlagStride, 0.0f,
                         stream);
-    // tags of an earlier solve must not match: clear the exchange words
-    if (e == hipSuccess && resident)
-        e = launch_fill(reinterpret_cast<float*>(xchg), 2 * resident_exchange_words(rgrid, H, T), 0.0f, stream);
-    if (e == hipSuccess && resident)  // the 2 x grid tagged partial words
+    // tags of an earlier solve must not match: clear the exchange words and
+    // the 2 x grid tagged partial words
+    const int64_t xwords = resident ? resident_exchange_words(rgrid, H, T)
+                                    : ares ? ares_exchange_words(rgrid, tile_x, tile_y) : 0;
+    if (e == hipSuccess && xwords > 0) e = launch_fill(reinterpret_cast<float*>(xchg), 2 * xwords, 0.0f, stream);
+    if (e == hipSuccess && (resident || ares))
         e = launch_fill(reinterpret_cast<float*>(partial), 4 * (int64_t)rgrid, 0.0f, stream);
     if (e != hipSuccess) return e;
     void* args[] = {&a};
@@ -967,6 +1296,11 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
         const void* fr = sa.fastdiv ? reinterpret_cast<const void*>(k_persist_res<true>)
                                     : reinterpret_cast<const void*>(k_persist_res<false>);
         return hipLaunchCooperativeKernel(fr, dim3(rgrid), dim3(kResThreads), args, (unsigned)rlds, stream);
+    }
+    if (ares) {
+        const void* fa = sa.fastdiv ? reinterpret_cast<const void*>(k_persist_ares<true>)
+                                    : reinterpret_cast<const void*>(k_persist_ares<false>);
+        return hipLaunchCooperativeKernel(fa, dim3(rgrid), dim3(athr), args, (unsigned)alds, stream);
     }
     const void* fn = sa.fastdiv ? reinterpret_cast<const void*>(k_persist<true>)
                                 : reinterpret_cast<const void*>(k_persist<false>);

@@ -46,6 +46,56 @@ def test_async_bitwise(tile, D):
     assert_same(got, ref, f"{tile} D={D}")
 
 
+@pytest.mark.parametrize("N,tile,D", [(256, (32, 16), 8), (256, (32, 8), 4), (33, (32, 8), 8), (150, (64, 16), 12),
+                                      (1, (32, 8), 8), (2, (32, 16), 3), (97, (16, 16), 1), (300, (64, 60), 6),
+                                      (130, (1, 64), 5), (150, (7, 5), 3)])
+def test_async_resident_and_staged_tiles_bitwise(N, tile, D):
+    """Block-async under the persistent driver keeps each tile and a one-cell
+    halo in LDS (three copies: a chunk's input survives it until the check
+    that measured it is decided) and trades edges with its four neighbours
+    after every chunk, where all tiles fit one round: 32 x 16 and 32 x 8 tiles
+    at N = 256, ragged tiles one cell wide and high (N = 33), lone tiles
+    (N = 1, 2), 64 x 60 tiles (four cells per thread, ragged 44 cells wide),
+    one-column tiles.  More tiles than resident blocks (7 x 5 at
+    N = 150) takes re-staged tiles.  Both equal the oracle's block-async
+    model bit for bit."""
+    r = 10.0
+    say("persist async tiles", N, tile, D)
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=3, M=8, mode=oracle.ASYNC, D=D, tx=tile[0], ty=tile[1])
+    got = lib_solve(N, r, s, 3, opts(kernel=jac.JAC_ASYNC, D=D, tile_x=tile[0], tile_y=tile[1], driver=PER))
+    assert_same(got, ref, f"N={N} {tile} D={D}")
+
+
+@pytest.mark.parametrize("D", [3, 8])
+def test_async_resident_nan_and_noconv(D):
+    """A failed step ends the resident block-async solve with the oracle's
+    status and field (the checked iterate, not the chunk run past it)."""
+    N, r, tile = 200, 10.0, (32, 16)
+    say("persist async resident noconv/nan", D)
+    s = workloads.gaussian_source(N, r)
+    o = dict(kernel=jac.JAC_ASYNC, D=D, tile_x=tile[0], tile_y=tile[1], driver=PER)
+    for cap in (8, 40, 41):
+        ref = oracle.solve(N, r, s, steps=2, M=8, mode=oracle.ASYNC, D=D, tx=tile[0], ty=tile[1], max_sweeps=cap)
+        assert ref.status == oracle.ENOCONV
+        assert_same(lib_solve(N, r, s, 2, opts(max_sweeps=cap, **o)), ref, f"noconv D={D} cap={cap}")
+    u0 = np.zeros((N, N), np.float32)
+    u0[N // 3, N // 2] = np.inf
+    ref = oracle.solve(N, r, s, u0=u0, steps=2, M=8, mode=oracle.ASYNC, D=D, tx=tile[0], ty=tile[1])
+    assert ref.status == oracle.ENAN
+    assert_same(lib_solve(N, r, s, 2, opts(**o), u0=u0), ref, f"nan D={D}")
+
+
+@pytest.mark.parametrize("tile,D,r", [((32, 16), 8, 10.0), ((32, 8), 4, 10.0), ((32, 16), 8, 1.0)])
+def test_config_c5_async_bitwise(tile, D, r):
+    """N = 256, ten steps of block-async in one kernel with resident tiles."""
+    say("persist C5 async", tile, D, r)
+    s = workloads.gaussian_source(256, r)
+    ref = oracle.solve(256, r, s, M=8, mode=oracle.ASYNC, D=D, tx=tile[0], ty=tile[1])
+    got = lib_solve(256, r, s, 10, opts(kernel=jac.JAC_ASYNC, D=D, tile_x=tile[0], tile_y=tile[1], driver=PER))
+    assert_same(got, ref, f"C5 async {tile} D={D} r={r}")
+
+
 @pytest.mark.parametrize("kernel,D", [(jac.JAC_SYNC, 1), (jac.JAC_TBLOCK, 8)])
 @pytest.mark.parametrize("r", [1.0, 10.0])
 def test_config_c5_bitwise(kernel, D, r):
