@@ -77,7 +77,14 @@ enum jac_checks {
                                    LAUNCH: launches of up to D sweeps measure the residual of the
                                    levels where checks fall (at most two); a check that stops at an
                                    inner level is followed by a launch that recomputes that iterate
-                                   from the launch's input; a launch ends on a predicted check */
+                                   from the launch's input; a launch ends on a predicted check.  A
+                                   check that is neither predicted to stop (below 2 * tol) nor within
+                                   two intervals of the previous step's count measures the residual on
+                                   every 8th row only, where no iterate can overflow: that maximum
+                                   bounds R from below, so at or above tol it decides the check
+                                   exactly; below tol the iterate is measured again in full.
+                                   JACOBI_SAMPLED_CHECKS=n at create time sets the row stride (a power
+                                   of two; 0 or 1: every row) */
     JAC_CHECKS_BLOCKING = 1     /* after each interval a standalone residual kernel, then the host waits
                                    for R and decides before anything more is queued */
 };
@@ -278,7 +285,9 @@ int jac_stream_probe(float* c, const float* a, const float* b, size_t n, int kin
  * 5 residual only, 6 persistent solve, 7 launches issued ahead of a check that
  * stopped the step (they return at once and do no sweep), 8 one-block
  * reductions of a check or of ||b_A||, 9 the first temporal-blocking launch of
- * a step when it also forms b (launch driver, overlapped checks).
+ * a step when it also forms b (launch driver, overlapped checks), 10 a deep
+ * temporal-blocking launch shorter than D (one that ends on a check, or one
+ * that recomputes the iterate a check inside a launch stopped at).
  */
 int jac_profile(jac_t ctx, int every);
 int jac_profile_read(jac_t ctx, int kclass, double* ms_timed, int64_t* launches, int64_t* timed_launches);

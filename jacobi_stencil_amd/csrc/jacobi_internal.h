@@ -125,6 +125,10 @@ struct StepArgs {
     int64_t part_off;  // the reduction reads partial slots from here
     int slot2;         // >= 0: the reduction also reduces the next npart slots, a second check, into this
                        // mailbox slot (a launch that checks two levels)
+    // per checked level, a row mask: a temporal-blocking launch measures the
+    // residual on the rows i with (i & smask) == 0 only (0: every row).  Their
+    // maximum is a lower bound of R, enough to show that a check goes on.
+    int smask[2];
 };
 
 // ---------------------------------------------------------------- device

@@ -298,6 +298,7 @@ struct TBStream {
     uint32_t m;     // running max |res| (CHK) or |b_A| (RHS), as bits
     uint32_t m2;    // D >= 9: running max |res| of the second checked level
     int chk0, chk1; // D >= 9: the checked levels (chk1 < 0: one)
+    int sm0, sm1;   // their row masks: the residual is taken on rows i with (i & mask) == 0
 
     // One row j: read it, push every level one row further, store level D.
     // UP/MID/NEW are the level registers in this row's rotation.
@@ -346,7 +347,7 @@ struct TBStream {
                     const bool at1 = CL >= 0 ? (t - 1 == C1) : (t - 1 == chk1);
                     if (at0 || at1) {
                         const int i = j - DIR * t;
-                        if (i >= y0 && i <= last) {
+                        if (i >= y0 && i <= last && (i & (at0 ? sm0 : sm1)) == 0) {
                             const uint32_t v = DIR > 0 ? level_residual(UP[t - 1], MID[t - 1], NEW[t - 1], bb, r, L)
                                                        : level_residual(NEW[t - 1], MID[t - 1], UP[t - 1], bb, r, L);
                             if (at0) m = m > v ? m : v;
@@ -356,7 +357,7 @@ struct TBStream {
                 } else if (CHK && t == 1) {
                     // residual of u_k on the row level 1 computes, from the stencil it reads
                     const int i = j - DIR;
-                    if (i >= y0 && i <= last) {
+                    if (i >= y0 && i <= last && (i & sm0) == 0) {
                         const uint32_t v = DIR > 0 ? level_residual(UP[0], MID[0], NEW[0], bb, r, L)
                                                    : level_residual(NEW[0], MID[0], UP[0], bb, r, L);
                         m = m > v ? m : v;
@@ -397,6 +398,8 @@ __device__ __forceinline__ uint32_t tb_band(const float* __restrict__ uin, const
     st.m2 = 0;
     st.chk0 = a.chk[0];
     st.chk1 = a.chk[1];
+    st.sm0 = a.smask[0];
+    st.sm1 = a.smask[1];
     const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     st.nu = zero;
     st.nb = zero;

@@ -97,6 +97,9 @@ struct jac_ctx {
     int fastdiv;     // 1: the constant-divisor quotient was verified for this d
     bool rhs_pending;  // the next temporal-blocking launch forms b itself (first of a step)
     float predict_margin;  // overlapped checks: a check predicted below margin * tol runs alone (0: never)
+    int sample_rows;       // deep temporal blocking: checks far from the stop measure every sample_rows-th row (0: off)
+    int64_t prev_sweeps;   // sweeps of the previous step (0: none yet)
+    int64_t verified;      // sampled checks below tol measured again in full
     int fast_now;    // division path of the work being enqueued (see division_path)
     bool src_plain;  // the source is finite and holds no -0
     double smax;     // max |s|
@@ -191,6 +194,8 @@ StepArgs base_args(const jac_ctx* c, float tol) {
     a.force = 0;
     a.part_off = 0;
     a.slot2 = -1;
+    a.smask[0] = 0;
+    a.smask[1] = 0;
     return a;
 }
 
@@ -628,11 +633,15 @@ int run_step_blocking(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float*
 // (g - 1) % kRing and followed by that check's event.  `force` runs it even
 // after a check has stopped the step (a redo).
 int enqueue_tb_deep(jac_ctx* c, const jac_opts* o, int m, const int* levels, const int64_t* g, bool force,
-                    int* buf) {
+                    int* buf, const int* smask = nullptr) {
     StepArgs a = base_args(c, o->tol);
     const bool check = levels[0] >= 0;
     a.chk[0] = levels[0];
     a.chk[1] = levels[1];
+    if (smask) {
+        a.smask[0] = smask[0];
+        a.smask[1] = smask[1];
+    }
     a.force = force ? 1 : 0;
     a.slot = check ? (int)((g[0] - 1) % kRing) : 0;
     if (check && m <= 8 && (levels[0] != 0 || levels[1] >= 0))
@@ -706,10 +715,24 @@ int run_step_deep(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho
         int buf;            // the buffer holding the input of the launch that measured it
         int level;          // its level in that launch (0: the input itself)
         int64_t launch;     // that launch's profiling group
+        bool sampled;       // measured on every sample_rows-th row: a lower bound of R
     };
     Pending info[kRing];
     auto stops_here = [&](int64_t g) {
         return g >= gmax || hist.predicts_stop(g, o->tol, c->predict_margin);
+    };
+    // Checks far from the stop measure a sample of the rows, only where no
+    // residual can be NaN or overflow (every iterate and b bounded by Ub, as
+    // for the constant-divisor path), so that a sample >= tol decides exactly
+    // what the whole residual would.
+    double Ub = 0.0;
+    const bool may_sample =
+        c->sample_rows > 1 && c->fast_now &&
+        division_path(c, 1, (double)o->max_sweeps + (double)L + 2.0 * (double)D, &Ub) &&
+        (8.0 + 8.0 * (double)c->r) * Ub * 1.001 < (double)FLT_MAX;
+    auto sampled = [&](int64_t g) {
+        return may_sample && !stops_here(g) && !hist.predicts_stop(g, o->tol, kSampleFar) &&
+               !(c->prev_sweeps > 0 && g * L >= c->prev_sweeps - 2 * L);
     };
     auto enqueue_more = [&]() -> int {
         const int64_t gk = g_next;
@@ -722,7 +745,7 @@ int run_step_deep(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho
             int s2 = enqueue_residual(c, o, buf, slot);
             if (s2) return s2;
             JAC_HIP(hipEventRecord(c->ev[gk % kRing], c->stream));
-            info[gk % kRing] = Pending{buf, 0, c->cur_group};
+            info[gk % kRing] = Pending{buf, 0, c->cur_group, false};
             final_enqueued = true;
             if (gk < gmax) predicted = gk;
             g_next = gk + 1;
@@ -739,18 +762,21 @@ int run_step_deep(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho
         if (m <= 8) m = std::min<int64_t>(m, gk * L == k ? L : gk * L - k);  // the shallow kernels check only their input
         int levels[2] = {-1, -1};
         int64_t gs[2] = {0, 0};
+        int sm[2] = {0, 0};
         int n = 0;
         for (int64_t g = gk; g * L < k + m && n < 2; ++g, ++n) {
             levels[n] = (int)(g * L - k);
             gs[n] = g;
+            sm[n] = sampled(g) ? c->sample_rows - 1 : 0;
             c->mail->R[(g - 1) % kRing] = kEmpty;
         }
         c->cur_group = launch_no++;
         c->cur_first = true;
         const int in_buf = buf;
-        int s2 = enqueue_tb_deep(c, o, (int)m, levels, gs, false, &buf);
+        int s2 = enqueue_tb_deep(c, o, (int)m, levels, gs, false, &buf, sm);
         if (s2) return s2;
-        for (int q = 0; q < n; ++q) info[gs[q] % kRing] = Pending{in_buf, levels[q], c->cur_group};
+        for (int q = 0; q < n; ++q)
+            info[gs[q] % kRing] = Pending{in_buf, levels[q], c->cur_group, sm[q] != 0};
         k += m;
         g_next = gk + n;
         return JAC_OK;
@@ -772,25 +798,52 @@ int run_step_deep(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho
         const bool stop = !(rho >= o->tol);
         if (stop || kk >= o->max_sweeps) {
             const Pending p = info[ev];
+            // every launch queued behind the check returned at once (stop flag)
             if (c->prof_every > 0 && stop) mark_noops(c, p.launch);
-            for (int64_t i = 0; i < g; ++i) c->dlog.push_back(D);
-            if (p.level == 0) {
-                c->cur = p.buf;
-            } else {
-                // the result u_{gL} lies p.level sweeps past the intact input
-                int b2 = p.buf;
+            // u_{gL}: the intact input, or p.level sweeps past it (a redo)
+            int b2 = p.buf;
+            if (p.level > 0) {
                 const int none[2] = {-1, -1};
                 const int64_t g0[2] = {0, 0};
                 c->cur_group = p.launch;
                 c->cur_first = true;
                 st = enqueue_tb_deep(c, o, p.level, none, g0, true, &b2);
                 if (st) return st;
-                c->cur = b2;
             }
+            float rho_f = rho;
+            if (p.sampled) {
+                // a sample below tol decides nothing: the whole residual of
+                // u_{gL}, with the stop flag cleared (behind the launches that
+                // returned at once) so that its reduction reports
+                JAC_HIP(launch_fill(reinterpret_cast<float*>(&c->sc->stop), 1, 0.0f, c->stream));
+                c->mail->R[slot] = kEmpty;
+                c->cur_group = p.launch;
+                c->cur_first = false;
+                st = enqueue_residual(c, o, b2, slot);
+                if (st) return st;
+                JAC_HIP(hipEventRecord(c->ev[ev], c->stream));
+                JAC_HIP(hipEventSynchronize(c->ev[ev]));
+                if (await_mail(c, &c->mail->R[slot]) == kEmpty) return fail(JAC_EDEVICE, "a residual check did not report");
+                rho_f = mail_float(&c->mail->R[slot]) / mail_float(&c->mail->bA_bits);
+                c->verified += 1;
+                if (rho_f >= o->tol) {
+                    // the step goes on from u_{gL}
+                    buf = b2;
+                    k = kk;
+                    g_next = g + 1;
+                    final_enqueued = false;
+                    predicted = 0;
+                    hist.push(g, rho_f);
+                    continue;
+                }
+            }
+            for (int64_t i = 0; i < g; ++i) c->dlog.push_back(D);
+            c->cur = b2;
+            c->prev_sweeps = kk;
             if (sweeps_out) *sweeps_out = kk;
-            if (rho_out) *rho_out = rho;
-            if (std::isnan(rho)) return fail(JAC_ENAN, "rho is NaN");
-            if (!stop) return fail(JAC_ENOCONV, "max_sweeps reached before rho < tol");
+            if (rho_out) *rho_out = rho_f;
+            if (std::isnan(rho_f)) return fail(JAC_ENAN, "rho is NaN");
+            if (rho_f >= o->tol) return fail(JAC_ENOCONV, "max_sweeps reached before rho < tol");
             return JAC_OK;
         }
         hist.push(g, rho);
@@ -1131,6 +1184,14 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
         const char* pm = std::getenv("JACOBI_PREDICT_MARGIN");
         const float m = pm ? std::strtof(pm, nullptr) : kPredictMargin;
         c->predict_margin = (std::isfinite(m) && m > 0.0f) ? m : 0.0f;
+        // JACOBI_SAMPLED_CHECKS=n at create time: the row stride of the
+        // residual a deep temporal-blocking launch takes at a check that is
+        // not expected to stop (a power of two; 0 or 1: every row)
+        const char* sr = std::getenv("JACOBI_SAMPLED_CHECKS");
+        long n = sr ? std::strtol(sr, nullptr, 10) : (long)kSampleRows;
+        c->sample_rows = (n >= 2 && n <= (1L << 20) && (n & (n - 1)) == 0) ? (int)n : 0;
+        c->prev_sweeps = 0;
+        c->verified = 0;
     }
     c->prof_every = 0;
     c->step_serial = 0;
@@ -1330,6 +1391,7 @@ int jac_reset(jac_t c) {
     c->cur = 0;
     JAC_HIP(hipStreamSynchronize(c->stream));
     c->ubound = 100.0;
+    c->prev_sweeps = 0;
     return JAC_OK;
 }
 

@@ -40,12 +40,17 @@ def solve_profiled(N, r, s, steps, o, u0=None):
 @pytest.mark.parametrize("D", list(range(9, 17)))
 def test_deep_launches_bitwise(D, M, margin, monkeypatch):
     """Every depth over checks every 8 and every 5 sweeps, with prediction off
-    (stops land inside launches: redo launches), at its default and forced at
-    every check (launches end on each predicted check, most predictions fail)."""
+    (stops land inside launches: redo launches; row-sampled checks off too, so
+    that no check is measured twice), at its default and forced at every check
+    (launches end on each predicted check, most predictions fail)."""
     if margin is None:
         monkeypatch.delenv("JACOBI_PREDICT_MARGIN", raising=False)
     else:
         monkeypatch.setenv("JACOBI_PREDICT_MARGIN", margin)
+    if margin == "0":
+        monkeypatch.setenv("JACOBI_SAMPLED_CHECKS", "0")
+    else:
+        monkeypatch.delenv("JACOBI_SAMPLED_CHECKS", raising=False)
     N, r = 150, 10.0
     say("deep", D, M, margin)
     s = workloads.random_source(N, r, 31)
@@ -126,3 +131,40 @@ def test_deep_band_heights_and_graph_and_blocking_bitwise():
     assert_same(res, ref, "blocking")
     res, _ = solve_profiled(N, r, s, 2, opts(kernel=TB, D=11, driver=jac.JAC_PERSISTENT))
     assert_same(res, ref, "persistent")
+
+
+@pytest.mark.parametrize("D,M", [(11, 8), (9, 8), (12, 8), (16, 5)])
+def test_sampled_checks_bitwise(D, M, monkeypatch):
+    """A check that is not expected to stop measures the residual on every
+    8th row: that maximum bounds R from below, so a sample at or above tol
+    decides the check exactly, and a sample below tol is measured again in
+    full before the step stops or goes on.  With only row 0 sampled (stride
+    2^20) many late checks are measured twice, and the step goes on from the
+    checked iterate; with sampling off every check measures every row.  All
+    three give the oracle's sweeps, rho and field bit for bit."""
+    N, r = 300, 10.0
+    s = workloads.gaussian_source(N, r)
+    u0 = workloads.random_field(N, 7)
+    ref = oracle.solve(N, r, s, u0=u0, steps=3, M=M)
+    runs = {}
+    for stride in ("0", "8", "1048576"):
+        monkeypatch.setenv("JACOBI_SAMPLED_CHECKS", stride)
+        say("deep sampled", D, M, stride)
+        res, n = solve_profiled(N, r, s, 3, opts(kernel=TB, D=D, M=M), u0=u0)
+        assert_same(res, ref, f"D={D} M={M} stride={stride}")
+        runs[stride] = n
+    # every sample below tol is measured again by a residual pass of its own
+    assert runs["1048576"]["residual"] > runs["0"]["residual"]
+
+
+def test_sampled_checks_c3_shape(monkeypatch):
+    """N = 1024, r = 10, the benchmark's depth and interval: sampled checks
+    (the default) against sampling off, both the oracle's bits."""
+    N, r = 1024, 10.0
+    s = workloads.gaussian_source(N, r)
+    ref = oracle.solve(N, r, s, steps=2, M=8)
+    for stride in ("8", "0"):
+        monkeypatch.setenv("JACOBI_SAMPLED_CHECKS", stride)
+        say("deep sampled N=1024", stride)
+        res, _ = solve_profiled(N, r, s, 2, opts(kernel=TB, D=11, M=8))
+        assert_same(res, ref, f"stride={stride}")
