@@ -100,6 +100,7 @@ struct jac_ctx {
     int sample_rows;       // deep temporal blocking: checks far from the stop measure every sample_rows-th row (0: off)
     int64_t prev_sweeps;   // sweeps of the previous step (0: none yet)
     int64_t verified;      // sampled checks below tol measured again in full
+    int cur_smask;         // row mask of the next checking temporal-blocking launch (0: every row)
     int fast_now;    // division path of the work being enqueued (see division_path)
     bool src_plain;  // the source is finite and holds no -0
     double smax;     // max |s|
@@ -360,6 +361,7 @@ int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, i
             }
             if (check && npart > c->npart_cap)
                 return fail(JAC_EINVAL, "band_rows too small for this N: too many wavefront bands");
+            if (check) a.smask[0] = c->cur_smask;
             st = timed(c, KC_TBLOCK, [&] { return launch_tblock(in, c->b, out, m, check, a, H, c->stream); });
             break;
         }
@@ -903,6 +905,18 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
     bool final_enqueued = false;
     int64_t predicted = 0;  // the check queued alone on a prediction (0: none)
     CheckHistory hist;
+    // Temporal-blocking launches measure checks far from the stop on a sample
+    // of the rows, as run_step_deep does (same bound, same policy)
+    double Ub = 0.0;
+    const bool may_sample =
+        !graph && o->kernel == JAC_TBLOCK && c->sample_rows > 1 && c->fast_now &&
+        division_path(c, 1, (double)o->max_sweeps + 2.0 * (double)L, &Ub) &&
+        (8.0 + 8.0 * (double)c->r) * Ub * 1.001 < (double)FLT_MAX;
+    bool samp[kRing] = {};
+    auto sampled = [&](int64_t g) {
+        return may_sample && !hist.predicts_stop(g, o->tol, kSampleFar) &&
+               !(c->prev_sweeps > 0 && g * L >= c->prev_sweeps - 2 * L);
+    };
     // the interval after check g, from u_{gL}, without a check (group 0's form)
     auto enqueue_plain_interval = [&](int64_t g) -> int {
         c->cur_group = g;
@@ -925,6 +939,7 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
         c->mail->R[slot] = kEmpty;
         c->cur_group = g_enq;
         c->cur_first = true;
+        samp[ev] = false;
         int s2;
         if (g_enq * L >= o->max_sweeps) {
             // the last allowed check: measure only, keep u_{gL} in place
@@ -950,7 +965,10 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
         } else {
             // one launch that checks u_{gL} and starts the next interval, then the rest
             const int64_t first = std::min<int64_t>(L, sweeps_per_launch(o));
+            samp[ev] = sampled(g_enq);
+            c->cur_smask = samp[ev] ? c->sample_rows - 1 : 0;
             s2 = enqueue_sweeps(c, o, first, true, slot, &buf);
+            c->cur_smask = 0;
             if (s2) return s2;
             JAC_HIP(hipEventRecord(c->ev[ev], c->stream));
             s2 = enqueue_sweeps(c, o, L - first, false, slot, &buf);
@@ -978,12 +996,41 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
         const bool stop = !(rho >= o->tol);
         if (stop || k >= o->max_sweeps) {
             if (c->prof_every > 0 && stop) mark_noops(c, g);
+            float rho_f = rho;
+            if (samp[ev] && stop) {
+                // a sample below tol decides nothing: the whole residual of
+                // u_{gL} (intact: every launch behind the check returned at
+                // once), with the stop flag cleared so that its reduction reports
+                JAC_HIP(launch_fill(reinterpret_cast<float*>(&c->sc->stop), 1, 0.0f, c->stream));
+                c->mail->R[slot] = kEmpty;
+                c->cur_group = g;
+                c->cur_first = false;
+                st = enqueue_residual(c, o, c->start_buf[ev], slot);
+                if (st) return st;
+                JAC_HIP(hipEventRecord(c->ev[ev], c->stream));
+                JAC_HIP(hipEventSynchronize(c->ev[ev]));
+                if (await_mail(c, &c->mail->R[slot]) == kEmpty) return fail(JAC_EDEVICE, "a residual check did not report");
+                rho_f = mail_float(&c->mail->R[slot]) / mail_float(&c->mail->bA_bits);
+                c->verified += 1;
+                if (rho_f >= o->tol) {
+                    // the step goes on: the interval after check g, from u_{gL}
+                    buf = c->start_buf[ev];
+                    g_enq = g + 1;
+                    final_enqueued = false;
+                    predicted = 0;
+                    hist.push(g, rho_f);
+                    st = enqueue_plain_interval(g);
+                    if (st) return st;
+                    continue;
+                }
+            }
             for (int64_t i = 0; i < g; ++i) c->dlog.push_back(sweeps_per_launch(o));
             c->cur = c->start_buf[ev];
+            c->prev_sweeps = k;
             if (sweeps_out) *sweeps_out = k;
-            if (rho_out) *rho_out = rho;
-            if (std::isnan(rho)) return fail(JAC_ENAN, "rho is NaN");
-            if (!stop) return fail(JAC_ENOCONV, "max_sweeps reached before rho < tol");
+            if (rho_out) *rho_out = rho_f;
+            if (std::isnan(rho_f)) return fail(JAC_ENAN, "rho is NaN");
+            if (rho_f >= o->tol) return fail(JAC_ENOCONV, "max_sweeps reached before rho < tol");
             return JAC_OK;
         }
         hist.push(g, rho);
@@ -1192,6 +1239,7 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
         c->sample_rows = (n >= 2 && n <= (1L << 20) && (n & (n - 1)) == 0) ? (int)n : 0;
         c->prev_sweeps = 0;
         c->verified = 0;
+        c->cur_smask = 0;
     }
     c->prof_every = 0;
     c->step_serial = 0;

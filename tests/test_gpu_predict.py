@@ -42,6 +42,12 @@ def test_prediction_keeps_oracle_bits(kernel, D, driver, margin, monkeypatch):
         monkeypatch.delenv("JACOBI_PREDICT_MARGIN", raising=False)
     else:
         monkeypatch.setenv("JACOBI_PREDICT_MARGIN", margin)
+    # with the prediction off, no residual pass of its own may run: row-sampled
+    # checks (whose samples below tol are measured again in full) off as well
+    if margin == "0":
+        monkeypatch.setenv("JACOBI_SAMPLED_CHECKS", "0")
+    else:
+        monkeypatch.delenv("JACOBI_SAMPLED_CHECKS", raising=False)
     N, r = 150, 10.0
     say("predict", kernel, D, driver, margin)
     s = workloads.random_source(N, r, 21)

@@ -297,3 +297,32 @@ def test_config_c4_against_stored_oracle(kernel, D):
             assert field_hash(sol.field()) == exp["field_sha256"][n], f"step {n}"
     finally:
         sol.close()
+
+
+@pytest.mark.parametrize("D", [8, 5, 4, 1])
+def test_sampled_checks_bitwise(D, monkeypatch):
+    """Launches of at most 8 sweeps measure the residual of their input; a
+    check not expected to stop takes it on every 8th row (a lower bound of R
+    that decides a going-on check exactly), and a sample below tol is measured
+    again in full, the step then stopping or going on with the interval after
+    the check.  Row 0 alone (stride 2^20) forces many such second
+    measurements; stride 0 turns sampling off.  All give the oracle's bits."""
+    N, r = 300, 10.0
+    s = workloads.gaussian_source(N, r)
+    u0 = workloads.random_field(N, 7)
+    ref = oracle.solve(N, r, s, u0=u0, steps=3, M=8)
+    counts = {}
+    for stride in ("0", "8", "1048576"):
+        monkeypatch.setenv("JACOBI_SAMPLED_CHECKS", stride)
+        say("tblock sampled", D, stride)
+        sol = jac.Solver(N, r, s)
+        try:
+            sol.set_field(u0)
+            sol.profile(1)
+            st, k, rho = sol.solve(3, opts(kernel=jac.JAC_TBLOCK, D=D))
+            got = (st, sol.field(), k, rho)
+            counts[stride] = sol.profile_read("residual")[1]
+        finally:
+            sol.close()
+        assert_same(got, ref, f"D={D} stride={stride}")
+    assert counts["1048576"] > counts["0"]
