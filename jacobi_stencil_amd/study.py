@@ -221,7 +221,10 @@ def study_depths(a):
     base = R.run(N, r, steps, kernel=jac.JAC_SYNC)
     base.update(study="depths", family="sync", D=1, s=1.0, c=1.0)
     _emit(a.out, base)
-    for fam, kernel, kc in (("temporal", jac.JAC_TBLOCK, "tblock"), ("async_32x16", jac.JAC_ASYNC, "async")):
+    fams = (("temporal", jac.JAC_TBLOCK, "tblock"), ("async_32x16", jac.JAC_ASYNC, "async"))
+    for fam, kernel, kc in fams:
+        if a.family != "all" and not fam.startswith(a.family):
+            continue
         for D in range(1, 17):
             o = dict(kernel=kernel, D=D, tile_x=32, tile_y=16)
             rec = R.run(N, r, steps, **o)
@@ -311,6 +314,8 @@ def main():
     ap.add_argument("--out", default=None)
     ap.add_argument("--repeats", type=int, default=3)
     ap.add_argument("--quick", action="store_true")
+    ap.add_argument("--family", choices=("all", "temporal", "async"), default="all",
+                    help="depths: the strategy families to run")
     a = ap.parse_args()
     {"checks": study_checks, "regimes": study_regimes, "controllers": study_controllers,
      "overlap": study_overlap, "depths": study_depths, "launches": study_launches, "fit": fit}[a.study](a)
