@@ -64,6 +64,7 @@ struct PersistArgs {
     int async_mode;      // 0: exact tiles (ghost zone), 1: block-asynchronous tiles
     int D, L;            // sweeps per chunk, check interval
     int tx, ty;          // tile core
+    int group;           // resident block-asynchronous tiles: tiles per block
     int lds_cells;       // staged region of the deepest chunk; the second LDS buffer starts there
     int64_t max_sweeps;
     Scratch* sc;         // barrier words (cleared by the host before the launch)
@@ -838,45 +839,65 @@ __global__ __launch_bounds__(kResThreads) void k_persist_res(PersistArgs a) {
 // ---------------------------------------------------------------- resident block-asynchronous tiles
 //
 // The block-asynchronous kernel (ASYNC) on grids whose tiles all fit one round
-// of co-resident blocks: each block owns one tx x ty tile and keeps three
-// copies of it, each with a one-cell halo, in LDS, and b of its cells in
-// registers.  A chunk of Dc sweeps updates the tile with its halo frozen --
-// exactly one block-asynchronous launch (page "stencil-jacobian.vercel.app",
-// section 02) -- and writes only the two copies other than its input, so the
-// chunk's input survives it.  The block then publishes its four edges and
-// refills its halo from its neighbours' edges (no corners: the five-point
-// stencil never reads them), in the tagged-word exchange described above,
-// here one cell deep.  A check at k = gL (g >= 1) measures the residual of
-// u_k once the halo holds the neighbours' u_k, as the re-staged kernel
-// measures it at the start of the next chunk; the grid-wide maximum completes
-// under the next chunk's exchange, and a stop keeps u_k, that chunk's
-// preserved input, whose halo the dropped refill has left as it was.
+// of co-resident blocks: each block owns a group of G consecutive tx x ty
+// tiles (in row-major tile order; G = 1 on small grids) and keeps three copies
+// of each, with a one-cell halo, in LDS, and b of its cells in registers.  A
+// chunk of Dc sweeps updates every tile with its halo frozen -- exactly one
+// block-asynchronous launch (page "stencil-jacobian.vercel.app", section 02):
+// tiles of one block see each other only through the halo refill, as tiles of
+// different blocks do -- and writes only the two copies other than its input,
+// so the chunk's input survives it.  Each tile then publishes its four edges
+// and refills its halo from its neighbours' edges (no corners: the five-point
+// stencil never reads them), in the tagged-word exchange described above, here
+// one cell deep.  A check at k = gL (g >= 1) measures the residual of u_k once
+// the halo holds the neighbours' u_k, as the re-staged kernel measures it at
+// the start of the next chunk; the grid-wide maximum completes under the next
+// chunk's exchange, and a stop keeps u_k, that chunk's preserved input, whose
+// halo the dropped refill has left as it was.
 //
 // Exchange memory: per tile and parity 2 (tx + ty) words -- the top row
 // [0, tx), the bottom row [tx, 2tx), the left column [2tx, 2tx + ty), the
 // right column [2tx + ty, 2tx + 2ty) of the tile.  Tiles in one column share
 // a width and tiles in one row a height, so every halo cell lies in one
 // neighbour's edge, whatever the ragged last tiles.
+//
+// LDS: copy c of tile q of the group at floats (c G + q) R, R = (tx+2)(ty+2);
+// the tile's cells at rows 1..h, columns 1..w of its copy (pitch tx + 2).
 
-constexpr int kAresEdge = 2;  // edge words published and taken per thread: tx + ty <= block size
+constexpr int kAresEdge = 2;  // edge words published and taken per thread: G (tx + ty) <= block size
 constexpr int kAresPoll = 4;  // partial slots per thread: grid <= 4 x block size
 
 int64_t ares_exchange_words(int ntiles, int tx, int ty) { return (int64_t)ntiles * 4 * (tx + ty); }
 
-// Dc sweeps from copy `in` (copies R floats apart) through the other two
+// Dc sweeps from copy `in` (copies RB floats apart) through the other two
 // copies; returns the copy that holds the last sweep.
 template <bool FAST, int NQ>
-__device__ __forceinline__ int ares_sweeps(float* lds, int in, int Dc, int R, int lp4, const int* at,
+__device__ __forceinline__ int ares_sweeps(float* lds, int in, int Dc, int RB, int lp4, const int* at,
                                            const uint32_t* info, const float* bv, float r, float d, float y) {
     const int x = in == 2 ? 0 : in + 1, z = 3 - in - x;
     int src = in, dst = x;
     for (int sw = 1; sw <= Dc; ++sw) {
-        res_sweep<FAST, NQ>(lds, src * R * 4, dst * R * 4, lp4, at, info, bv, r, d, y);
+        res_sweep<FAST, NQ>(lds, src * RB * 4, dst * RB * 4, lp4, at, info, bv, r, d, y);
         __syncthreads();
         src = dst;
         dst = dst == x ? z : x;
     }
     return src;
+}
+
+// Geometry of tile t of a tx x ty tiling of the N x N grid.
+struct AresTile {
+    int ti, tj, x0, y0, w, h;
+};
+__device__ __forceinline__ AresTile ares_tile(int t, int N, int TX, int TY, int ntx) {
+    AresTile g;
+    g.ti = t / ntx;
+    g.tj = t - g.ti * ntx;
+    g.x0 = g.tj * TX;
+    g.y0 = g.ti * TY;
+    g.w = g.x0 + TX <= N ? TX : N - g.x0;
+    g.h = g.y0 + TY <= N ? TY : N - g.y0;
+    return g;
 }
 
 template <bool FAST>
@@ -886,78 +907,91 @@ __global__ __launch_bounds__(kResThreads) void k_persist_ares(PersistArgs a) {
     __shared__ uint32_t gave_up;  // a wait of this block outlasted the spin budget
     const Geom g = a.g;
     const int N = g.N, P = g.P;
-    const int TX = a.tx, TY = a.ty;
+    const int TX = a.tx, TY = a.ty, GT = a.group;
     const int ntx = (N + TX - 1) / TX, nty = (N + TY - 1) / TY;
-    const int tile = blockIdx.x;
-    const int ti = tile / ntx, tj = tile % ntx;
-    const int tx0 = tj * TX, ty0 = ti * TY;
-    const int w = tx0 + TX <= N ? TX : N - tx0, h = ty0 + TY <= N ? TY : N - ty0;
-    const int lp = TX + 2;          // copy pitch; the tile's cells sit at rows 1..h, columns 1..w
-    const int R = lp * (TY + 2);    // floats per copy
-    const int EW = 2 * (TX + TY);   // exchange words per tile and parity
+    const int t0 = blockIdx.x * GT;                                    // the group's first tile
+    const int ng = ntx * nty - t0 < GT ? ntx * nty - t0 : GT;         // tiles in this group
+    const int lp = TX + 2;            // copy pitch
+    const int R = lp * (TY + 2);      // floats per tile copy
+    const int RB = GT * R;            // floats per copy of the group
+    const int TC = TX * TY;           // cell slots per tile
+    const int EW = 2 * (TX + TY);     // exchange words per tile and parity
     const float r = a.r, d = a.d, y = a.y;
     const int tid = threadIdx.x, nthr = blockDim.x;
     if (tid < kResWaves) wmax[tid] = 0;  // the words of absent waves stay 0
     if (tid == 0) gave_up = 0;
-    // the tile and its halo of u^n (ghost cells included) into all three copies
-    {
-        const float* src = (a.cur0 ? a.u1 : a.u0) + g.origin + (int64_t)(ty0 - 1) * P + (tx0 - 1);
-        const int rw = w + 2;
-        for (int k = tid; k < rw * (h + 2); k += nthr) {
+    // each tile and its halo of u^n (ghost cells included) into all three copies
+    for (int q = 0; q < ng; ++q) {
+        const AresTile T = ares_tile(t0 + q, N, TX, TY, ntx);
+        const float* src = (a.cur0 ? a.u1 : a.u0) + g.origin + (int64_t)(T.y0 - 1) * P + (T.x0 - 1);
+        const int rw = T.w + 2;
+        for (int k = tid; k < rw * (T.h + 2); k += nthr) {
             const int rr = k / rw, cc = k - rr * rw;
             const float v = src[(int64_t)rr * P + cc];
-            const int c = rr * lp + cc;
+            const int c = q * R + rr * lp + cc;
             lds[c] = v;
-            lds[R + c] = v;
-            lds[2 * R + c] = v;
+            lds[RB + c] = v;
+            lds[2 * RB + c] = v;
         }
     }
-    // this thread's tile cells k = tid + q*nthr (row k / w, column k % w): the
-    // byte offset of the west neighbour and its bits; a lane past the tile
-    // keeps cell 0's offset and no bits
-    const int ncell = w * h;
-    const int nq = (ncell + nthr - 1) / nthr;
+    // this thread's cells k = tid + n*nthr: tile k / TC of the group, cell
+    // k % TC of it (row / w, column % w); the byte offset of the west
+    // neighbour in copy 0 and the cell's bits; a lane past the cells keeps
+    // cell 0's offset and no bits
+    const int nq = (ng * TC + nthr - 1) / nthr;
     int at[kResCells];
     uint32_t info[kResCells];
 #pragma unroll
-    for (int q = 0; q < kResCells; ++q) {
-        const int k = tid + q * nthr;
-        const int kk = k < ncell ? k : 0;
-        const int i = kk / w, j = kk - (kk / w) * w;
-        at[q] = ((1 + i) * lp + j) * 4;
-        info[q] = k < ncell ? (kCellUnk | kCellCore | (ty0 + i == 0 ? kCellTop : 0u)) : 0u;
+    for (int n = 0; n < kResCells; ++n) {
+        const int k = tid + n * nthr;
+        const int q = k / TC, l = k - q * TC;
+        at[n] = lp * 4;
+        info[n] = 0u;
+        if (q < ng) {
+            const AresTile T = ares_tile(t0 + q, N, TX, TY, ntx);
+            if (l < T.w * T.h) {
+                const int i = l / T.w, j = l - i * T.w;
+                at[n] = (q * R + (1 + i) * lp + j) * 4;
+                info[n] = kCellUnk | kCellCore | (T.y0 + i == 0 ? kCellTop : 0u);
+            }
+        }
     }
-    // the edge words this thread publishes (LDS cell, slot) and takes
-    // (neighbour word without parity, LDS cell; -1: none or a ghost)
-    int psrc[kAresEdge], pslot[kAresEdge], roff[kAresEdge], rdst[kAresEdge];
+    // the edge words this thread publishes (LDS cell, word without parity)
+    // and takes (neighbour word without parity, LDS cell; -1: none or a ghost)
+    int psrc[kAresEdge], pword[kAresEdge], roff[kAresEdge], rdst[kAresEdge];
 #pragma unroll
     for (int p = 0; p < kAresEdge; ++p) {
         const int e = tid + p * nthr;
+        const int q = e / EW, le = e - q * EW;
         psrc[p] = -1;
-        pslot[p] = 0;
+        pword[p] = 0;
         roff[p] = -1;
         rdst[p] = 0;
-        int nb = -1;
-        if (e < w) {  // top row; the halo row above from the north tile's bottom row
-            psrc[p] = lp + 1 + e;
-            pslot[p] = e;
-            if (ti > 0) nb = (ti - 1) * ntx + tj, roff[p] = TX + e, rdst[p] = 1 + e;
-        } else if (e < 2 * w) {  // bottom row; the halo row below from the south tile's top row
-            const int jj = e - w;
-            psrc[p] = h * lp + 1 + jj;
-            pslot[p] = TX + jj;
-            if (ti + 1 < nty) nb = (ti + 1) * ntx + tj, roff[p] = jj, rdst[p] = (h + 1) * lp + 1 + jj;
-        } else if (e < 2 * w + h) {  // left column; the halo column left from the west tile's right column
-            const int ii = e - 2 * w;
-            psrc[p] = (1 + ii) * lp + 1;
-            pslot[p] = 2 * TX + ii;
-            if (tj > 0) nb = ti * ntx + tj - 1, roff[p] = 2 * TX + TY + ii, rdst[p] = (1 + ii) * lp;
-        } else if (e < 2 * w + 2 * h) {  // right column; the halo column right from the east tile's left column
-            const int ii = e - 2 * w - h;
-            psrc[p] = (1 + ii) * lp + w;
-            pslot[p] = 2 * TX + TY + ii;
-            if (tj + 1 < ntx) nb = ti * ntx + tj + 1, roff[p] = 2 * TX + ii, rdst[p] = (1 + ii) * lp + w + 1;
+        if (q >= ng) continue;
+        const AresTile T = ares_tile(t0 + q, N, TX, TY, ntx);
+        const int w = T.w, h = T.h, ti = T.ti, tj = T.tj, base = q * R;
+        int nb = -1, slot = 0;
+        if (le < w) {  // top row; the halo row above from the north tile's bottom row
+            psrc[p] = base + lp + 1 + le;
+            slot = le;
+            if (ti > 0) nb = (ti - 1) * ntx + tj, roff[p] = TX + le, rdst[p] = base + 1 + le;
+        } else if (le < 2 * w) {  // bottom row; the halo row below from the south tile's top row
+            const int jj = le - w;
+            psrc[p] = base + h * lp + 1 + jj;
+            slot = TX + jj;
+            if (ti + 1 < nty) nb = (ti + 1) * ntx + tj, roff[p] = jj, rdst[p] = base + (h + 1) * lp + 1 + jj;
+        } else if (le < 2 * w + h) {  // left column; the halo column left from the west tile's right column
+            const int ii = le - 2 * w;
+            psrc[p] = base + (1 + ii) * lp + 1;
+            slot = 2 * TX + ii;
+            if (tj > 0) nb = ti * ntx + tj - 1, roff[p] = 2 * TX + TY + ii, rdst[p] = base + (1 + ii) * lp;
+        } else if (le < 2 * w + 2 * h) {  // right column; the halo column right from the east tile's left column
+            const int ii = le - 2 * w - h;
+            psrc[p] = base + (1 + ii) * lp + w;
+            slot = 2 * TX + TY + ii;
+            if (tj + 1 < ntx) nb = ti * ntx + tj + 1, roff[p] = 2 * TX + ii, rdst[p] = base + (1 + ii) * lp + w + 1;
         }
+        pword[p] = (t0 + q) * 2 * EW + slot;
         if (nb >= 0) roff[p] += nb * 2 * EW;
     }
     __syncthreads();
@@ -971,21 +1005,23 @@ __global__ __launch_bounds__(kResThreads) void k_persist_ares(PersistArgs a) {
     int status = 1;
     float bv[kResCells];    // b of this thread's cells
     for (int step = 0; step < a.nsteps; ++step) {
-        // ---- b = u^n + s on the tile, max |b + r*g|
+        // ---- b = u^n + s on the tiles, max |b + r*g|
         {
             __syncthreads();  // every thread has read the last reduction from wmax
-            const int ob4 = cur * R * 4;
+            const int ob4 = cur * RB * 4;
             uint32_t m = 0;
 #pragma unroll
-            for (int q = 0; q < kResCells; ++q) {
-                bv[q] = 0.0f;
-                if (!(info[q] & kCellUnk)) continue;
-                const int k = tid + q * nthr, i = k / w, j = k - (k / w) * w;
-                bv[q] = lds_at(lds, at[q] + ob4 + 4) + a.s[g.origin + (int64_t)(ty0 + i) * P + tx0 + j];
+            for (int n = 0; n < kResCells; ++n) {
+                bv[n] = 0.0f;
+                if (!(info[n] & kCellUnk)) continue;
+                const int k = tid + n * nthr, q = k / TC, l = k - q * TC;
+                const AresTile T = ares_tile(t0 + q, N, TX, TY, ntx);
+                const int i = l / T.w, j = l - i * T.w;
+                bv[n] = lds_at(lds, at[n] + ob4 + 4) + a.s[g.origin + (int64_t)(T.y0 + i) * P + T.x0 + j];
                 float tg = kTop;
                 asm volatile("" : "+v"(tg));
-                const float rg = r * ((info[q] & kCellTop) ? tg : 0.0f);
-                const uint32_t v = __float_as_uint(fabsf(bv[q] + rg));
+                const float rg = r * ((info[n] & kCellTop) ? tg : 0.0f);
+                const uint32_t v = __float_as_uint(fabsf(bv[n] + rg));
                 m = m > v ? m : v;
             }
             block_max_put(wmax, m);
@@ -1023,24 +1059,24 @@ __global__ __launch_bounds__(kResThreads) void k_persist_ares(PersistArgs a) {
             const int left = a.L - done;
             const int Dc = a.D < left ? a.D : left;
             const int in = cur;
-            // ---- Dc sweeps with the halo frozen, into the copies other than `in`
-#define JAC_ARES_SWEEPS(NQ) cur = ares_sweeps<FAST, NQ>(lds, in, Dc, R, lp * 4, at, info, bv, r, d, y)
+            // ---- Dc sweeps with the halos frozen, into the copies other than `in`
+#define JAC_ARES_SWEEPS(NQ) cur = ares_sweeps<FAST, NQ>(lds, in, Dc, RB, lp * 4, at, info, bv, r, d, y)
             JAC_RES_NQ(JAC_ARES_SWEEPS)
 #undef JAC_ARES_SWEEPS
             k += Dc;
             done += Dc;
             if (done == a.L) done = 0;
             ++serial;
-            const int ob = cur * R;
-            // ---- publish the tile's edges, tagged with the chunk number
+            const int ob = cur * RB;
+            // ---- publish the tiles' edges, tagged with the chunk number
             {
-                uint64_t* e = xbuf + ((int64_t)tile * 2 + (serial & 1)) * EW;
+                const int par = (int)(serial & 1) * EW;
                 const uint64_t tag = (uint64_t)serial << 32;
 #pragma unroll
                 for (int p = 0; p < kAresEdge; ++p)
                     if (psrc[p] >= 0)
-                        __hip_atomic_store(&e[pslot[p]], tag | __float_as_uint(lds[ob + psrc[p]]), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(&xbuf[pword[p] + par], tag | __float_as_uint(lds[ob + psrc[p]]),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             // ---- the neighbours' edges of this chunk, and with a pending check
             // every block's partial: all words in flight at once
@@ -1082,18 +1118,18 @@ __global__ __launch_bounds__(kResThreads) void k_persist_ares(PersistArgs a) {
                     break;
                 }
             }
-            // ---- the halo of the next chunk, in all three copies
+            // ---- the halos of the next chunk, in all three copies
 #pragma unroll
             for (int p = 0; p < kAresEdge; ++p)
                 if (roff[p] >= 0) {
                     const float v = __uint_as_float((uint32_t)x1[p]);
                     lds[rdst[p]] = v;
-                    lds[R + rdst[p]] = v;
-                    lds[2 * R + rdst[p]] = v;
+                    lds[RB + rdst[p]] = v;
+                    lds[2 * RB + rdst[p]] = v;
                 }
             __syncthreads();
             if (gave_up) return;
-            // ---- a check point: the residual of u_k, whose halo is now the
+            // ---- a check point: the residual of u_k, whose halos are now the
             // neighbours' u_k; the block's partial goes out for the next exchange
             if (done == 0) {
                 uint32_t m = 0;
@@ -1121,12 +1157,13 @@ __global__ __launch_bounds__(kResThreads) void k_persist_ares(PersistArgs a) {
         }
         if (status != 0) break;
     }
-    // the field: the tile of the current iterate, into the buffer u^n came from
-    {
-        float* dst = (a.cur0 ? a.u1 : a.u0) + g.origin + (int64_t)ty0 * P + tx0;
-        const int ob = cur * R;
-        for (int k = tid; k < w * h; k += nthr) {
-            const int i = k / w, j = k - i * w;
+    // the field: each tile of the current iterate, into the buffer u^n came from
+    for (int q = 0; q < ng; ++q) {
+        const AresTile T = ares_tile(t0 + q, N, TX, TY, ntx);
+        float* dst = (a.cur0 ? a.u1 : a.u0) + g.origin + (int64_t)T.y0 * P + T.x0;
+        const int ob = cur * RB + q * R;
+        for (int k = tid; k < T.w * T.h; k += nthr) {
+            const int i = k / T.w, j = k - i * T.w;
             dst[(int64_t)i * P + j] = lds[ob + (1 + i) * lp + 1 + j];
         }
     }
@@ -1197,6 +1234,7 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
     a.D = D;
     a.L = L;
     a.sc = sa.sc;
+    a.group = 1;
     a.max_sweeps = max_sweeps;
     int dev = 0, max_lds = 0;
     const bool have_lds = hipGetDevice(&dev) == hipSuccess &&
@@ -1238,26 +1276,46 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
         }
     }
     // Block-asynchronous resident tiles are the tile_x x tile_y tiles of the
-    // launch kernel, one thread per cell (at most 9 cells per thread past 1024
-    // cells, and at least tx + ty threads for the edges); three copies in LDS.
+    // launch kernel, in groups of G consecutive tiles per block: the smallest
+    // G of 1, 2, 4, 8, 16 (more blocks on small grids) and, for it, the
+    // largest block of 1024 ... 64 threads with at most 9 cells and 2 edge
+    // words per thread whose grid fits one round; three copies per tile in LDS.
     bool ares = false;
-    int athr = 0;
+    int athr = 0, agroup = 1;
     size_t alds = 0;
     if (async_mode && have_lds) {
-        const int TX = tile_x, TY = tile_y;
-        const int want = TX * TY > TX + TY ? TX * TY : TX + TY;
-        athr = want >= kResThreads ? kResThreads : (want + 63) / 64 * 64;
-        const int64_t nt = (int64_t)((N + TX - 1) / TX) * ((N + TY - 1) / TY);
-        alds = (size_t)3 * (TX + 2) * (TY + 2) * sizeof(float);
-        int per_cu = 0;
-        if (TX * TY <= athr * kResCells && TX + TY <= athr && alds <= (size_t)max_lds &&
-            (sa.fastdiv ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_persist_ares<true>, athr, alds)
-                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_persist_ares<false>, athr, alds)) ==
-                hipSuccess &&
-            per_cu > 0 && nt <= (int64_t)cus * per_cu && nt <= kMaxPersistBlocks && nt <= (int64_t)kAresPoll * athr &&
-            ares_exchange_words((int)nt, TX, TY) <= xchg_words) {
-            ares = true;
-            rgrid = (int)nt;
+        const int TX = tile_x, TY = tile_y, TC = TX * TY;
+        const int64_t ntiles = (int64_t)((N + TX - 1) / TX) * ((N + TY - 1) / TY);
+        for (int G = 1; G <= 16 && !ares; G *= 2) {
+            if (G > 1 && ntiles < 2 * (int64_t)G) break;  // groups larger than the grid gain nothing
+            const int64_t nb = (ntiles + G - 1) / G;
+            const size_t lds_g = (size_t)3 * G * (TX + 2) * (TY + 2) * sizeof(float);
+            if (lds_g > (size_t)max_lds) break;
+            // block sizes: one thread per cell (a multiple of 64, at most 1024), then
+            // the powers of two below it (whole wavefronts: the block maxima read lane 63)
+            const int64_t want = (int64_t)G * (TC > TX + TY ? TC : TX + TY);
+            const int first = want >= kResThreads ? kResThreads : (int)((want + 63) / 64 * 64);
+            int cand[8], nc = 0;
+            cand[nc++] = first;
+            for (int t = kResThreads; t >= 64; t /= 2)
+                if (t < first) cand[nc++] = t;
+            for (int ci = 0; ci < nc && !ares; ++ci) {
+                const int thr = cand[ci];
+                if ((int64_t)G * TC > (int64_t)thr * kResCells || (int64_t)G * (TX + TY) > thr) break;
+                int per_cu = 0;
+                if ((sa.fastdiv ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_persist_ares<true>, thr,
+                                                                              lds_g)
+                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_persist_ares<false>, thr,
+                                                                              lds_g)) == hipSuccess &&
+                    per_cu > 0 && nb <= (int64_t)cus * per_cu && nb <= kMaxPersistBlocks &&
+                    nb <= (int64_t)kAresPoll * thr && ares_exchange_words((int)ntiles, TX, TY) <= xchg_words) {
+                    ares = true;
+                    athr = thr;
+                    agroup = G;
+                    alds = lds_g;
+                    rgrid = (int)nb;
+                }
+            }
         }
     }
     PersistPlan p;
@@ -1268,6 +1326,7 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
     } else if (ares) {
         a.tx = tile_x;
         a.ty = tile_y;
+        a.group = agroup;
         a.lds_cells = 0;
         *grid_used = rgrid;
     } else {
@@ -1285,8 +1344,11 @@ hipError_t launch_persist(const StepArgs& sa, float* u0, float* u1, float* b, co
                         stream);
     // tags of an earlier solve must not match: clear the exchange words and
     // the 2 x grid tagged partial words
-    const int64_t xwords = resident ? resident_exchange_words(rgrid, H, T)
-                                    : ares ? ares_exchange_words(rgrid, tile_x, tile_y) : 0;
+    const int64_t xwords =
+        resident ? resident_exchange_words(rgrid, H, T)
+                 : ares ? ares_exchange_words((int)((int64_t)((N + tile_x - 1) / tile_x) * ((N + tile_y - 1) / tile_y)),
+                                              tile_x, tile_y)
+                        : 0;
     if (e == hipSuccess && xwords > 0) e = launch_fill(reinterpret_cast<float*>(xchg), 2 * xwords, 0.0f, stream);
     if (e == hipSuccess && (resident || ares))
         e = launch_fill(reinterpret_cast<float*>(partial), 4 * (int64_t)rgrid, 0.0f, stream);

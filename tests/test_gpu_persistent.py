@@ -48,7 +48,8 @@ def test_async_bitwise(tile, D):
 
 @pytest.mark.parametrize("N,tile,D", [(256, (32, 16), 8), (256, (32, 8), 4), (33, (32, 8), 8), (150, (64, 16), 12),
                                       (1, (32, 8), 8), (2, (32, 16), 3), (97, (16, 16), 1), (300, (64, 60), 6),
-                                      (130, (1, 64), 5), (150, (7, 5), 3)])
+                                      (130, (1, 64), 5), (150, (7, 5), 3), (1024, (32, 16), 8), (700, (32, 8), 4),
+                                      (1000, (16, 16), 3), (1500, (64, 64), 2)])
 def test_async_resident_and_staged_tiles_bitwise(N, tile, D):
     """Block-async under the persistent driver keeps each tile and a one-cell
     halo in LDS (three copies: a chunk's input survives it until the check
@@ -56,9 +57,12 @@ def test_async_resident_and_staged_tiles_bitwise(N, tile, D):
     after every chunk, where all tiles fit one round: 32 x 16 and 32 x 8 tiles
     at N = 256, ragged tiles one cell wide and high (N = 33), lone tiles
     (N = 1, 2), 64 x 60 tiles (four cells per thread, ragged 44 cells wide),
-    one-column tiles.  More tiles than resident blocks (7 x 5 at
-    N = 150) takes re-staged tiles.  Both equal the oracle's block-async
-    model bit for bit."""
+    one-column tiles.  Where one tile per block does not fit one round, each
+    block holds a group of consecutive tiles (7 x 5 at N = 150, 32 x 16 at
+    N = 1024: 2048 tiles, 32 x 8 at N = 700 and 16 x 16 at N = 1000, ragged,
+    the last group short).  Tiles that no group fits in one round (64 x 64 at
+    N = 1500: 576 tiles of 4096 cells) take re-staged tiles.  Both equal the
+    oracle's block-async model bit for bit."""
     r = 10.0
     say("persist async tiles", N, tile, D)
     s = workloads.gaussian_source(N, r)
