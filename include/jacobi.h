@@ -78,7 +78,7 @@ enum jac_checks {
                                    levels where checks fall (at most two); a check that stops at an
                                    inner level is followed by a launch that recomputes that iterate
                                    from the launch's input; a launch ends on a predicted check.  Under
-                                   LAUNCH, a TBLOCK or ASYNC check that is neither predicted to stop
+                                   LAUNCH, a TBLOCK check that is neither predicted to stop
                                    (below 2 * tol) nor within
                                    two intervals of the previous step's count measures the residual on
                                    every 8th row only, where no iterate can overflow: that maximum

@@ -95,12 +95,10 @@ __global__ __launch_bounds__(kAsyncThreads) void k_async(const float* __restrict
         }
         __syncthreads();
         if (CHK) {
-            // residual of u_k on the tile's own points (the halo is u_k too),
-            // on the rows the check's row mask keeps
-            const int sm = a.smask[0];
+            // residual of u_k on the tile's own points (the halo is u_k too)
 #pragma unroll
             for (int q = 0; q < kAsyncPerThread; ++q) {
-                if (q < nq && (ij[q] & 0x80000000u) && ((ey0 + (int)((ij[q] >> 16) & 0x7FFFu)) & sm) == 0) {
+                if (q < nq && (ij[q] & 0x80000000u)) {
                     const int c = cl[q];
                     const uint32_t v = residual_bits(A[c], A[c + 1], A[c - 1], A[c - lp], A[c + lp], bb[q], r);
                     m = m > v ? m : v;
@@ -199,7 +197,7 @@ __device__ __forceinline__ uint32_t async_strip(const float* __restrict__ uin, c
             const float Nn = i > 0 ? src[i - 1] : top;
             const float Sn = i + 1 < TY ? src[i + 1] : bot;
             const bool live = (!EDGE || Y + i < N) && in_col;
-            if (CHK && check && ((Y + i) & a.smask[0]) == 0) {  // rows the row mask keeps
+            if (CHK && check) {
                 const uint32_t e = residual_bits(c, E, W, Nn, Sn, bb[i], r);
                 if (live) m = m > e ? m : e;
             }
@@ -328,7 +326,7 @@ __device__ __forceinline__ uint32_t async_wide_strip(const float* __restrict__ u
         const float l = from_left(c.w), rr = from_right(c.x);  // in every lane, then select
         const float W = west ? hw[i] : l;
         const float E = east ? he[i] : rr;
-        if (CHK && check && ((Y + i) & a.smask[0]) == 0) residual_row(i, c, n, sth, W, E);  // rows the mask keeps
+        if (CHK && check) residual_row(i, c, n, sth, W, E);
         float4 v;
         v.x = jacobi_update<FAST>(c.y, W, n.x, sth.x, bb[i].x, r, d, y);
         v.y = jacobi_update<FAST>(c.z, c.x, n.y, sth.y, bb[i].y, r, d, y);
