@@ -79,7 +79,7 @@ enum jac_checks {
                                    inner level is followed by a launch that recomputes that iterate
                                    from the launch's input; a launch ends on a predicted check.  Under
                                    LAUNCH, a TBLOCK check that is neither predicted to stop
-                                   (below 2 * tol) nor within
+                                   (below 1.25 * tol) nor within
                                    two intervals of the previous step's count measures the residual on
                                    every 8th row only, where no iterate can overflow: that maximum
                                    bounds R from below, so at or above tol it decides the check

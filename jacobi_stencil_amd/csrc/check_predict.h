@@ -18,14 +18,14 @@ namespace jac {
 
 constexpr float kPredictMargin = 0.97f;
 
-// Deep temporal blocking: a check that is not expected to stop measures the
-// residual on every kSampleRows-th row only.  That maximum bounds R from
-// below, so a sample at or above tol shows that the step goes on, exactly as
-// the full residual would; a sample below tol is checked again in full.  A
-// check predicted below kSampleFar * tol, or within two intervals of the
-// previous step's sweep count, measures every row.
+// Temporal blocking through the launch driver: a check that is not expected
+// to stop measures the residual on every kSampleRows-th row only.  That
+// maximum bounds R from below, so a sample at or above tol shows that the
+// step goes on, exactly as the full residual would; a sample below tol is
+// checked again in full.  A check predicted below kSampleFar * tol, or within
+// two intervals of the previous step's sweep count, measures every row.
 constexpr int kSampleRows = 8;
-constexpr float kSampleFar = 2.0f;
+constexpr float kSampleFar = 1.25f;
 
 struct CheckHistory {
     float rho[3] = {0.0f, 0.0f, 0.0f};  // rho of the last three checks of the step, newest first
