@@ -71,12 +71,13 @@ def test_async_resident_and_staged_tiles_bitwise(N, tile, D):
     assert_same(got, ref, f"N={N} {tile} D={D}")
 
 
-@pytest.mark.parametrize("D", [3, 8])
-def test_async_resident_nan_and_noconv(D):
+@pytest.mark.parametrize("N,D", [(200, 3), (200, 8), (1024, 8)])
+def test_async_resident_nan_and_noconv(N, D):
     """A failed step ends the resident block-async solve with the oracle's
-    status and field (the checked iterate, not the chunk run past it)."""
-    N, r, tile = 200, 10.0, (32, 16)
-    say("persist async resident noconv/nan", D)
+    status and field (the checked iterate, not the chunk run past it), with
+    one tile per block (N = 200) and with two (N = 1024)."""
+    r, tile = 10.0, (32, 16)
+    say("persist async resident noconv/nan", N, D)
     s = workloads.gaussian_source(N, r)
     o = dict(kernel=jac.JAC_ASYNC, D=D, tile_x=tile[0], tile_y=tile[1], driver=PER)
     for cap in (8, 40, 41):
