@@ -78,8 +78,10 @@ enum jac_checks {
                                    levels where checks fall (at most two); a check that stops at an
                                    inner level is followed by a launch that recomputes that iterate
                                    from the launch's input; a launch ends on a predicted check.  Under
-                                   LAUNCH, a TBLOCK check that is neither predicted to stop
-                                   (below 1.25 * tol) nor within
+                                   LAUNCH, a TBLOCK check (and an ASYNC one in launches of at most 8
+                                   sweeps whose tiles the one-lane strip kernel runs with a height
+                                   that is a multiple of 8, such as 32 x 16) that is neither predicted
+                                   to stop (below 1.25 * tol) nor within
                                    two intervals of the previous step's count measures the residual on
                                    every 8th row only, where no iterate can overflow: that maximum
                                    bounds R from below, so at or above tol it decides the check

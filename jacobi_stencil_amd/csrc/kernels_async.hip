@@ -151,7 +151,7 @@ bool async_wave_form(int tx, int ty, int o) {
     return o == 0 && (tx == 8 || tx == 16 || tx == 32 || tx == 64) && (ty == 4 || ty == 8 || ty == 16 || ty == 32);
 }
 
-template <int TY, bool EDGE, bool CHK, bool FAST>
+template <int TY, bool EDGE, bool CHK, bool FAST, bool SMP>
 __device__ __forceinline__ uint32_t async_strip(const float* __restrict__ uin, const float* __restrict__ bin,
                                                 float* __restrict__ uout, const StepArgs& a, int tx, int D, int X,
                                                 int Y) {
@@ -197,7 +197,7 @@ __device__ __forceinline__ uint32_t async_strip(const float* __restrict__ uin, c
             const float Nn = i > 0 ? src[i - 1] : top;
             const float Sn = i + 1 < TY ? src[i + 1] : bot;
             const bool live = (!EDGE || Y + i < N) && in_col;
-            if (CHK && check) {
+            if (CHK && check && (!SMP || (i & 7) == 0)) {  // SMP: every 8th row (the strip starts on one)
                 const uint32_t e = residual_bits(c, E, W, Nn, Sn, bb[i], r);
                 if (live) m = m > e ? m : e;
             }
@@ -223,7 +223,7 @@ __device__ __forceinline__ uint32_t async_strip(const float* __restrict__ uin, c
     return m;
 }
 
-template <int TY, bool CHK, bool FAST>
+template <int TY, bool CHK, bool FAST, bool SMP = false>
 __global__ __launch_bounds__(256) void k_async_wave(const float* __restrict__ uin, const float* __restrict__ bin,
                                                     float* __restrict__ uout, StepArgs a, int tx, int D) {
     if (a.sc->stop) return;  // a previous check already stopped the step
@@ -234,9 +234,9 @@ __global__ __launch_bounds__(256) void k_async_wave(const float* __restrict__ ui
     if (wid < sx * sy) {
         const int X = (wid % sx) * kWaveStrip, Y = (wid / sx) * TY;
         if (X + kWaveStrip <= N && Y + TY <= N)
-            m = async_strip<TY, false, CHK, FAST>(uin, bin, uout, a, tx, D, X, Y);
+            m = async_strip<TY, false, CHK, FAST, SMP>(uin, bin, uout, a, tx, D, X, Y);
         else
-            m = async_strip<TY, true, CHK, FAST>(uin, bin, uout, a, tx, D, X, Y);
+            m = async_strip<TY, true, CHK, FAST, SMP>(uin, bin, uout, a, tx, D, X, Y);
     }
     if (CHK) store_block_max<4>(m, a.sc, blockIdx.x);
 }
@@ -264,6 +264,14 @@ bool async_wide_form(int N, int tx, int ty, int o) {
     if (!(o == 0 && tx % 4 == 0 && kWideStrip % tx == 0 && (ty == 4 || ty == 8))) return false;
     const int64_t waves = (int64_t)((N + kWideStrip - 1) / kWideStrip) * ((N + ty - 1) / ty);
     return waves >= kWideMinWaves;
+}
+
+// Checking launches of D sweeps on this tiling take a check's residual on
+// every 8th row when asked (row mask 7, constant-divisor path): the one-lane
+// strip kernel with strips a multiple of 8 rows tall, for D <= 8 (deeper
+// launches of that variant ran slower than the residual they save).
+bool async_samples_rows(int N, int tx, int ty, int o, int D) {
+    return !async_wide_form(N, tx, ty, o) && async_wave_form(tx, ty, o) && ty % 8 == 0 && D <= 8;
 }
 
 template <int TY, bool EDGE, bool CHK, bool FAST>
@@ -429,6 +437,13 @@ static void launch_wave_t(const float* uin, const float* b, float* uout, int tx,
                           const StepArgs& a, dim3 grid, hipStream_t s) {
     const dim3 block(256);
     if (check) {
+        if constexpr (TY % 8 == 0) {
+            // a check far from the stop: the residual on every 8th row (strips start on one)
+            if (a.fastdiv && a.smask[0] == 7 && D <= 8) {
+                hipLaunchKernelGGL((k_async_wave<TY, true, true, true>), grid, block, 0, s, uin, b, uout, a, tx, D);
+                return;
+            }
+        }
         if (a.fastdiv)
             hipLaunchKernelGGL((k_async_wave<TY, true, true>), grid, block, 0, s, uin, b, uout, a, tx, D);
         else

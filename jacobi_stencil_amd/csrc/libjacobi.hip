@@ -34,6 +34,12 @@
 
 using namespace jac;
 
+namespace jac {
+// kernels_async.hip: whether checking launches of D sweeps on this tiling
+// honour a row mask of 7 (take a check's residual on every 8th row)
+bool async_samples_rows(int N, int tx, int ty, int o, int D);
+}  // namespace jac
+
 namespace {
 
 thread_local std::string g_err;
@@ -368,6 +374,7 @@ int enqueue_launch(jac_ctx* c, const jac_opts* o, int m, bool check, int slot, i
         case JAC_ASYNC:
             npart = async_blocks(c->N, o->tile_x, o->tile_y, o->overlap);
             if (check && npart > c->npart_cap) return fail(JAC_EINVAL, "tile too small for this N");
+            if (check) a.smask[0] = c->cur_smask;
             st = timed(c, KC_ASYNC, [&] {
                 return launch_async(in, c->b, out, o->tile_x, o->tile_y, m, o->overlap, check, a, c->stream);
             });
@@ -909,7 +916,11 @@ int run_step(jac_ctx* c, const jac_opts* o, int64_t* sweeps_out, float* rho_out)
     // of the rows, as run_step_deep does (same bound, same policy)
     double Ub = 0.0;
     const bool may_sample =
-        !graph && o->kernel == JAC_TBLOCK && c->sample_rows > 1 && c->fast_now &&
+        !graph && c->sample_rows > 1 &&
+        (o->kernel == JAC_TBLOCK ||
+         (o->kernel == JAC_ASYNC && c->sample_rows == 8 &&
+          async_samples_rows(c->N, o->tile_x, o->tile_y, o->overlap, o->D))) &&
+        c->fast_now &&
         division_path(c, 1, (double)o->max_sweeps + 2.0 * (double)L, &Ub) &&
         (8.0 + 8.0 * (double)c->r) * Ub * 1.001 < (double)FLT_MAX;
     bool samp[kRing] = {};

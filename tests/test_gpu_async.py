@@ -241,3 +241,28 @@ def test_page_tolerance_at_full_size(cfg):
         assert margin <= 1e-4, f"{cfg} D{D}: {margin:.3e} ||b_A||"
         del u
 
+
+
+@pytest.mark.parametrize("tile,D", [((32, 16), 8), ((32, 8), 8), ((16, 16), 4), ((32, 16), 3)])
+def test_async_sampled_checks_bitwise(tile, D, monkeypatch):
+    """Block-async launches of at most 8 sweeps on strips a multiple of 8 rows
+    tall take a check that is not expected to stop on every 8th row (a lower
+    bound of R that decides a going-on check exactly); a sample below tol is
+    measured again in full by a residual pass, and the step stops there or
+    goes on with the interval after the check.  With sampling off and on,
+    the oracle's block-async bits."""
+    N, r = 300, 10.0
+    s = workloads.gaussian_source(N, r)
+    u0 = workloads.random_field(N, 7)
+    ref = oracle.solve(N, r, s, u0=u0, steps=3, M=8, mode=oracle.ASYNC, D=D, tx=tile[0], ty=tile[1])
+    for stride in ("0", "8"):
+        monkeypatch.setenv("JACOBI_SAMPLED_CHECKS", stride)
+        say("async sampled", tile, D, stride)
+        sol = jac.Solver(N, r, s)
+        try:
+            sol.set_field(u0)
+            st, k, rho = sol.solve(3, opts(kernel=jac.JAC_ASYNC, D=D, tile_x=tile[0], tile_y=tile[1]))
+            got = (st, sol.field(), k, rho)
+        finally:
+            sol.close()
+        assert_same(got, ref, f"{tile} D={D} stride={stride}")
