@@ -188,10 +188,14 @@ def test_mirror_symmetry_bitwise(orc, N, kind, r):
 
 def test_thread_count_does_not_change_results(orc):
     s = workloads.gaussian_source(70, 10.0)
-    orc.set_threads(1)
-    a = orc.solve(70, 10.0, s, steps=2)
-    orc.set_threads(8)
-    b = orc.solve(70, 10.0, s, steps=2)
+    before = orc.get_threads()
+    try:
+        orc.set_threads(1)
+        a = orc.solve(70, 10.0, s, steps=2)
+        orc.set_threads(8)
+        b = orc.solve(70, 10.0, s, steps=2)
+    finally:
+        orc.set_threads(before)
     assert np.array_equal(a.u, b.u) and np.array_equal(a.sweeps, b.sweeps)
 
 

@@ -57,6 +57,11 @@ def test_mutant_fails_a_pin(name, tmp_path):
     lib = tmp_path / "libmutant.so"
     subprocess.run(["gcc", *oracle.CFLAGS, str(msrc), "-o", str(lib), "-lm"], check=True)
     env = dict(os.environ, JACOBI_ORACLE_LIB=str(lib))
+    # under parallel test workers, share the cores out: OpenMP threads that
+    # spin at barriers on oversubscribed cores slow the pins a hundredfold
+    workers = int(os.environ.get("PYTEST_XDIST_WORKER_COUNT", "1"))
+    if workers > 1:
+        env["OMP_NUM_THREADS"] = str(max(1, (os.cpu_count() or 1) // workers))
     proc = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                            os.path.join(ROOT, "tests", "test_oracle.py")],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
