@@ -49,7 +49,7 @@ enum jac_status {
     JAC_ENOMEM = -2,   /* workspace too small, or host allocation failed */
     JAC_EDEVICE = -3,  /* a HIP call failed (message names it) */
     JAC_ENOCONV = -4,  /* max_sweeps reached without rho < tol */
-    JAC_ENAN = -5      /* rho is NaN (a NaN or Inf reached the field) */
+    JAC_ENAN = -5      /* rho is NaN (a NaN or Inf reached the field, or R = ||b_A|| = 0: r = 0 with b = 0) */
 };
 
 /* Sweep kernels. */

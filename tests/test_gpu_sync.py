@@ -131,6 +131,24 @@ def test_nan_source_gives_enan():
     assert np.array_equal(bits(u[ok]), bits(ref.u[ok]))
 
 
+@pytest.mark.parametrize("kernel,D,tile", [(jac.JAC_SYNC, 1, (32, 8)), (jac.JAC_TBLOCK, 8, (32, 8)),
+                                           (jac.JAC_TBLOCK, 11, (32, 8)), (jac.JAC_ASYNC, 8, (32, 16)),
+                                           (jac.JAC_ASYNC, 4, (32, 8))])
+def test_zero_problem_gives_enan(kernel, D, tile):
+    """r = 0, s = 0 from u = 0: b_A = 0, the iterate stays 0 and the first
+    check divides 0 by 0.  As in the oracle, the NaN rho ends the step with
+    ENAN after 8 sweeps and leaves the zero field."""
+    N = 300
+    say("zero problem", kernel, D, tile)
+    s = np.zeros((N, N), np.float32)
+    kw = dict(mode=oracle.ASYNC, D=D, tx=tile[0], ty=tile[1]) if kernel == jac.JAC_ASYNC else {}
+    ref = oracle.solve(N, 0.0, s, steps=2, **kw)
+    assert ref.status == oracle.ENAN and ref.sweeps.tolist() == [8, 0]
+    st, u, k, rho = lib_solve(N, 0.0, s, 2, opts(kernel=kernel, D=D, tile_x=tile[0], tile_y=tile[1]))
+    assert st == jac.JAC_ENAN and k.tolist() == [8, 0] and np.isnan(rho[0]), (st, k, rho)
+    assert not np.any(u)
+
+
 def test_zero_coupling_single_check():
     N = 40
     say("sync r=0")

@@ -237,6 +237,20 @@ def test_nan_source_reports_enan(orc):
     assert res.sweeps.tolist() == [8, 0]
 
 
+@pytest.mark.parametrize("mode", ["sync", "async"])
+def test_zero_problem_reports_enan(orc, mode):
+    """r = 0, s = 0 and u = 0: b_A = 0 and every iterate stays 0, so the first
+    check forms rho = 0 / 0, a NaN under IEEE arithmetic; the step ends there
+    with ENAN and the zero field."""
+    N = 17
+    kw = dict(mode=orc.ASYNC, D=4, tx=8, ty=4) if mode == "async" else {}
+    res = orc.solve(N, 0.0, np.zeros((N, N), np.float32), steps=2, **kw)
+    assert res.status == orc.ENAN
+    assert res.sweeps.tolist() == [8, 0]
+    assert np.isnan(res.rho[0])
+    assert not np.any(res.u)
+
+
 # --------------------------------------------------------- block-async model
 
 def test_async_d1_is_sync(orc):
