@@ -13,6 +13,9 @@ Beside it, on the same JSON line:
                 average launch time, measured with HIP events on the library's
                 stream during the timed solves, against MI355X's 8 TB/s;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+With --pcie the line also carries pcie_inclusive: the same solve with its host
+buffers, from jac_create copying the source in to jac_get_field copying the
+field out (the workspace already allocated), never the value.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--kernel sync|tblock|async] [--D D]
                        [--config C1..C5] [--driver launch|graph|persistent]
@@ -63,6 +66,8 @@ def parse():
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all host cores)")
     ap.add_argument("--cpu-only", action="store_true",
                     help="time only the CPU oracle on the workload and print its cpu_baseline object")
+    ap.add_argument("--pcie", action="store_true",
+                    help="also time create (source in) + solve + field out through host buffers")
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="array size of the bandwidth probe, MiB (0: skip)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -347,10 +352,48 @@ def main():
         "stream_probe_gbs": probe,
         "roofline": roofline,
     }
+    if args.pcie:
+        sol.close()
+        line["pcie_inclusive"] = pcie_inclusive(jac, torch, sol, s, nsteps, opts, exact_sweeps)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_steps, args.cpu_threads)
     sol.close()
     print(json.dumps(line), flush=True)
+
+
+def pcie_inclusive(jac, torch, sol, s, nsteps, opts, exact_sweeps, repeats=3):
+    """Whole solves through host buffers on the bench's own workspace: jac_create
+    (copies the N x N source in, fills the planes, checks the division), the
+    solve, jac_get_field (copies the field out).  Host arrays are touched
+    beforehand; median of the repeats."""
+    import ctypes
+    import statistics
+
+    lib = jac.load_library()
+    N = sol.N
+    src = np.ascontiguousarray(s, dtype=np.float32)
+    out = np.ones((N, N), np.float32)
+    rec = []
+    for _ in range(repeats):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        st, h = jac.jac_create(N, sol.r, src, sol.workspace.data_ptr(), sol.ws_bytes, sol.stream.cuda_stream)
+        if st != jac.JAC_OK:
+            raise RuntimeError(jac.jac_last_error())
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        st, _, _ = jac.jac_solve(h, nsteps, opts)
+        t2 = time.perf_counter()
+        st2 = lib.jac_get_field(h, out.ctypes.data_as(ctypes.c_void_p))
+        t3 = time.perf_counter()
+        jac.jac_destroy(h)
+        if st != jac.JAC_OK or st2 != jac.JAC_OK:
+            raise RuntimeError(jac.jac_last_error())
+        rec.append((t1 - t0, t2 - t1, t3 - t2, t3 - t0))
+    med = [statistics.median(x[i] for x in rec) * 1e3 for i in range(4)]
+    return {"value": round(N * N * exact_sweeps / (med[3] / 1e3) / 1e9, 2), "unit": "Gpoint-updates/s",
+            "ms": round(med[3], 3), "create_ms": round(med[0], 3), "solve_ms": round(med[1], 3),
+            "get_field_ms": round(med[2], 3), "repeats": repeats}
 
 
 def _kernel_source_hash(kclass):

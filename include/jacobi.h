@@ -220,8 +220,12 @@ int jac_sweep_static(jac_t ctx, const jac_opts* opts, int64_t nsweeps, float* rh
 /* Copy the current field u^n to / from host memory (N*N floats, row-major,
  * row 0 next to the 100 boundary; the unknowns of page
  * "stencil-jacobian.vercel.app", section 01), for checkpoint and resume.
- * Blocking: waits for the context's stream.  jac_set_field also resets the
- * bound the constant-divisor division path relies on (see below). */
+ * Blocking: waits for the context's stream.  Both enqueue on that stream one
+ * 1-D copy of the N*N block through the idle iterate plane of the workspace
+ * (the one the next sweep overwrites), a pitch-changing kernel and a refill of
+ * that plane.  The host array is read (written) only during the call.
+ * jac_set_field also resets the bound the constant-divisor division path
+ * relies on (see below). */
 int jac_get_field(jac_t ctx, float* host_out);
 int jac_set_field(jac_t ctx, const float* host_in);
 

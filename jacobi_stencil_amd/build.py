@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libjacobi.so")
 
 SOURCES = ["libjacobi.hip", "kernels_sync.hip", "kernels_tblock.hip", "kernels_async.hip", "kernels_persist.hip",
-           "kernels_probe.hip"]
+           "kernels_probe.hip", "kernels_copy.hip"]
 
 # -ffp-contract=off        : no fused multiply-add anywhere in the method's arithmetic
 # -fno-fast-math           : no reassociation, no approximate division

@@ -38,6 +38,8 @@ namespace jac {
 // kernels_async.hip: whether checking launches of D sweeps on this tiling
 // honour a row mask of 7 (take a check's residual on every 8th row)
 bool async_samples_rows(int N, int tx, int ty, int o, int D);
+// kernels_copy.hip: an N x N block from pitch spitch to pitch dpitch
+hipError_t launch_copy_rect(float* dst, int64_t dpitch, const float* src, int64_t spitch, int N, hipStream_t s);
 }  // namespace jac
 
 namespace {
@@ -1153,6 +1155,26 @@ size_t jac_workspace_bytes(int N) {
 
 const char* jac_last_error(void) { return g_err.c_str(); }
 
+// Between calls the iterate plane other than u_cur holds nothing a later call
+// reads: the next sweep writes all of its unknowns before any is read.  Host
+// transfers stage the N x N field there as one contiguous block -- one 1-D
+// copy (a pitched copy from pageable host memory ran several times slower)
+// and a pitch-changing kernel -- and then restore the plane to what every
+// sweep expects of its ghost ring and padding: zeros, the top ghost row 100.
+static hipError_t restore_plane(jac_ctx* c, int k) {
+    hipError_t e = launch_fill(c->u[k], c->g.plane, 0.0f, c->stream);
+    if (e == hipSuccess) e = launch_ghosts(c->u[k], c->g, c->stream);
+    return e;
+}
+
+// host_in (N x N, row-major) into the unknowns of plane dst, through plane
+// u[stage]; stream-ordered, host_in must stay valid until the stream is synced
+static hipError_t upload_block(jac_ctx* c, float* dst, const float* host_in, int stage) {
+    hipError_t e = hipMemcpyAsync(c->u[stage], host_in, (size_t)c->N * c->N * 4, hipMemcpyHostToDevice, c->stream);
+    if (e == hipSuccess) e = launch_copy_rect(dst + c->g.origin, c->g.P, c->u[stage], c->N, c->N, c->stream);
+    return e;
+}
+
 int jac_create(int N, float r, const float* source_host, void* workspace, size_t ws_bytes, void* stream,
                jac_t* out) {
     if (!out) return fail(JAC_EINVAL, "out is NULL");
@@ -1186,15 +1208,20 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
     c->smax = 0.0;
     c->src_plain = true;
     if (source_host) {
+        // max |s| as the largest magnitude bit pattern (Inf and NaN sit above
+        // every finite value), and whether any element is -0: one pass the
+        // compiler vectorises
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(source_host);
+        uint32_t mb = 0, negz = 0;
         for (int64_t i = 0; i < (int64_t)N * N; ++i) {
-            const float v = source_host[i];
-            const double a = std::fabs((double)v);
-            if (!std::isfinite(a) || (v == 0.0f && std::signbit(v))) {
-                c->src_plain = false;
-                break;
-            }
-            if (a > c->smax) c->smax = a;
+            const uint32_t a = w[i] & 0x7fffffffu;
+            mb = a > mb ? a : mb;
+            negz |= (uint32_t)(w[i] == 0x80000000u);
         }
+        float mf;
+        std::memcpy(&mf, &mb, 4);
+        c->src_plain = mb < 0x7f800000u && !negz;
+        c->smax = mb < 0x7f800000u ? (double)mf : (double)INFINITY;
     }
     c->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
     c->sync_rows = sync_rows_for(N, c->cus);
@@ -1279,11 +1306,11 @@ int jac_create(int N, float r, const float* source_host, void* workspace, size_t
                                c->g.plane * 4 + (int64_t)(sizeof(Scratch) / 4) +
                                    (int64_t)kMaxPersistBlocks * kFlagStride + c->npart_cap,
                                0.0f, c->stream);
+    // the source goes through u_1 (idle until the first sweep) as one block
+    if (e == hipSuccess && source_host) e = upload_block(c, c->s, source_host, 1);
+    if (e == hipSuccess) e = launch_fill(c->u[1], c->g.plane, 0.0f, c->stream);
     if (e == hipSuccess) e = launch_ghosts(c->u[0], c->g, c->stream);
     if (e == hipSuccess) e = launch_ghosts(c->u[1], c->g, c->stream);
-    if (e == hipSuccess && source_host)
-        e = hipMemcpy2DAsync(c->s + c->g.origin, (size_t)c->g.P * 4, source_host, (size_t)N * 4, (size_t)N * 4,
-                             (size_t)N, hipMemcpyHostToDevice, c->stream);
     // The sweep divides by the constant d.  Use the reciprocal-and-correct
     // quotient only if it equals the IEEE quotient on every float input.
     const char* ieee_env = std::getenv("JACOBI_IEEE_DIVISION");
@@ -1418,8 +1445,12 @@ int jac_sweep_static(jac_t c, const jac_opts* o, int64_t nsweeps, float* rho) {
 
 int jac_get_field(jac_t c, float* host_out) {
     if (!c || !host_out) return fail(JAC_EINVAL, "NULL argument");
-    JAC_HIP(hipMemcpy2DAsync(host_out, (size_t)c->N * 4, c->u[c->cur] + c->g.origin, (size_t)c->g.P * 4,
-                             (size_t)c->N * 4, (size_t)c->N, hipMemcpyDeviceToHost, c->stream));
+    // u_cur's unknowns packed into the idle plane, one 1-D copy out, the
+    // idle plane restored
+    const int idle = 1 - c->cur;
+    JAC_HIP(launch_copy_rect(c->u[idle], c->N, c->u[c->cur] + c->g.origin, c->g.P, c->N, c->stream));
+    JAC_HIP(hipMemcpyAsync(host_out, c->u[idle], (size_t)c->N * c->N * 4, hipMemcpyDeviceToHost, c->stream));
+    JAC_HIP(restore_plane(c, idle));
     JAC_HIP(hipStreamSynchronize(c->stream));
     return JAC_OK;
 }
@@ -1427,16 +1458,20 @@ int jac_get_field(jac_t c, float* host_out) {
 int jac_set_field(jac_t c, const float* host_in) {
     if (!c || !host_in) return fail(JAC_EINVAL, "NULL argument");
     c->ubound = INFINITY;
-    double m = 100.0;  // the top ghost row
+    // max(100, max |u|) (100: the top ghost row), or Inf if any value is not
+    // finite: |x| compared as the bits of a non-negative float, where NaN and
+    // Inf sit above every finite value
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(host_in);
+    uint32_t mb = 0;
     for (int64_t i = 0; i < (int64_t)c->N * c->N; ++i) {
-        const double v = std::fabs((double)host_in[i]);
-        if (!(v <= m)) {
-            if (!std::isfinite(v)) { m = INFINITY; break; }
-            m = v;
-        }
+        const uint32_t a = w[i] & 0x7fffffffu;
+        mb = a > mb ? a : mb;
     }
-    JAC_HIP(hipMemcpy2DAsync(c->u[c->cur] + c->g.origin, (size_t)c->g.P * 4, host_in, (size_t)c->N * 4,
-                             (size_t)c->N * 4, (size_t)c->N, hipMemcpyHostToDevice, c->stream));
+    float mf;
+    std::memcpy(&mf, &mb, 4);
+    const double m = mb >= 0x7f800000u ? (double)INFINITY : std::max(100.0, (double)mf);
+    JAC_HIP(upload_block(c, c->u[c->cur], host_in, 1 - c->cur));
+    JAC_HIP(restore_plane(c, 1 - c->cur));
     JAC_HIP(hipStreamSynchronize(c->stream));
     c->ubound = m;
     return JAC_OK;

@@ -149,6 +149,37 @@ def test_zero_problem_gives_enan(kernel, D, tile):
     assert not np.any(u)
 
 
+@pytest.mark.parametrize("kernel,D,driver", [(jac.JAC_SYNC, 1, jac.JAC_LAUNCH), (jac.JAC_TBLOCK, 8, jac.JAC_LAUNCH),
+                                             (jac.JAC_TBLOCK, 11, jac.JAC_LAUNCH), (jac.JAC_ASYNC, 8, jac.JAC_LAUNCH),
+                                             (jac.JAC_SYNC, 1, jac.JAC_GRAPH), (jac.JAC_TBLOCK, 8, jac.JAC_PERSISTENT)])
+def test_field_transfers_between_steps_bitwise(kernel, D, driver):
+    """The host transfers stage the field in the idle iterate plane and then
+    restore it: a field read after every step and written back after the
+    second leave every step on the oracle's bits (ragged N = 301, random
+    u^0 written in first)."""
+    N, r = 301, 10.0
+    say("field transfers", kernel, D, driver)
+    s = workloads.gaussian_source(N, r)
+    prev = workloads.random_field(N, 3)
+    kw = dict(mode=oracle.ASYNC, D=D, tx=32, ty=16) if kernel == jac.JAC_ASYNC else {}
+    o = opts(kernel=kernel, D=D, driver=driver, tile_x=32, tile_y=16 if kernel == jac.JAC_ASYNC else 8)
+    sol = jac.Solver(N, r, s)
+    try:
+        sol.set_field(prev)
+        for n in range(3):
+            ref = oracle.solve(N, r, s, u0=prev, steps=1, **kw)
+            st, k, rho = sol.step(o)
+            u = sol.field()
+            assert (st, k) == (jac.JAC_OK, int(ref.sweeps[0])), (n, st, k)
+            assert np.float32(rho).view(np.uint32) == ref.rho[0].view(np.uint32), n
+            assert np.array_equal(bits(u), bits(ref.u)), f"step {n}"
+            if n == 1:
+                sol.set_field(u)
+            prev = ref.u
+    finally:
+        sol.close()
+
+
 def test_zero_coupling_single_check():
     N = 40
     say("sync r=0")
