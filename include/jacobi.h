@@ -126,7 +126,10 @@ typedef struct {
     int32_t kernel;      /* jac_kernel */
     int32_t driver;      /* jac_driver */
     int32_t D;           /* sweeps per launch: TBLOCK 1..16, ASYNC 1..32; ignored for SYNC */
-    int32_t tile_x;      /* ASYNC tile width in columns (1..256; tile_x * tile_y <= 4096) */
+    int32_t tile_x;      /* ASYNC tile width in columns (1..256; tile_x * tile_y <= 4096; a check
+                            takes one slot per block of the N*N/64 + 65536 in the workspace, so
+                            jac_step / jac_solve reject, with JAC_EINVAL and before any work, tiles
+                            whose launch needs more: only tiles under 64 points on large grids) */
     int32_t tile_y;      /* ASYNC tile height in rows (1..256) */
     int32_t M;           /* check interval in sweeps (>= 1).  SYNC and TBLOCK check every M sweeps
                             whatever D (a TBLOCK launch deeper than M measures the residual at the

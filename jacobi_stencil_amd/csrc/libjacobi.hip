@@ -1354,6 +1354,12 @@ int jac_solve(jac_t c, int nsteps, const jac_opts* o, int64_t* sweeps, float* rh
     if (nsteps < 0) return fail(JAC_EINVAL, "nsteps must be >= 0");
     int st = check_opts(c, o);
     if (st) return st;
+    // a block-async check takes one partial-maximum slot per block, and the
+    // launch forms run one block per tile: tiles far smaller than 64 points
+    // on a large grid would fail at the first check, after work had run
+    if (o->kernel == JAC_ASYNC && o->driver != JAC_PERSISTENT &&
+        async_blocks(c->N, o->tile_x, o->tile_y, o->overlap) > c->npart_cap)
+        return fail(JAC_EINVAL, "tile too small for this N: more blocks than partial-maximum slots");
     for (int n = 0; n < nsteps; ++n) {
         if (sweeps) sweeps[n] = 0;
         if (rho) rho[n] = NAN;

@@ -1,0 +1,97 @@
+"""Seeded random combinations of the options, each against the oracle bit for
+bit: ragged and tiny grids, couplings from 0.05 to 100, every kernel and
+driver, blocking and overlapped checks, check intervals 1..12, depths up to
+16 (temporal blocking) and 32 (block-async), odd tile shapes, sweep caps and
+random initial fields.  The combinations are fixed by the seed, so a failure
+names a case that repeats (page "stencil-jacobian.vercel.app", sections 01
+and 02: the step, the check every M sweeps, the three kernels)."""
+import numpy as np
+import pytest
+
+import jacobi_stencil_amd as jac
+import oracle
+import workloads
+from tests.gpu_helpers import assert_same, opts, say
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = {"sync": jac.JAC_SYNC, "tblock": jac.JAC_TBLOCK, "async": jac.JAC_ASYNC, "unfused": jac.JAC_SYNC_UNFUSED}
+DRIVERS = {"launch": jac.JAC_LAUNCH, "graph": jac.JAC_GRAPH, "persistent": jac.JAC_PERSISTENT}
+CHECKS = {"overlapped": jac.JAC_CHECKS_OVERLAPPED, "blocking": jac.JAC_CHECKS_BLOCKING}
+
+
+def make_cases(n=48, seed=20261202):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kernel = str(rng.choice(list(KERNELS)))
+        driver = str(rng.choice(list(DRIVERS)))
+        if kernel == "unfused" and driver == "persistent":
+            driver = "launch"
+        sizes = [1, 2, 3, 5, 17, 33, 64, 70, 97, 128, 150, 255, 256, 257, 300, 384, 400]
+        if driver == "persistent":
+            sizes = [s for s in sizes if s <= 300]
+        N = int(rng.choice(sizes))
+        c = {"i": i, "N": N, "r": float(rng.choice([0.05, 1.0, 10.0, 100.0])), "kernel": kernel,
+             "driver": driver, "checks": str(rng.choice(list(CHECKS))), "M": int(rng.integers(1, 13)),
+             "D": 1, "tile": (32, 8), "cap": 10**6, "u0": bool(rng.integers(0, 2)),
+             "source": str(rng.choice(["gaussian", "random", "point"]))}
+        if kernel == "tblock":
+            c["D"] = int(rng.integers(1, 17))
+        elif kernel == "async":
+            c["D"] = int(rng.integers(1, 33))
+            while True:
+                tx = int(rng.choice([1, 3, 4, 7, 8, 16, 24, 32, 64]))
+                ty = int(rng.choice([1, 2, 4, 8, 13, 16, 32]))
+                if tx * ty <= 4096 and (driver != "persistent" or tx * ty >= 16):
+                    break
+            c["tile"] = (tx, ty)
+        if rng.integers(0, 4) == 0:
+            c["cap"] = int(rng.integers(1, 60))
+        cases.append(c)
+    return cases
+
+
+CASES = make_cases()
+
+
+def source(c):
+    N, r = c["N"], c["r"]
+    if c["source"] == "gaussian":
+        return workloads.gaussian_source(N, r)
+    if c["source"] == "point":
+        return workloads.point_source(N, r)
+    return workloads.random_source(N, r, 100 + c["i"])
+
+
+@pytest.mark.parametrize("c", CASES, ids=[f"case{c['i']}" for c in CASES])
+def test_random_configuration_bitwise(c):
+    say("random config", c)
+    N, r = c["N"], c["r"]
+    s = source(c)
+    u0 = workloads.random_field(N, 200 + c["i"]) if c["u0"] else None
+    if c["kernel"] == "async":
+        ref = oracle.solve(N, r, s, u0=u0, steps=2, M=c["M"], mode=oracle.ASYNC, D=c["D"], tx=c["tile"][0],
+                           ty=c["tile"][1], max_sweeps=c["cap"])
+    else:
+        ref = oracle.solve(N, r, s, u0=u0, steps=2, M=c["M"], max_sweeps=c["cap"])
+    o = opts(kernel=KERNELS[c["kernel"]], driver=DRIVERS[c["driver"]], D=c["D"], tile_x=c["tile"][0],
+             tile_y=c["tile"][1], M=c["M"], max_sweeps=c["cap"], checks=CHECKS[c["checks"]])
+    sol = jac.Solver(N, r, s)
+    try:
+        if u0 is not None:
+            sol.set_field(u0)
+        try:
+            st, k, rho = sol.solve(2, o, allow=(jac.JAC_ENOCONV, jac.JAC_ENAN))
+        except jac.JacobiError as e:
+            # block-async tiles under 64 points can need more check slots than
+            # the workspace holds: rejected before any work runs
+            assert c["kernel"] == "async" and c["tile"][0] * c["tile"][1] < 64, str(e)
+            assert "tile too small" in str(e)
+            want = u0 if u0 is not None else np.zeros((N, N), np.float32)
+            assert np.array_equal(sol.field(), want)
+            return
+        res = (st, sol.field(), k, rho)
+    finally:
+        sol.close()
+    assert_same(res, ref, str(c))
