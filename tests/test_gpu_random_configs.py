@@ -2,7 +2,8 @@
 bit: ragged and tiny grids, couplings from 0.05 to 100, every kernel and
 driver, blocking and overlapped checks, check intervals 1..12, depths up to
 16 (temporal blocking) and 32 (block-async), odd tile shapes, sweep caps and
-random initial fields.  The combinations are fixed by the seed, so a failure
+random initial fields; a second group on grids of 511 to 1100.  The
+combinations are fixed by the seeds, so a failure
 names a case that repeats (page "stencil-jacobian.vercel.app", sections 01
 and 02: the step, the check every M sweeps, the three kernels)."""
 import numpy as np
@@ -20,19 +21,22 @@ DRIVERS = {"launch": jac.JAC_LAUNCH, "graph": jac.JAC_GRAPH, "persistent": jac.J
 CHECKS = {"overlapped": jac.JAC_CHECKS_OVERLAPPED, "blocking": jac.JAC_CHECKS_BLOCKING}
 
 
-def make_cases(n=48, seed=20261202):
+def make_cases(n=48, seed=20261202, first=0, large=False):
     rng = np.random.default_rng(seed)
     cases = []
-    for i in range(n):
+    for i in range(first, first + n):
         kernel = str(rng.choice(list(KERNELS)))
         driver = str(rng.choice(list(DRIVERS)))
         if kernel == "unfused" and driver == "persistent":
             driver = "launch"
         sizes = [1, 2, 3, 5, 17, 33, 64, 70, 97, 128, 150, 255, 256, 257, 300, 384, 400]
+        if large:
+            sizes = [511, 512, 513, 640, 777, 1024, 1100]
         if driver == "persistent":
-            sizes = [s for s in sizes if s <= 300]
+            sizes = [s for s in sizes if s <= 300] or [512, 513, 1024]
         N = int(rng.choice(sizes))
-        c = {"i": i, "N": N, "r": float(rng.choice([0.05, 1.0, 10.0, 100.0])), "kernel": kernel,
+        couplings = [0.05, 1.0, 10.0] if large else [0.05, 1.0, 10.0, 100.0]
+        c = {"i": i, "N": N, "r": float(rng.choice(couplings)), "kernel": kernel,
              "driver": driver, "checks": str(rng.choice(list(CHECKS))), "M": int(rng.integers(1, 13)),
              "D": 1, "tile": (32, 8), "cap": 10**6, "u0": bool(rng.integers(0, 2)),
              "source": str(rng.choice(["gaussian", "random", "point"]))}
@@ -52,7 +56,7 @@ def make_cases(n=48, seed=20261202):
     return cases
 
 
-CASES = make_cases()
+CASES = make_cases() + make_cases(n=48, seed=7, first=48, large=True)
 
 
 def source(c):
