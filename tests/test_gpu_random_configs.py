@@ -12,7 +12,7 @@ import pytest
 import jacobi_stencil_amd as jac
 import oracle
 import workloads
-from tests.gpu_helpers import assert_same, opts, say
+from tests.gpu_helpers import assert_same, bits, opts, say
 
 pytestmark = pytest.mark.gpu
 
@@ -99,3 +99,59 @@ def test_random_configuration_bitwise(c):
     finally:
         sol.close()
     assert_same(res, ref, str(c))
+
+
+def make_sweep_cases(n=32, seed=5):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kernel = str(rng.choice(list(KERNELS)))
+        c = {"i": i, "N": int(rng.choice([1, 2, 9, 64, 97, 130, 256, 301, 513])),
+             "r": float(rng.choice([0.05, 1.0, 10.0, 100.0])), "kernel": kernel, "D": 1, "tile": (32, 8),
+             "n": int(rng.integers(0, 41))}
+        if kernel == "tblock":
+            c["D"] = int(rng.integers(1, 17))
+        elif kernel == "async":
+            c["D"] = int(rng.integers(1, 33))
+            tx = int(rng.choice([1, 3, 4, 8, 16, 24, 32, 64]))
+            ty = int(rng.choice([1, 2, 4, 8, 13, 16, 32]))
+            c["tile"] = (tx, ty)
+        cases.append(c)
+    return cases
+
+
+SWEEP_CASES = make_sweep_cases()
+
+
+@pytest.mark.parametrize("c", SWEEP_CASES, ids=[f"sweeps{c['i']}" for c in SWEEP_CASES])
+def test_random_fixed_sweeps_bitwise(c):
+    """jac_sweep and jac_sweep_static from the same random field: b = u^n + s,
+    then exactly n sweeps -- for temporal blocking and block-async q launches
+    of D and one of the remaining n - qD -- and rho of the result, against the
+    oracle's single sweep and single block-asynchronous launch composed."""
+    say("random fixed sweeps", c)
+    N, r, n, D = c["N"], c["r"], c["n"], c["D"]
+    s = workloads.random_source(N, r, 300 + c["i"])
+    u0 = workloads.random_field(N, 400 + c["i"])
+    b = oracle.rhs(u0, s)
+    want = u0
+    if c["kernel"] == "async":
+        tx, ty = c["tile"]
+        for q in range(0, n, D):
+            want = oracle.async_launch(want, b, r, tx, ty, min(D, n - q))
+    else:
+        for _ in range(n):
+            want = oracle.sweep(want, b, r)
+    want_rho = np.float32(oracle.residual(want, b, r)) / oracle.rhs_norm(b, r)
+    o = opts(kernel=KERNELS[c["kernel"]], D=D, tile_x=c["tile"][0], tile_y=c["tile"][1])
+    sol = jac.Solver(N, r, s)
+    try:
+        for fn in (jac.jac_sweep, jac.jac_sweep_static):
+            sol.set_field(u0)
+            st, rho = fn(sol.ctx, o, n, True)
+            assert st == jac.JAC_OK, jac.jac_last_error()
+            assert np.array_equal(bits(sol.field()), bits(want)), f"{fn.__name__} {c}"
+            assert np.float32(rho).view(np.uint32) == np.float32(want_rho).view(np.uint32), (fn.__name__, rho,
+                                                                                            want_rho)
+    finally:
+        sol.close()
