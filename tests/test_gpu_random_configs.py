@@ -155,3 +155,50 @@ def test_random_fixed_sweeps_bitwise(c):
                                                                                             want_rho)
     finally:
         sol.close()
+
+
+def make_study_cases(n=32, seed=9):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        tx = int(rng.choice([1, 3, 4, 8, 16, 24, 32, 64]))
+        ty = int(rng.choice([1, 2, 4, 8, 13, 16, 32]))
+        o = int(rng.integers(0, 9))
+        while (tx + 2 * o) * (ty + 2 * o) > 4096:
+            o -= 1
+        ctrl = str(rng.choice(["static", "asc", "desc"]))
+        c = {"i": i, "N": int(rng.choice([17, 64, 97, 150, 256, 300])), "r": float(rng.choice([1.0, 10.0, 100.0])),
+             "D": int(rng.integers(1, 17)), "tile": (tx, ty), "o": o, "ctrl": ctrl, "M": int(rng.integers(1, 13)),
+             "checks": "blocking" if ctrl != "static" else str(rng.choice(list(CHECKS))),
+             "driver": "launch" if ctrl != "static" else str(rng.choice(["launch", "graph"]))}
+        cases.append(c)
+    return cases
+
+
+STUDY_CASES = make_study_cases()
+CTRL = {"static": (jac.JAC_STATIC, oracle.STATIC), "asc": (jac.JAC_G_ASC, oracle.G_ASC),
+        "desc": (jac.JAC_G_DESC, oracle.G_DESC)}
+
+
+@pytest.mark.parametrize("c", STUDY_CASES, ids=[f"study{c['i']}" for c in STUDY_CASES])
+def test_random_overlap_and_controllers_bitwise(c):
+    """Block-async with overlapping tiles (o cells per side, the page
+    "Hierarchical Jacobi Iteration ...", section 3.5) and the G-asc / G-desc
+    depth controllers (page "stencil-jacobian.vercel.app", section 02) on
+    random tilings, depths, intervals and grids, against the oracle."""
+    say("random overlap / controller", c)
+    N, r = c["N"], c["r"]
+    s = workloads.random_source(N, r, 500 + c["i"])
+    lib_ctrl, orc_ctrl = CTRL[c["ctrl"]]
+    tx, ty = c["tile"]
+    ref = oracle.solve(N, r, s, steps=2, M=c["M"], mode=oracle.ASYNC, D=c["D"], tx=tx, ty=ty, o=c["o"],
+                       controller=orc_ctrl)
+    o = opts(kernel=jac.JAC_ASYNC, D=c["D"], tile_x=tx, tile_y=ty, M=c["M"], overlap=c["o"], controller=lib_ctrl,
+             checks=CHECKS[c["checks"]], driver=DRIVERS[c["driver"]])
+    sol = jac.Solver(N, r, s)
+    try:
+        st, k, rho = sol.solve(2, o, allow=(jac.JAC_ENOCONV, jac.JAC_ENAN))
+        res = (st, sol.field(), k, rho)
+    finally:
+        sol.close()
+    assert_same(res, ref, str(c))
