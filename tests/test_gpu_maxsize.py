@@ -104,6 +104,8 @@ def big_solver():
     sol = jac.Solver(N_MAX, R, np.full((N_MAX, N_MAX), C, np.float32))
     yield sol
     sol.close()
+    sol.workspace = None      # the fixture's cached value still refers to sol
+    torch.cuda.empty_cache()  # hand the 64.5 GiB back for the tests that follow
 
 
 @pytest.mark.gpu
