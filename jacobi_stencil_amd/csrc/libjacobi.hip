@@ -1453,11 +1453,15 @@ int jac_get_field(jac_t c, float* host_out) {
     if (!c || !host_out) return fail(JAC_EINVAL, "NULL argument");
     // u_cur's unknowns packed into the idle plane, one 1-D copy out, the
     // idle plane restored
+    // idle plane restored even when the copy out fails (a bad host pointer)
     const int idle = 1 - c->cur;
-    JAC_HIP(launch_copy_rect(c->u[idle], c->N, c->u[c->cur] + c->g.origin, c->g.P, c->N, c->stream));
-    JAC_HIP(hipMemcpyAsync(host_out, c->u[idle], (size_t)c->N * c->N * 4, hipMemcpyDeviceToHost, c->stream));
-    JAC_HIP(restore_plane(c, idle));
-    JAC_HIP(hipStreamSynchronize(c->stream));
+    hipError_t e = launch_copy_rect(c->u[idle], c->N, c->u[c->cur] + c->g.origin, c->g.P, c->N, c->stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(host_out, c->u[idle], (size_t)c->N * c->N * 4, hipMemcpyDeviceToHost, c->stream);
+    const hipError_t er = restore_plane(c, idle);
+    if (e == hipSuccess) e = er;
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return fail(JAC_EDEVICE, std::string("jac_get_field: ") + hipGetErrorString(e));
     return JAC_OK;
 }
 
@@ -1476,9 +1480,11 @@ int jac_set_field(jac_t c, const float* host_in) {
     float mf;
     std::memcpy(&mf, &mb, 4);
     const double m = mb >= 0x7f800000u ? (double)INFINITY : std::max(100.0, (double)mf);
-    JAC_HIP(upload_block(c, c->u[c->cur], host_in, 1 - c->cur));
-    JAC_HIP(restore_plane(c, 1 - c->cur));
-    JAC_HIP(hipStreamSynchronize(c->stream));
+    hipError_t e = upload_block(c, c->u[c->cur], host_in, 1 - c->cur);
+    const hipError_t er = restore_plane(c, 1 - c->cur);  // also after a failed copy in
+    if (e == hipSuccess) e = er;
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return fail(JAC_EDEVICE, std::string("jac_set_field: ") + hipGetErrorString(e));
     c->ubound = m;
     return JAC_OK;
 }
